@@ -1,0 +1,243 @@
+"""Python binding of libmla (MLA decode with weight absorption on MI355X).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. Functions carry the C names of include/mla.h and take torch tensors
+on the current HIP device (contiguous), or plain Python values. PyTorch
+supplies device memory and the current stream; the library allocates no
+device memory. A missing library raises; there is no fallback.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "F32", "BF16", "FP8_E4M3", "MLAError", "MlaDims", "MlaCache", "Plan", "load", "lib_path",
+    "dims", "cache", "mla_plan_create", "mla_append_workspace_bytes",
+    "mla_decode_workspace_bytes", "mla_append", "mla_decode", "mla_append_decode",
+    "mla_workspace_init", "mla_device_error", "mla_status_str", "mla_abi_version",
+    "mla_prof_begin", "mla_prof_end", "mla_calib_copy", "EXPORTED",
+]
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "MLA_ERR_CAPACITY",
+          4: "MLA_ERR_HIP", 5: "MLA_ERR_WORKSPACE", 6: "MLA_ERR_PLAN"}
+
+# Every extern "C" entry point of include/mla.h.
+EXPORTED = [
+    "mla_append_workspace_bytes", "mla_append", "mla_plan_create", "mla_plan_destroy",
+    "mla_plan_num_items", "mla_plan_item", "mla_decode_workspace_bytes", "mla_decode",
+    "mla_append_decode", "mla_workspace_init", "mla_device_error", "mla_status_str",
+    "mla_abi_version", "mla_prof_begin", "mla_prof_end", "mla_prof_kernel_name",
+    "mla_prof_num_kernels", "mla_calib_copy",
+]
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status, where=""):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("d_c", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("d_nope", ctypes.c_int32), ("d_v", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+
+class MlaCache(ctypes.Structure):
+    _fields_ = [("latent_dtype", ctypes.c_int), ("rope_dtype", ctypes.c_int),
+                ("rows", ctypes.c_void_p), ("row_stride", ctypes.c_int64),
+                ("scale", ctypes.c_void_p), ("n_rows", ctypes.c_int64), ("batch", ctypes.c_int32),
+                ("seq_start", ctypes.c_void_p), ("seq_cap", ctypes.c_void_p),
+                ("seq_len", ctypes.c_void_p)]
+
+
+_LIB = None
+_P = ctypes.c_void_p
+
+
+def lib_path():
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+
+
+def load():
+    """Load libmla.so (built in-tree by __graft_entry__.build()); raises if absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    p = lib_path()
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(p)
+    sig = {
+        "mla_append_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int32]),
+        "mla_append": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_int, _P,
+                                      ctypes.c_size_t, _P]),
+        "mla_plan_create": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, _P]),
+        "mla_plan_destroy": (None, [_P]),
+        "mla_plan_num_items": (ctypes.c_int32, [_P]),
+        "mla_plan_item": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, _P]),
+        "mla_decode_workspace_bytes": (ctypes.c_size_t, [_P, _P]),
+        "mla_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
+                                      ctypes.c_int, _P, ctypes.c_size_t, _P]),
+        "mla_append_decode": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                             _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
+                                             ctypes.c_size_t, _P]),
+        "mla_workspace_init": (ctypes.c_int, [_P, ctypes.c_size_t, _P]),
+        "mla_device_error": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32]),
+        "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "mla_abi_version": (ctypes.c_int32, []),
+        "mla_prof_begin": (ctypes.c_int, [ctypes.c_int32]),
+        "mla_prof_end": (ctypes.c_int, [_P, _P, ctypes.c_int32]),
+        "mla_prof_kernel_name": (ctypes.c_char_p, [ctypes.c_int32]),
+        "mla_prof_num_kernels": (ctypes.c_int32, []),
+        "mla_calib_copy": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _check(st, where):
+    if st != 0:
+        raise MLAError(st, where)
+
+
+def _ptr(t):
+    """Device pointer of a contiguous tensor (or None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dims(n_heads, d_c, d_rope, d_nope, d_v, d_model=0, softmax_scale=None, rope_base=10000.0):
+    if softmax_scale is None:
+        softmax_scale = (d_nope + d_rope) ** -0.5
+    return MlaDims(n_heads, d_c, d_rope, d_nope, d_v, d_model, softmax_scale, rope_base)
+
+
+def cache(rows, row_stride, latent_dtype, rope_dtype, seq_start, seq_cap, seq_len, scale=None):
+    """Describe a cache held in torch tensors: rows is uint8 [n_rows, row_stride];
+    seq_* are int32 [batch]; scale is float32 [n_rows] for fp8 latents."""
+    c = MlaCache(latent_dtype, rope_dtype, _ptr(rows), row_stride, _ptr(scale),
+                 rows.numel() // row_stride, seq_start.numel(), _ptr(seq_start), _ptr(seq_cap),
+                 _ptr(seq_len))
+    c._keep = (rows, scale, seq_start, seq_cap, seq_len)
+    return c
+
+
+class Plan:
+    """Owns an mla_plan*; destroyed with the object."""
+
+    def __init__(self, handle, batch):
+        self.handle = handle
+        self.batch = batch
+
+    @property
+    def n_items(self):
+        return load().mla_plan_num_items(self.handle)
+
+    def items(self):
+        lib = load()
+        b, t0, t1 = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        out = []
+        for k in range(self.n_items):
+            _check(lib.mla_plan_item(self.handle, k, ctypes.byref(b), ctypes.byref(t0), ctypes.byref(t1)),
+                   "mla_plan_item")
+            out.append((b.value, t0.value, t1.value))
+        return out
+
+    def __del__(self):
+        if self.handle and _LIB is not None:
+            _LIB.mla_plan_destroy(self.handle)
+            self.handle = None
+
+
+def mla_plan_create(d, host_lens, n_workers=0):
+    lens = [int(x) for x in host_lens]
+    arr = (ctypes.c_int32 * len(lens))(*lens)
+    h = ctypes.c_void_p()
+    _check(load().mla_plan_create(ctypes.byref(d), arr, len(lens), n_workers, ctypes.byref(h)),
+           "mla_plan_create")
+    return Plan(h, len(lens))
+
+
+def mla_append_workspace_bytes(d, batch, n_new):
+    return load().mla_append_workspace_bytes(ctypes.byref(d), batch, n_new)
+
+
+def mla_decode_workspace_bytes(d, plan):
+    return load().mla_decode_workspace_bytes(ctypes.byref(d), plan.handle)
+
+
+def mla_append(d, c, h, n_new, w_dkv, w_kr, act_w_dtype, ws, stream=None):
+    _check(load().mla_append(ctypes.byref(d), ctypes.byref(c), _ptr(h), n_new, _ptr(w_dkv),
+                             _ptr(w_kr), act_w_dtype, _ptr(ws), ws.numel() * ws.element_size(),
+                             _stream(stream)), "mla_append")
+
+
+def mla_decode(d, c, plan, q_nope, q_rope, q_pos, w_uk, w_uv, q_w_dtype, o, o_dtype, ws, stream=None):
+    _check(load().mla_decode(ctypes.byref(d), ctypes.byref(c), plan.handle, _ptr(q_nope),
+                             _ptr(q_rope), _ptr(q_pos), _ptr(w_uk), _ptr(w_uv), q_w_dtype, _ptr(o),
+                             o_dtype, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "mla_decode")
+
+
+def mla_append_decode(d, c, plan, h, n_new, w_dkv, w_kr, q_nope, q_rope, q_pos, w_uk, w_uv,
+                      act_w_dtype, o, o_dtype, ws, stream=None):
+    _check(load().mla_append_decode(ctypes.byref(d), ctypes.byref(c), plan.handle, _ptr(h), n_new,
+                                    _ptr(w_dkv), _ptr(w_kr), _ptr(q_nope), _ptr(q_rope), _ptr(q_pos),
+                                    _ptr(w_uk), _ptr(w_uv), act_w_dtype, _ptr(o), o_dtype, _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)),
+           "mla_append_decode")
+
+
+def mla_workspace_init(ws, stream=None):
+    _check(load().mla_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "mla_workspace_init")
+
+
+def mla_device_error(ws, reset=True, stream=None):
+    code = ctypes.c_int32()
+    _check(load().mla_device_error(_ptr(ws), _stream(stream), ctypes.byref(code), int(reset)),
+           "mla_device_error")
+    return code.value
+
+
+def mla_status_str(s):
+    return load().mla_status_str(s).decode()
+
+
+def mla_abi_version():
+    return load().mla_abi_version()
+
+
+def mla_prof_begin(max_records=100000):
+    _check(load().mla_prof_begin(max_records), "mla_prof_begin")
+
+
+def mla_prof_end():
+    """Returns {kernel name: (total ms, launches)} for kernels that ran."""
+    lib = load()
+    n = lib.mla_prof_num_kernels()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    _check(lib.mla_prof_end(ms, cnt, n), "mla_prof_end")
+    return {lib.mla_prof_kernel_name(k).decode(): (ms[k], cnt[k]) for k in range(n) if cnt[k]}
+
+
+def mla_calib_copy(dst, src, n_bytes, stream=None):
+    _check(load().mla_calib_copy(_ptr(dst), _ptr(src), n_bytes, _stream(stream)), "mla_calib_copy")

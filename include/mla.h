@@ -1,0 +1,223 @@
+/*
+ * mla.h — C ABI of libmla: Multi-head Latent Attention (MLA) decode with
+ * weight absorption, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources cited by page title and section):
+ *
+ *  - The cache holds, per token, only a compressed latent c_t = W_DKV h_t
+ *    (width d_c) and a small decoupled rotary key k^R_t (width d_rope),
+ *    shared by all heads; per-head keys and values are the up-projections
+ *    W_UK c_t and W_UV c_t.  ("02 — Multi-Latent Attention (MLA)", sections
+ *    "La compresión de MLA" and "Truco de codificación posicional";
+ *    "Multi-head Latent Attention (MLA) și arhitectura DeepSeekMoE", opening
+ *    paragraph: (d_c + d_hR) elements per token and layer.)
+ *  - The score of a cached token is a content term plus a positional term
+ *    ("DeepSeek MLA" card, section on the problem RoPE causes).
+ *  - Weight absorption: the up-projections fold into the query side (W_UK)
+ *    and the output side (W_UV), so attention runs directly on the latent
+ *    and full per-head K/V are never formed ("02 — Multi-Latent Attention
+ *    (MLA)", "Coste de cómputo"; "Atención latente de múltiples cabezas",
+ *    "Información técnica").
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless the comment says "host".
+ *  - Every call is asynchronous on the given stream; MLA_OK means the work
+ *    was validated and launched. The caller keeps all buffers alive until
+ *    the stream has completed the work.
+ *  - Arguments are validated on the host before any HIP call; a rejected
+ *    call launches nothing and returns its status synchronously.
+ *  - Errors that only the device can see (an append past a sequence's
+ *    capacity, a seq_len that differs from the plan) are recorded, first
+ *    error wins, in a status word at the start of the workspace; read it with
+ *    mla_device_error(). The offending sequence's rows are not written and
+ *    its output is set to zero.
+ *  - The library never allocates device memory. The caller owns the cache,
+ *    weights, activations, outputs and workspace; the library owns only the
+ *    host-side plan (pinned host memory) between mla_plan_create() and
+ *    mla_plan_destroy().
+ *  - No C++ exception crosses this boundary.
+ *  - Calls on different streams may run concurrently if they use different
+ *    workspaces.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null pointer, bad size or dtype, misalignment */
+  MLA_ERR_UNSUPPORTED = 2, /* a valid combination no kernel implements      */
+  MLA_ERR_CAPACITY = 3,    /* device: append would pass seq_cap             */
+  MLA_ERR_HIP = 4,         /* a HIP runtime call or launch failed           */
+  MLA_ERR_WORKSPACE = 5,   /* ws_bytes below the required size              */
+  MLA_ERR_PLAN = 6         /* device: seq_len differs from the plan         */
+} mla_status;
+
+typedef enum {
+  MLA_F32 = 0,
+  MLA_BF16 = 1,
+  MLA_FP8_E4M3 = 2 /* OCP E4M3FN: bias 7, max 448, no inf, NaN 0x7F/0xFF */
+} mla_dtype;
+
+/* Shapes of one MLA layer. softmax_scale multiplies the whole
+ * (d_nope + d_rope)-wide score; rope_base is the RoPE base (10000 in the
+ * workloads). RoPE pairs are interleaved, (2j, 2j+1), at frequency
+ * rope_base^(-2j/d_rope), positions absolute from 0. d_model is used only by
+ * mla_append. d_rope must be even. */
+typedef struct {
+  int32_t n_heads, d_c, d_rope, d_nope, d_v, d_model;
+  float softmax_scale, rope_base;
+} mla_dims;
+
+/* A ragged, contiguous-per-sequence latent cache.
+ * Row r is rows + r * row_stride: [c_kv: d_c elements of latent_dtype |
+ * k_rope: d_rope elements of rope_dtype], packed from byte 0; the rest of
+ * the stride is padding the library never reads or writes. Sequence b owns
+ * rows seq_start[b] .. seq_start[b] + seq_cap[b] - 1, of which the first
+ * seq_len[b] are valid. k_rope is stored already rotated at its own
+ * position. For MLA_FP8_E4M3 latents, scale[r] (fp32) multiplies row r's
+ * latent codes; scale is NULL otherwise. */
+typedef struct {
+  mla_dtype latent_dtype; /* F32, BF16 or FP8_E4M3 */
+  mla_dtype rope_dtype;   /* F32 or BF16 */
+  void *rows;             /* [n_rows, row_stride] bytes, 16-byte aligned */
+  int64_t row_stride;     /* bytes, multiple of 16                      */
+  float *scale;           /* [n_rows] for FP8 latents, else NULL         */
+  int64_t n_rows;
+  int32_t batch;
+  const int32_t *seq_start; /* [batch] first row of each sequence */
+  const int32_t *seq_cap;   /* [batch] rows reserved per sequence  */
+  int32_t *seq_len;         /* [batch] valid rows; mla_append adds */
+} mla_cache;
+
+/* Host-side split plan for decode (opaque). */
+typedef struct mla_plan mla_plan;
+
+/* ------------------------------------------------------------------ append
+ * mla_append — down-project n_new new tokens per sequence into the cache.
+ * For sequence b and new token j (0 <= j < n_new), at position
+ * p = seq_len[b] + j:
+ *     c   = W_DKV h[b, j]                 (d_c values)
+ *     k_r = RoPE(W_KR h[b, j], p)         (d_rope values)
+ * written to row seq_start[b] + p in the cache's dtypes (round to nearest
+ * even; FP8 latents: s = max|c| / 448 in fp32, codes = RNE(c / s) clamped
+ * to +-448, scale[row] = s, s = 1 for an all-zero row); then
+ * seq_len[b] += n_new. Accumulation is fp32.
+ * ("02 — Multi-Latent Attention (MLA)", "La compresión de MLA": c_t = W_DKV
+ *  h_t is what is cached; "Truco de codificación posicional": the rotary key
+ *  part is cached as it is.)
+ *   h       [batch, n_new, d_model], act_w_dtype (F32 or BF16)
+ *   w_dkv   [d_c, d_model], act_w_dtype
+ *   w_kr    [d_rope, d_model], act_w_dtype
+ *   ws      workspace of at least mla_append_workspace_bytes() bytes; its
+ *           first 256 bytes hold the device status word (see
+ *           mla_workspace_init).
+ * A sequence with seq_len[b] + n_new > seq_cap[b] is left untouched and
+ * MLA_ERR_CAPACITY is recorded in the status word. */
+size_t mla_append_workspace_bytes(const mla_dims *dims, int32_t batch, int32_t n_new);
+mla_status mla_append(const mla_dims *dims, const mla_cache *cache, const void *h,
+                      int32_t n_new, const void *w_dkv, const void *w_kr,
+                      mla_dtype act_w_dtype, void *ws, size_t ws_bytes,
+                      void *stream /* hipStream_t */);
+
+/* -------------------------------------------------------------------- plan
+ * mla_plan_create — split the decode work of a batch with cached lengths
+ * host_lens[batch] (host) into work items (b, t0, t1) of about equal token
+ * counts, so that one launch fills the GPU even for a few long sequences.
+ * Split-K over the sequence is not on the pages; it is exact by the
+ * log-sum-exp identity (the combine step). n_workers is the number of
+ * concurrent work items to aim for; 0 means "derive from the current HIP
+ * device" (one per compute unit). The plan is deterministic in its inputs
+ * and reusable across layers and calls with the same lengths. Returns
+ * MLA_ERR_INVALID_ARG for batch < 1, a negative length or a null pointer. */
+mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32_t batch,
+                           int32_t n_workers, mla_plan **out);
+void mla_plan_destroy(mla_plan *plan);
+/* Plan inspection (host): number of work items, and item k's
+ * (sequence, first token, end token). */
+int32_t mla_plan_num_items(const mla_plan *plan);
+mla_status mla_plan_item(const mla_plan *plan, int32_t k, int32_t *b, int32_t *t0, int32_t *t1);
+
+/* ------------------------------------------------------------------ decode
+ * mla_decode — one query token per sequence attends over its cached rows.
+ * For sequence b (L = the plan's length for b, P = q_pos[b] if q_pos is not
+ * NULL, else L - 1) and head i:
+ *     q~   = W_UK,i^T q_nope[b,i]                        (absorbed, d_c)
+ *     q_r  = RoPE(q_rope[b,i], P)
+ *     s_t  = softmax_scale * (q~ . c_t + q_r . k_rope_t),  t = 0 .. L-1
+ *     o^   = sum_t softmax(s)_t c_t                      (latent space, d_c)
+ *     o[b,i] = W_UV,i o^                                 (d_v)
+ * which equals standard softmax attention with K = [W_UK c | k_rope] and
+ * V = W_UV c in exact arithmetic. L = 0 gives o = 0.
+ * ("02 — Multi-Latent Attention (MLA)", "Coste de cómputo" and "Lo que MLA no
+ *  es"; "Atención latente de múltiples cabezas", "Información técnica";
+ *  "DeepSeek MLA", content + positional score.)
+ *   q_nope  [batch, n_heads, d_nope], q_w_dtype (F32 or BF16)
+ *   q_rope  [batch, n_heads, d_rope], q_w_dtype, unrotated
+ *   q_pos   [batch] int32 or NULL
+ *   w_uk    [n_heads, d_nope, d_c], q_w_dtype
+ *   w_uv    [n_heads, d_v, d_c], q_w_dtype
+ *   o       [batch, n_heads, d_v], o_dtype (F32 or BF16)
+ *   ws      at least mla_decode_workspace_bytes(dims, plan) bytes
+ * The device checks seq_len[b] against the plan (MLA_ERR_PLAN). Arithmetic:
+ * fp32 accumulation throughout; the bf16 fast path (d_c = 512, d_rope = 64,
+ * n_heads % 32 == 0, bf16 q/weights, bf16 or fp8 latents, bf16 k_rope)
+ * feeds bf16 operands to the matrix cores; every other shape runs fp32
+ * kernels. */
+size_t mla_decode_workspace_bytes(const mla_dims *dims, const mla_plan *plan);
+mla_status mla_decode(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
+                      const void *q_nope, const void *q_rope, const int32_t *q_pos,
+                      const void *w_uk, const void *w_uv, mla_dtype q_w_dtype, void *o,
+                      mla_dtype o_dtype, void *ws, size_t ws_bytes, void *stream);
+
+/* mla_append_decode — mla_append of n_new tokens followed, in stream order,
+ * by mla_decode. The plan must have been made from the lengths after the
+ * append (old lengths + n_new). ws must satisfy both workspace sizes. */
+mla_status mla_append_decode(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
+                             const void *h, int32_t n_new, const void *w_dkv, const void *w_kr,
+                             const void *q_nope, const void *q_rope, const int32_t *q_pos,
+                             const void *w_uk, const void *w_uv, mla_dtype act_w_dtype, void *o,
+                             mla_dtype o_dtype, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ status
+ * mla_workspace_init — clear the device status word at the start of ws
+ * (a one-thread kernel, no memset, so it can sit in a captured graph).
+ * mla_device_error — synchronise the stream, read the status word into
+ * *code (an mla_status value), and clear it if reset != 0. */
+mla_status mla_workspace_init(void *ws, size_t ws_bytes, void *stream);
+mla_status mla_device_error(void *ws, void *stream, int32_t *code, int32_t reset);
+
+const char *mla_status_str(mla_status s);
+int32_t mla_abi_version(void);
+
+/* ------------------------------------------------------------- profiling
+ * Optional per-kernel timing with HIP events recorded around each kernel
+ * this library launches (kernel ids: see mla_prof_kernel_name).
+ * mla_prof_begin enables recording of up to max_records launches;
+ * mla_prof_end synchronises the recorded events, writes the summed
+ * milliseconds and launch counts per kernel id into ms[n] / count[n] and
+ * disables recording. */
+mla_status mla_prof_begin(int32_t max_records);
+mla_status mla_prof_end(double *ms, int32_t *count, int32_t n);
+const char *mla_prof_kernel_name(int32_t id);
+int32_t mla_prof_num_kernels(void);
+
+/* ------------------------------------------------------------ calibration
+ * mla_calib_copy — a plain device copy (16-byte vector loads and stores) of
+ * n_bytes (multiple of 16) from src to dst. Not part of the method: it gives
+ * hardware counters a kernel of known traffic to calibrate against. */
+mla_status mla_calib_copy(void *dst, const void *src, size_t n_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */
