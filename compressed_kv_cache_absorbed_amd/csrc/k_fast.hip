@@ -1,26 +1,278 @@
-// Matrix-core (MFMA) fast path: selection and launchers.
+// Matrix-core (MFMA) fast path for the DeepSeek-V3 shape: latent width 512,
+// RoPE key width 64, heads a multiple of 128, bf16 activations and weights,
+// bf16 or fp8-e4m3 latents with a bf16 RoPE key.
+//
+//   absorb_fast_kernel   Q[b,i] = fp16([W_UK,i^T q_nope[b,i] ; RoPE(q_rope[b,i], P_b)]
+//                                      * softmax_scale * log2 e)
+//                        (fp16, not bf16: the score's sensitivity to the
+//                        rounding of q~ is what limits accuracy on peaked rows)
+//   (the split-K kernel between them lives in k_splitk.hip)
+//   combine_fast_kernel  log-sum-exp merge of the splits, then o = W_UV o^
+//
+// Weight absorption ("02 — Multi-Latent Attention (MLA)", "Coste de cómputo";
+// "Atención latente de múltiples cabezas", "Información técnica"): W_UK is
+// applied to the query once per sequence and W_UV to the latent-space output,
+// so the loop over cached tokens touches only [c_kv | k_rope] rows, each one
+// reused by all heads.
+//
+// MFMA lane layouts used (v_mfma_f32_32x32x16_bf16, wave64, checked on the
+// hardware): A[32 x 16]: lane l holds row l%32, k = 8(l/32) .. +7;
+// B[16 x 32]: lane l holds column l%32, k = 8(l/32) .. +7; D[32 x 32]: lane l,
+// register r holds row 8(r/4) + 4(l/32) + r%4, column l%32. The k order inside
+// one product is free as long as A and B agree, which the value product uses
+// to take P straight from the score registers.
+// ds_read_b64_tr_b16: in each 16-lane group, source lane j supplies the
+// address of 4 consecutive 16-bit elements; lane i receives element i%4 of
+// source lanes i/4 + 4e, e = 0..3 (a 4x16 -> 16x4 transpose).
+#include <cmath>
+#include <cstdlib>
+
 #include "device_util.hpp"
 
 namespace mla {
 
-bool decode_fast_path(const mla_dims &, const mla_cache &, mla_dtype) { return false; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
+
+namespace fast {
+constexpr int DC = 512;        // latent width
+constexpr int DR = 64;         // RoPE key width
+constexpr int D = DC + DR;     // 576: score width
+constexpr int DNOPE = 128;     // query no-RoPE width
+constexpr int DV = 128;        // value head width
+constexpr int HPW = 32;        // heads per wave of the split-K kernel
+constexpr int WAVES = 4;       // its waves: 128 heads per workgroup
+}  // namespace fast
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// MLA_FORCE_GENERIC=1 in the environment routes every call to the generic
+// kernels (for differential testing of the two paths on the same inputs).
+static bool force_generic() {
+  const char *e = std::getenv("MLA_FORCE_GENERIC");
+  return e && e[0] == '1';
+}
+
+bool decode_fast_path(const mla_dims &d, const mla_cache &c, mla_dtype q_w_dtype) {
+  return !force_generic() && d.d_c == fast::DC && d.d_rope == fast::DR && d.d_nope == fast::DNOPE && d.d_v == fast::DV &&
+         d.n_heads % (fast::HPW * fast::WAVES) == 0 && q_w_dtype == MLA_BF16 &&
+         (c.latent_dtype == MLA_BF16 || c.latent_dtype == MLA_FP8_E4M3) && c.rope_dtype == MLA_BF16;
+}
+
+namespace {
+
+// ----------------------------------------------------------------- absorb
+// Grid (H, ceil(B/32)), 256 threads. W_UK,i [128 x 512] is staged in LDS
+// (128 KB) and read transposed as the A operand of q~^T = W_UK,i^T q_nope^T.
+// Each wave owns 128 latent columns (4 blocks of 32) for 32 sequences.
+__global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qscale, float rope_base,
+                                                          const uint16_t *__restrict__ q_nope,
+                                                          const uint16_t *__restrict__ q_rope,
+                                                          const int32_t *__restrict__ q_pos,
+                                                          const uint16_t *__restrict__ w_uk,
+                                                          const SeqInfo *__restrict__ seqs,
+                                                          uint16_t *__restrict__ Q) {
+  using namespace fast;
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // [128][512] bf16
+  const int i = blockIdx.x, b0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint16_t *W = w_uk + static_cast<size_t>(i) * DNOPE * DC;
+  // 128 KB of weights: 8192 chunks of 16 bytes, 32 per thread
+  for (int q = tid; q < DNOPE * DC / 8; q += 256)
+    *reinterpret_cast<u32x4 *>(smem + q * 16) = *reinterpret_cast<const u32x4 *>(W + q * 8);
+
+  // RoPE part: thread per (sequence, pair) within this sequence tile
+  for (int x = tid; x < 32 * (DR / 2); x += 256) {
+    const int bb = b0 + x / (DR / 2), p = x % (DR / 2);
+    if (bb >= B) continue;
+    const size_t bi = static_cast<size_t>(bb) * H + i;
+    const int64_t P = q_pos ? q_pos[bb] : static_cast<int64_t>(seqs[bb].len) - 1;
+    float cs, sn;
+    rope_cos_sin(P, p, DR, rope_base, &cs, &sn);
+    const float x0 = bf16_bits_to_f32(q_rope[bi * DR + 2 * p]);
+    const float x1 = bf16_bits_to_f32(q_rope[bi * DR + 2 * p + 1]);
+    Q[bi * D + DC + 2 * p] = __builtin_bit_cast(uint16_t, static_cast<_Float16>((x0 * cs - x1 * sn) * qscale));
+    Q[bi * D + DC + 2 * p + 1] = __builtin_bit_cast(uint16_t, static_cast<_Float16>((x0 * sn + x1 * cs) * qscale));
+  }
+  __syncthreads();
+
+  // B operand: q_nope^T [16 n x 32 b]: lane holds sequence b0 + l%32, n = 16 kk + 8(l/32) .. +7
+  const int bb = b0 + (lane & 31);
+  bf16x8 qb[DNOPE / 16];
+#pragma unroll
+  for (int kk = 0; kk < DNOPE / 16; ++kk) {
+    if (bb < B) {
+      qb[kk] = *reinterpret_cast<const bf16x8 *>(q_nope + (static_cast<size_t>(bb) * H + i) * DNOPE +
+                                                 16 * kk + 8 * (lane >> 5));
+    } else {
+      qb[kk] = bf16x8{};
+    }
+  }
+  // A operand: W^T [32 c x 16 n] via transposed LDS reads of W [n][c], with
+  // the same contiguous k order as the B operand: in 16-lane group g the
+  // lanes take c = c0 + 16(g%2) + i and n = 16 kk + 8(g/2) + e, e = 0..3 from
+  // the first read and 4..7 from the second; source lane j points at
+  // W[16 kk + 8(g/2) + j/4 (+4)][c0 + 16(g%2) + 4(j%4)].
+  const int g = (lane >> 4) & 3, j = lane & 15;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int c0 = 128 * w + 32 * cb;
+    f32x16 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < DNOPE / 16; ++kk) {
+      const int n0 = 16 * kk + 8 * (g >> 1) + (j >> 2);
+      const int cc = c0 + 16 * (g & 1) + 4 * (j & 3);
+      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, smem + (n0 * DC + cc) * 2));
+      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, smem + ((n0 + 4) * DC + cc) * 2));
+      bf16x8 a;
+      a.lo = __builtin_bit_cast(bf16x4, lo);
+      a.hi = __builtin_bit_cast(bf16x4, hi);
+      acc = mfma32(a, qb[kk], acc);
+    }
+    // D [32 c x 32 b]: lane holds sequence b0 + l%32, c = c0 + 8(r/4) + 4(l/32) + r%4
+    if (bb < B) {
+      uint16_t *dst = Q + (static_cast<size_t>(bb) * H + i) * D + c0 + 4 * (lane >> 5);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = static_cast<_Float16>(acc[4 * g4 + r] * qscale);
+        *reinterpret_cast<f16x4 *>(dst + 8 * g4) = v;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------- combine
+// Grid (H, ceil(B/32)), 256 threads. Merge each sequence's splits into the
+// latent-space output o^ (a bf16 hi + lo pair in LDS), then
+// o^T [128 v x 32 b] = W_UV,i [128 x 512] o^^T [512 x 32 b] on the matrix cores;
+// wave w owns v = 32 w .. 32 w + 31.
+__global__ __launch_bounds__(256) void combine_fast_kernel(int B, int H, const SeqInfo *__restrict__ seqs,
+                                                           const int32_t *__restrict__ dev_len,
+                                                           const float *__restrict__ opart,
+                                                           const float *__restrict__ lse,
+                                                           const uint16_t *__restrict__ w_uv, void *o,
+                                                           int o_bf16) {
+  using namespace fast;
+  constexpr int OHB = DC * 2 + 16;  // bytes per o^ row in LDS (padded)
+  __shared__ __attribute__((aligned(16))) char oh[32 * OHB];
+  __shared__ __attribute__((aligned(16))) char ohl[32 * OHB];
+  const int i = blockIdx.x, b0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+  // ---- merge: wave w handles sequences b0 + w, + 4, ...; lane covers 8 latent
+  // columns. o^ is kept as a bf16 pair hi + lo (lo = bf16(o^ - hi)), which
+  // carries about 16 significant bits into the W_UV product.
+  for (int sb = w; sb < 32; sb += 4) {
+    const int b = b0 + sb;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (b < B) {
+      const SeqInfo si = seqs[b];
+      if (si.item_count > 0 && dev_len[b] == si.len) {
+        float M = -INFINITY;
+        for (int s = 0; s < si.item_count; ++s) M = fmaxf(M, lse[static_cast<size_t>(si.item_begin + s) * H + i]);
+        float den = 0.0f;
+        for (int s = 0; s < si.item_count; ++s) den += exp2f(lse[static_cast<size_t>(si.item_begin + s) * H + i] - M);
+        const float inv = 1.0f / den;
+        for (int s = 0; s < si.item_count; ++s) {
+          const size_t slot = static_cast<size_t>(si.item_begin + s) * H + i;
+          const float ws = exp2f(lse[slot] - M) * inv;
+          const float4 *src = reinterpret_cast<const float4 *>(opart + slot * DC + 8 * lane);
+          const float4 x0 = src[0], x1 = src[1];
+          acc[0] = fmaf(ws, x0.x, acc[0]); acc[1] = fmaf(ws, x0.y, acc[1]);
+          acc[2] = fmaf(ws, x0.z, acc[2]); acc[3] = fmaf(ws, x0.w, acc[3]);
+          acc[4] = fmaf(ws, x1.x, acc[4]); acc[5] = fmaf(ws, x1.y, acc[5]);
+          acc[6] = fmaf(ws, x1.z, acc[6]); acc[7] = fmaf(ws, x1.w, acc[7]);
+        }
+      }
+    }
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = static_cast<__bf16>(acc[e]);
+      lo[e] = static_cast<__bf16>(acc[e] - static_cast<float>(hi[e]));
+    }
+    *reinterpret_cast<bf16x8 *>(oh + sb * OHB + 16 * lane) = hi;
+    *reinterpret_cast<bf16x8 *>(ohl + sb * OHB + 16 * lane) = lo;
+  }
+  __syncthreads();
+
+  // ---- o^T [32 v x 32 b] per wave: A = W_UV,i rows (v = 32 w + l%32, c = 16 kk + 8(l/32)),
+  // B = o^^T (b = l%32, c = 16 kk + 8(l/32)) from LDS, hi and lo parts.
+  const int hl = lane & 31, half = lane >> 5;
+  const uint16_t *wrow = w_uv + (static_cast<size_t>(i) * DV + 32 * w + hl) * DC + 8 * half;
+  f32x16 acc = {};
+#pragma unroll 8
+  for (int kk = 0; kk < DC / 16; ++kk) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(wrow + 16 * kk);
+    const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(oh + hl * OHB + (16 * kk + 8 * half) * 2);
+    const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(ohl + hl * OHB + (16 * kk + 8 * half) * 2);
+    acc = mfma32(a, bh, acc);
+    acc = mfma32(a, bl, acc);
+  }
+  // D: lane holds sequence b0 + l%32, v = 32 w + 8(r/4) + 4(l/32) + r%4
+  const int b = b0 + hl;
+  if (b < B) {
+    const size_t base = (static_cast<size_t>(b) * H + i) * DV + 32 * w + 4 * half;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      if (o_bf16) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = static_cast<__bf16>(acc[4 * g4 + r]);
+        *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(o) + base + 8 * g4) = v;
+      } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(o) + base + 8 * g4) =
+            make_float4(acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
 bool append_fast_path(const mla_dims &, int32_t, mla_dtype) { return false; }
 
 hipError_t launch_append_fast(hipStream_t, const mla_dims &, const mla_cache &, const void *, int32_t,
                               const void *, const void *, float *, int, int32_t *) {
   return hipErrorNotSupported;
 }
-hipError_t launch_absorb_fast(hipStream_t, const mla_dims &, int32_t, const void *, const void *,
-                              const int32_t *, const void *, const SeqInfo *, uint16_t *) {
-  return hipErrorNotSupported;
+
+hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, const void *q_nope,
+                              const void *q_rope, const int32_t *q_pos, const void *w_uk,
+                              const SeqInfo *seqs, uint16_t *q_out) {
+  const size_t shm = fast::DNOPE * fast::DC * 2;  // 128 KB
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(absorb_fast_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  absorb_fast_kernel<<<dim3(d.n_heads, (batch + 31) / 32), 256, shm, s>>>(
+      batch, d.n_heads, d.softmax_scale * kLog2e, d.rope_base, static_cast<const uint16_t *>(q_nope),
+      static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seqs, q_out);
+  return hipGetLastError();
 }
-hipError_t launch_decode_fast(hipStream_t, const mla_dims &, const mla_cache &, int32_t, const WorkItem *,
-                              const SeqInfo *, const uint16_t *, float *, float *, int32_t *) {
-  return hipErrorNotSupported;
-}
-hipError_t launch_combine_fast(hipStream_t, const mla_dims &, const mla_cache &, const SeqInfo *,
-                               const float *, const float *, const void *, void *, mla_dtype) {
-  return hipErrorNotSupported;
+
+hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const SeqInfo *seqs,
+                               const float *opart, const float *lse, const void *w_uv, void *o,
+                               mla_dtype od) {
+  combine_fast_kernel<<<dim3(d.n_heads, (c.batch + 31) / 32), 256, 0, s>>>(
+      c.batch, d.n_heads, seqs, c.seq_len, opart, lse, static_cast<const uint16_t *>(w_uv), o,
+      od == MLA_BF16 ? 1 : 0);
+  return hipGetLastError();
 }
 
 }  // namespace mla

@@ -1,0 +1,531 @@
+// Split-K flash-decode over the latent cache (the hot loop of MLA decode).
+//
+// One workgroup per work item (sequence b, tokens [t0, t1)) and 128 heads:
+// 4 waves x 32 heads. For every tile of 32 cached tokens
+//   S^T [32 tok x 32 heads]  = K [32 x 576] Q^T [576 x 32]        (matrix cores)
+//   online softmax per head, base 2 (Q is pre-scaled by scale * log2 e)
+//   O^T [512 x 32 heads]    += C^T [512 x 32 tok] P^T [32 tok x 32] (matrix cores)
+// where K = [c_kv | k_rope] rows and C = the c_kv part of the same rows: the
+// score is the content term plus the positional term ("DeepSeek MLA" card),
+// and both products read the one tile, reused by all 128 heads, because W_UK
+// is already folded into Q and W_UV is applied after the loop ("02 —
+// Multi-Latent Attention (MLA)", "Coste de cómputo").
+//
+// Memory pipeline: each tile is copied global -> LDS with direct-to-LDS loads
+// (global_load_lds_dwordx4, no registers), three tiles in flight per
+// workgroup; a bare s_barrier plus an explicit vmcnt wait hands a tile from
+// the loads to the matrix cores. The tile loop is unrolled three times so
+// every LDS address is a per-lane base plus a constant.
+//
+// LDS tile layout (bf16): token t occupies 1152 bytes = 72 chunks of 16
+// bytes; chunk ch of token t sits at position ch ^ swz(t) (XOR on the low
+// three bits, which keeps it inside its group of 8) to spread the fragment
+// reads of both products over the banks.
+//
+// fp8 latents: raw rows [512 e4m3 codes | 64 bf16 k_rope] (640 bytes) are
+// loaded the same way into a raw buffer, widened exactly to bf16 into the
+// tile layout above by all waves (every e4m3 value is a bf16 value), and the
+// per-token scale multiplies the content score and P.
+#include <cmath>
+
+#include "device_util.hpp"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_VOID(p) ((__attribute__((address_space(3))) void *)(p))
+#define LDS_S16X4(p) ((__attribute__((address_space(3))) s16x4 *)(p))
+// LDS byte offset of a __shared__ array (a link-time constant when applied
+// to the array itself).
+#define LDS_OFF(arr) static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char *)(arr)))
+
+namespace sk {
+constexpr int DC = 512, DR = 64, D = 576;
+constexpr int CH = 72;              // 16-byte chunks per bf16 token row
+constexpr int ROWB = 1152;          // bytes per bf16 token row
+constexpr int T = kTile;            // 32 tokens per tile
+constexpr int TILE = T * ROWB;      // 36864 bytes
+constexpr int DMA_PER_WAVE = TILE / 1024 / 4;  // 9 direct loads of 1 KB per wave
+constexpr int RAW_ROWB = 640;       // fp8 row: 512 codes + 128 bytes k_rope
+constexpr int RAW_TILE = T * RAW_ROWB;          // 20480
+constexpr int RAW_DMA_PER_WAVE = RAW_TILE / 1024 / 4;  // 5
+constexpr int SLACK = 8;            // running max is kept unless exceeded by 2^8
+}  // namespace sk
+
+// bf16 tiles (three stages for bf16 latents; two for fp8 latents)
+__shared__ __attribute__((aligned(1024))) char g_tile0[sk::TILE];
+__shared__ __attribute__((aligned(1024))) char g_tile1[sk::TILE];
+__shared__ __attribute__((aligned(1024))) char g_tile2[sk::TILE];
+// raw fp8 tiles and per-token scales (fp8 latents only)
+__shared__ __attribute__((aligned(1024))) char g_raw0[sk::RAW_TILE];
+__shared__ __attribute__((aligned(1024))) char g_raw1[sk::RAW_TILE];
+__shared__ __attribute__((aligned(1024))) char g_raw2[sk::RAW_TILE];
+__shared__ __attribute__((aligned(256))) float g_scl[3][64];   // by raw buffer
+__shared__ __attribute__((aligned(256))) float g_sclbf[2][32];  // by bf16 buffer
+
+namespace {
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Score products (fp16 x fp16 -> fp32) in VGPR form, issued as inline asm: the compiler would
+// otherwise give every matrix-core accumulator of the kernel the AGPR form, and
+// the 256 output registers already fill the AGPR file. srcC is the destination
+// itself (exact overlap, same opcode: back-to-back accumulation is allowed);
+// the first product of a chain uses the inline constant 0 as srcC. Its result
+// is read by the vector ALU only after mfma_vgpr_drain().
+// The leading s_nop gives the wait states a matrix-core read of a register
+// needs after a vector-ALU write of it (the A operand is converted by VALU
+// instructions just before); the compiler does not know this asm is a
+// matrix-core op and would not insert them.
+__device__ __forceinline__ f32x16 mfma_vgpr_first(f16x8 a, f16x8 b) {
+  f32x16 d;
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma_vgpr_acc(f32x16 &c, f16x8 a, f16x8 b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+
+// 8 bf16 -> 8 fp16, exact for |x| < 65504 (a bf16 significand fits in fp16's);
+// round-toward-zero saturates larger magnitudes to +-65504 instead of inf.
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(bf16x8 x) {
+  const u32x4 v = __builtin_bit_cast(u32x4, x);
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[j] << 16), __uint_as_float(v[j] & 0xffff0000u));
+    r[2 * j] = h[0];
+    r[2 * j + 1] = h[1];
+  }
+  return r;
+}
+// Wait states between the last score product and any vector-ALU read of its
+// result (the hardware does not interlock this; 32 covers the 16-pass case).
+// Tied to both accumulators so no read can be scheduled above it.
+__device__ __forceinline__ void mfma_vgpr_drain(f32x16 &x, f32x16 &y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ int swz(int t) { return (t & 7) ^ ((t >> 3) & 1); }
+
+// A copy of a thread index the compiler cannot see through, so per-tile
+// address arithmetic is recomputed in place instead of hoisted into live
+// registers.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// vmcnt(n) with expcnt / lgkmcnt left unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int B> __device__ __forceinline__ char *tile_buf() {
+  return B == 0 ? g_tile0 : (B == 1 ? g_tile1 : g_tile2);
+}
+template <int B> __device__ __forceinline__ char *raw_buf() {
+  return B == 0 ? g_raw0 : (B == 1 ? g_raw1 : g_raw2);
+}
+template <int B> __device__ __forceinline__ uint32_t tile_lds() {
+  return B == 0 ? LDS_OFF(g_tile0) : (B == 1 ? LDS_OFF(g_tile1) : LDS_OFF(g_tile2));
+}
+template <int B> __device__ __forceinline__ uint32_t raw_lds() {
+  return B == 0 ? LDS_OFF(g_raw0) : (B == 1 ? LDS_OFF(g_raw1) : LDS_OFF(g_raw2));
+}
+template <int B> __device__ __forceinline__ uint32_t scl_lds() {
+  return LDS_OFF(g_scl) + 256u * B;
+}
+
+// Direct-to-LDS loads (global_load_lds_dword / _dwordx4, SGPR base + 32-bit
+// lane offset): lane i's 4 / 16 bytes from base + voff land at LDS byte
+// lds_addr + 4 i / 16 i. Issued as inline asm so the compiler's own LDS-DMA
+// tracking (which, lacking alias-scope information, would wait for every
+// outstanding copy before any LDS read) stays out of the way; the kernel waits
+// for its copies explicitly with wait_vm<>(). The instructions have no
+// register results, and VMEM operations the compiler does not see can only
+// make its own vmcnt waits stricter, never too weak.
+__device__ __forceinline__ void lds_dma16(const char *base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const char *base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+struct Item {
+  const char *rows;
+  const float *scale;
+  int64_t stride, row0;
+  int t0, t1, ntiles;
+};
+
+// Direct-to-LDS copy of bf16 tile `tile` into `dst` in the swizzled layout:
+// load q of wave w fills LDS bytes [1024 q, 1024 q + 1024) of the tile, lane
+// i the 16-byte chunk at physical position 64 q + i. Tokens past the item's
+// end repeat its last row (finite data; masked out of the softmax).
+__device__ __forceinline__ void dma_bf16(uint32_t dst, const Item &it, int tile, int w, int lane) {
+  const int ts = it.t0 + tile * sk::T;
+  const int tmax = it.t1 - 1 - ts;
+  const char *base = it.rows + (it.row0 + ts) * it.stride;
+  const int ln = opaque(lane);
+#pragma unroll
+  for (int x = 0; x < sk::DMA_PER_WAVE; ++x) {
+    const int q = sk::DMA_PER_WAVE * w + x;
+    const int P = 64 * q + ln;
+    const int t = P / sk::CH;
+    const int ch = (P - sk::CH * t) ^ swz(t);
+    const uint32_t voff = static_cast<uint32_t>(min(t, tmax) * static_cast<int>(it.stride) + ch * 16);
+    lds_dma16(base, voff, __builtin_amdgcn_readfirstlane(dst + 1024u * q));
+  }
+}
+
+// Direct-to-LDS copy of raw fp8 tile rows (640 bytes each, unswizzled) plus
+// one 4-byte scale per token (every wave loads the scales, into the same
+// place, so that every wave issues the same number of loads).
+__device__ __forceinline__ void dma_raw(uint32_t dst, uint32_t scl, const Item &it, int tile, int w, int lane) {
+  const int ts = it.t0 + tile * sk::T;
+  const int tmax = it.t1 - 1 - ts;
+  const char *base = it.rows + (it.row0 + ts) * it.stride;
+  const int ln = opaque(lane);
+#pragma unroll
+  for (int x = 0; x < sk::RAW_DMA_PER_WAVE; ++x) {
+    const int q = sk::RAW_DMA_PER_WAVE * w + x;
+    const int P = 64 * q + ln;             // chunk of 16 bytes, 40 per row
+    const int t = P / 40;
+    const int ch = P - 40 * t;
+    const uint32_t voff = static_cast<uint32_t>(min(t, tmax) * static_cast<int>(it.stride) + ch * 16);
+    lds_dma16(base, voff, __builtin_amdgcn_readfirstlane(dst + 1024u * q));
+  }
+  const char *sbase = reinterpret_cast<const char *>(it.scale + it.row0 + ts);
+  lds_dma4(sbase, static_cast<uint32_t>(min(ln & 31, tmax) * 4), scl);
+}
+
+// Widen a raw fp8 tile into the bf16 tile layout (1280 chunks, 5 per thread)
+// and move its scales next to it.
+__device__ __forceinline__ void widen(char *dst, const char *raw, float *dscl, const float *rscl, int tid_) {
+  const int tid = opaque(tid_);
+  if (tid < sk::T) dscl[tid] = rscl[tid];
+#pragma unroll
+  for (int x = 0; x < sk::RAW_TILE / 16 / 256; ++x) {
+    const int q = tid + 256 * x;
+    const int t = q / 40, ch = q - 40 * t;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(raw + q * 16);
+    if (ch < 32) {
+      u32x4 lo, hi;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        lo[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[k], 1.0f, false));
+        lo[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[k], 1.0f, true));
+        hi[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[k + 2], 1.0f, false));
+        hi[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[k + 2], 1.0f, true));
+      }
+      const int c0 = 2 * ch, c1 = 2 * ch + 1;
+      *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c0 ^ swz(t))) * 16) = lo;
+      *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c1 ^ swz(t))) * 16) = hi;
+    } else {
+      const int c = 64 + (ch - 32);
+      *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c ^ swz(t))) * 16) = v;
+    }
+  }
+}
+
+// Per-lane state of one wave: Q fragments, the output accumulator, softmax
+// statistics and the lane's LDS base addresses.
+struct WaveState {
+  f16x8 qf[sk::D / 16];   // absorbed query (fp16), B operand of the scores
+  f32x16 O[sk::DC / 32];
+  float m, l;
+  int sbase[4];     // score A-fragment bases, by kk % 4
+  int pbase[2][2];  // value A-fragment bases, by (db % 2, second read)
+  int half;
+};
+
+// A-fragment reads. Score fragment kk: token hl, latent/rope dims
+// 16 kk + 8 half .. +7 (one 16-byte read). Value fragment n = 16 kb + db:
+// latent columns 32 db + .., tokens 16 kb + 4 (g/2) + e and + 8 (two
+// transposed 8-byte reads).
+__device__ __forceinline__ bf16x8 score_frag(const WaveState &st, const char *tb, int kk) {
+  return *reinterpret_cast<const bf16x8 *>(tb + st.sbase[kk & 3] + 128 * (kk >> 2));
+}
+__device__ __forceinline__ bf16x8 value_frag(const WaveState &st, const char *tb, int n) {
+  const int kb = n >> 4, db = n & 15;
+  const char *p0 = tb + st.pbase[db & 1][0] + sk::ROWB * (16 * kb) + 128 * (db >> 1);
+  const char *p1 = tb + st.pbase[db & 1][1] + sk::ROWB * (16 * kb + 8) + 128 * (db >> 1);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(p1));
+  bf16x8 a;
+  a.lo = __builtin_bit_cast(bf16x4, lo);
+  a.hi = __builtin_bit_cast(bf16x4, hi);
+  return a;
+}
+
+// One tile: both contractions are software-pipelined by hand (fragment reads
+// run two steps ahead of the matrix-core op that consumes them) and each step
+// is fenced with a scheduling barrier, so the compiler keeps the order and the
+// register footprint small instead of hoisting every read.
+template <bool FP8>
+__device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, const float *tscl, int valid) {
+  using namespace sk;
+  const int half = st.half;
+  // ---- S^T = K Q^T. bf16: two alternating chains over all 36 k-steps.
+  // fp8: Sa accumulates the 32 latent k-steps, Sb the 4 RoPE k-steps;
+  // s = scale Sa + Sb.
+  f32x16 Sa, Sb;
+  {
+    bf16x8 af[3];
+    af[0] = score_frag(st, tb, 0);
+    af[1] = score_frag(st, tb, 1);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      if (kk + 2 < D / 16) af[(kk + 2) % 3] = score_frag(st, tb, kk + 2);
+      const f16x8 a = bf16x8_to_f16x8(af[kk % 3]);
+      if (FP8) {
+        if (kk < DC / 16) {
+          if (kk == 0) Sa = mfma_vgpr_first(a, st.qf[kk]);
+          else mfma_vgpr_acc(Sa, a, st.qf[kk]);
+        } else {
+          if (kk == DC / 16) Sb = mfma_vgpr_first(a, st.qf[kk]);
+          else mfma_vgpr_acc(Sb, a, st.qf[kk]);
+        }
+      } else {
+        if (kk == 0) Sa = mfma_vgpr_first(a, st.qf[kk]);
+        else if (kk == 1) Sb = mfma_vgpr_first(a, st.qf[kk]);
+        else if (kk & 1) mfma_vgpr_acc(Sb, a, st.qf[kk]);
+        else mfma_vgpr_acc(Sa, a, st.qf[kk]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_vgpr_drain(Sa, Sb);
+  }
+  // prefetch the first value fragments under the softmax
+  bf16x8 pf[3];
+  pf[0] = value_frag(st, tb, 0);
+  pf[1] = value_frag(st, tb, 1);
+  float S[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int tok = 8 * (r >> 2) + 4 * half + (r & 3);
+    const float s = FP8 ? fmaf(Sa[r], tscl[tok], Sb[r]) : Sa[r] + Sb[r];
+    S[r] = tok < valid ? s : -INFINITY;
+  }
+  // ---- online softmax (this lane's head: 16 tokens here, 16 in lane ^ 32)
+  float mx = S[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+  mx = pair_max(mx);
+  const float m_new = mx > st.m + SLACK ? mx : st.m;
+  const float alpha = exp2f(st.m - m_new);
+  float psum = 0.0f;
+  bf16x8 P[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float p = exp2f(S[r] - m_new);
+    psum += p;
+    if (FP8) p *= tscl[8 * (r >> 2) + 4 * half + (r & 3)];
+    P[r >> 3][r & 7] = static_cast<__bf16>(p);
+  }
+  st.l = fmaf(st.l, alpha, pair_sum(psum));
+  st.m = m_new;
+  if (__any(alpha != 1.0f)) {
+    // one 16-register block at a time through VGPRs, back into AGPRs
+#pragma unroll
+    for (int db = 0; db < DC / 32; ++db) {
+      f32x16 t = st.O[db];
+      asm volatile("" : "+v"(t));
+      t *= alpha;
+      st.O[db] = t;
+      asm volatile("" : "+a"(st.O[db]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- O^T += C^T P^T, fragment n = 16 kb + db (consecutive ops hit
+  // different accumulators)
+#pragma unroll
+  for (int n = 0; n < 2 * (DC / 32); ++n) {
+    if (n + 2 < 2 * (DC / 32)) pf[(n + 2) % 3] = value_frag(st, tb, n + 2);
+    const int kb = n >> 4, db = n & 15;
+    st.O[db] = mfma32(pf[n % 3], P[kb], st.O[db]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One pipeline step for bf16 latents: tile i is in buffer B.
+template <int B>
+__device__ __forceinline__ void step_bf16(WaveState &st, const Item &it, int i, int w, int lane) {
+  if (i + 1 < it.ntiles) wait_vm<sk::DMA_PER_WAVE>(); else wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  if (i + 2 < it.ntiles) dma_bf16(tile_lds<(B + 2) % 3>(), it, i + 2, w, lane);
+  compute_tile<false>(st, tile_buf<B>(), nullptr, min(sk::T, it.t1 - (it.t0 + i * sk::T)));
+}
+
+// One pipeline step for fp8 latents (B3 = i % 3, B2 = i % 2): after the
+// barrier, raw tile i+1 is widened into bf16 buffer (i+1)%2, raw tile i+3 is
+// fetched into the raw buffer tile i came from, and tile i is computed.
+template <int B3, int B2>
+__device__ __forceinline__ void step_fp8(WaveState &st, const Item &it, int i, int w, int lane, int tid) {
+  constexpr int N3 = (B3 + 1) % 3, N2 = (B2 + 1) % 2;
+  constexpr int PER = sk::RAW_DMA_PER_WAVE + 1;
+  if (i + 2 < it.ntiles) wait_vm<PER>(); else wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  if (i + 1 < it.ntiles) widen(tile_buf<N2>(), raw_buf<N3>(), g_sclbf[N2], g_scl[N3], tid);
+  if (i + 3 < it.ntiles) dma_raw(raw_lds<B3>(), scl_lds<B3>(), it, i + 3, w, lane);
+  compute_tile<true>(st, tile_buf<B2>(), g_sclbf[B2], min(sk::T, it.t1 - (it.t0 + i * sk::T)));
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
+                                                        const WorkItem *__restrict__ items,
+                                                        const SeqInfo *__restrict__ seqs,
+                                                        const uint16_t *__restrict__ Q,
+                                                        float *__restrict__ opart,
+                                                        float *__restrict__ lse,
+                                                        int32_t *__restrict__ status) {
+  using namespace sk;
+  const int k = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hl = lane & 31, half = lane >> 5;
+  const int head = blockIdx.y * 128 + 32 * w + hl;
+  const WorkItem wi = items[k];
+  float *op = opart + (static_cast<size_t>(k) * H + head) * DC;
+
+  const bool ok = c.seq_len[wi.b] == seqs[wi.b].len && wi.t0 >= 0 && wi.t0 < wi.t1 &&
+                  wi.t1 <= c.seq_cap[wi.b] && static_cast<int64_t>(c.seq_start[wi.b]) >= 0 &&
+                  static_cast<int64_t>(c.seq_start[wi.b]) + wi.t1 <= c.n_rows;
+  if (!ok) {
+    if (tid == 0 && blockIdx.y == 0) set_status(status, MLA_ERR_PLAN);
+    for (int x = half * 4; x < DC; x += 8) *reinterpret_cast<float4 *>(op + x) = make_float4(0, 0, 0, 0);
+    if (half == 0) lse[static_cast<size_t>(k) * H + head] = -INFINITY;
+    return;
+  }
+  Item it;
+  it.rows = static_cast<const char *>(c.rows);
+  it.scale = c.scale;
+  it.stride = c.row_stride;
+  it.row0 = c.seq_start[wi.b];
+  it.t0 = wi.t0;
+  it.t1 = wi.t1;
+  it.ntiles = (wi.t1 - wi.t0 + T - 1) / T;
+
+  // prologue loads first, so they overlap the Q fetch
+  if (FP8) {
+    dma_raw(raw_lds<0>(), scl_lds<0>(), it, 0, w, lane);
+    if (it.ntiles > 1) dma_raw(raw_lds<1>(), scl_lds<1>(), it, 1, w, lane);
+    if (it.ntiles > 2) dma_raw(raw_lds<2>(), scl_lds<2>(), it, 2, w, lane);
+  } else {
+    dma_bf16(tile_lds<0>(), it, 0, w, lane);
+    if (it.ntiles > 1) dma_bf16(tile_lds<1>(), it, 1, w, lane);
+  }
+
+  WaveState st;
+  st.half = half;
+  {
+    const uint16_t *qrow = Q + (static_cast<size_t>(wi.b) * H + head) * D + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) st.qf[kk] = *reinterpret_cast<const f16x8 *>(qrow + 16 * kk);
+  }
+#pragma unroll
+  for (int db = 0; db < DC / 32; ++db) {
+    st.O[db] = f32x16{};
+    asm volatile("" : "+a"(st.O[db]));
+  }
+  st.m = -INFINITY;
+  st.l = 0.0f;
+  // score A fragment for kk: token hl, chunk 2 kk + half ->
+  //   hl*1152 + 128 (kk / 4) + 16 ((2 (kk % 4)) ^ (half ^ swz(hl)))
+  {
+    const int s1 = half ^ swz(hl);
+#pragma unroll
+    for (int j2 = 0; j2 < 4; ++j2) st.sbase[j2] = hl * ROWB + 16 * ((2 * j2) ^ s1);
+  }
+  // value A fragment (transposed read): 16-lane group g, lane j in it points at
+  // token 16 kb + 8 h + tt (tt = 4 (g/2) + j/4), latent column 32 db + dd
+  // (dd = 16 (g%2) + 4 (j%4)); its chunk 4 db + dd/8 lands at
+  //   128 (db / 2) + 16 ((4 (db % 2)) ^ (dd / 8) ^ tt ^ h)  within the row.
+  {
+    const int g = (lane >> 4) & 3, j = lane & 15;
+    const int tt = 4 * (g >> 1) + (j >> 2);
+    const int dd = 16 * (g & 1) + 4 * (j & 3);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        st.pbase[a][h] = tt * ROWB + 16 * ((4 * a) ^ (dd >> 3) ^ tt ^ h) + (dd & 7) * 2;
+  }
+
+  if (FP8) {
+    // widen tile 0 before the loop; each step then widens one tile ahead
+    constexpr int PER = RAW_DMA_PER_WAVE + 1;
+    if (it.ntiles > 2) wait_vm<2 * PER>(); else if (it.ntiles > 1) wait_vm<PER>(); else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    widen(g_tile0, g_raw0, g_sclbf[0], g_scl[0], tid);
+    for (int i = 0; i < it.ntiles; i += 6) {
+      step_fp8<0, 0>(st, it, i, w, lane, tid);
+      if (i + 1 < it.ntiles) step_fp8<1, 1>(st, it, i + 1, w, lane, tid);
+      if (i + 2 < it.ntiles) step_fp8<2, 0>(st, it, i + 2, w, lane, tid);
+      if (i + 3 < it.ntiles) step_fp8<0, 1>(st, it, i + 3, w, lane, tid);
+      if (i + 4 < it.ntiles) step_fp8<1, 0>(st, it, i + 4, w, lane, tid);
+      if (i + 5 < it.ntiles) step_fp8<2, 1>(st, it, i + 5, w, lane, tid);
+    }
+  } else {
+    for (int i = 0; i < it.ntiles; i += 3) {
+      step_bf16<0>(st, it, i, w, lane);
+      if (i + 1 < it.ntiles) step_bf16<1>(st, it, i + 1, w, lane);
+      if (i + 2 < it.ntiles) step_bf16<2>(st, it, i + 2, w, lane);
+    }
+  }
+
+  // ---- normalised partial and log-sum-exp (base 2) of this head
+  const float inv = 1.0f / st.l;
+#pragma unroll
+  for (int db = 0; db < DC / 32; ++db) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = 32 * db + 8 * g4 + 4 * half;
+      *reinterpret_cast<float4 *>(op + d) = make_float4(st.O[db][4 * g4] * inv, st.O[db][4 * g4 + 1] * inv,
+                                                        st.O[db][4 * g4 + 2] * inv, st.O[db][4 * g4 + 3] * inv);
+    }
+  }
+  if (half == 0) lse[static_cast<size_t>(k) * H + head] = st.m + log2f(st.l);
+}
+
+}  // namespace
+
+hipError_t launch_decode_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,
+                              const WorkItem *items, const SeqInfo *seqs, const uint16_t *q, float *opart,
+                              float *lse, int32_t *status) {
+  if (n_items == 0) return hipSuccess;
+  const dim3 grid(n_items, d.n_heads / 128);
+  if (c.latent_dtype == MLA_FP8_E4M3)
+    splitk_kernel<true><<<grid, 256, 0, s>>>(c, d.n_heads, items, seqs, q, opart, lse, status);
+  else
+    splitk_kernel<false><<<grid, 256, 0, s>>>(c, d.n_heads, items, seqs, q, opart, lse, status);
+  return hipGetLastError();
+}
+
+}  // namespace mla
