@@ -11,20 +11,23 @@
 // is already folded into Q and W_UV is applied after the loop ("02 —
 // Multi-Latent Attention (MLA)", "Coste de cómputo").
 //
-// Memory pipeline: each tile is copied global -> LDS with direct-to-LDS loads
-// (global_load_lds_dwordx4, no registers), three tiles in flight per
-// workgroup; a bare s_barrier plus an explicit vmcnt wait hands a tile from
-// the loads to the matrix cores. The tile loop is unrolled three times so
-// every LDS address is a per-lane base plus a constant.
+// Arithmetic: both products take fp16 operands with fp32 accumulation. The
+// absorbed query arrives in fp16; cached bf16 (or e4m3) values are widened to
+// fp16 exactly (any bf16 value below 65504 in magnitude, every e4m3 value).
 //
-// LDS tile layout (bf16): token t occupies 1152 bytes = 72 chunks of 16
-// bytes; chunk ch of token t sits at position ch ^ swz(t) (XOR on the low
-// three bits, which keeps it inside its group of 8) to spread the fragment
-// reads of both products over the banks.
+// Memory pipeline: each tile is copied global -> LDS with direct-to-LDS loads
+// (global_load_lds_dwordx4, no registers), issued three tiles ahead; after a
+// bare s_barrier plus an explicit vmcnt wait, all waves widen the next tile in
+// LDS while computing the current one. The tile loop is unrolled by the buffer
+// count so every LDS address is a per-lane base plus a constant.
+//
+// LDS tile layout (16-bit elements): token t occupies 1152 bytes = 72 chunks
+// of 16 bytes; chunk ch of token t sits at position ch ^ swz(t) (XOR on the
+// low three bits, which keeps it inside its group of 8) to spread the
+// fragment reads of both products over the banks.
 //
 // fp8 latents: raw rows [512 e4m3 codes | 64 bf16 k_rope] (640 bytes) are
-// loaded the same way into a raw buffer, widened exactly to bf16 into the
-// tile layout above by all waves (every e4m3 value is a bf16 value), and the
+// loaded into a raw buffer and widened into the tile layout above; the
 // per-token scale multiplies the content score and P.
 #include <cmath>
 
@@ -32,10 +35,8 @@
 
 namespace mla {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -59,10 +60,11 @@ constexpr int RAW_DMA_PER_WAVE = RAW_TILE / 1024 / 4;  // 5
 constexpr int SLACK = 8;            // running max is kept unless exceeded by 2^8
 }  // namespace sk
 
-// bf16 tiles (three stages for bf16 latents; two for fp8 latents)
+// fp16 tiles (four stages for bf16 latents; two for fp8 latents)
 __shared__ __attribute__((aligned(1024))) char g_tile0[sk::TILE];
 __shared__ __attribute__((aligned(1024))) char g_tile1[sk::TILE];
 __shared__ __attribute__((aligned(1024))) char g_tile2[sk::TILE];
+__shared__ __attribute__((aligned(1024))) char g_tile3[sk::TILE];
 // raw fp8 tiles and per-token scales (fp8 latents only)
 __shared__ __attribute__((aligned(1024))) char g_raw0[sk::RAW_TILE];
 __shared__ __attribute__((aligned(1024))) char g_raw1[sk::RAW_TILE];
@@ -72,8 +74,8 @@ __shared__ __attribute__((aligned(256))) float g_sclbf[2][32];  // by bf16 buffe
 
 namespace {
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Score products (fp16 x fp16 -> fp32) in VGPR form, issued as inline asm: the compiler would
@@ -83,9 +85,9 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // the first product of a chain uses the inline constant 0 as srcC. Its result
 // is read by the vector ALU only after mfma_vgpr_drain().
 // The leading s_nop gives the wait states a matrix-core read of a register
-// needs after a vector-ALU write of it (the A operand is converted by VALU
-// instructions just before); the compiler does not know this asm is a
-// matrix-core op and would not insert them.
+// needs after a vector-ALU write of it (the compiler may move operands with
+// VALU instructions just before); it does not know this asm is a matrix-core
+// op and would not insert them.
 __device__ __forceinline__ f32x16 mfma_vgpr_first(f16x8 a, f16x8 b) {
   f32x16 d;
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
@@ -95,24 +97,18 @@ __device__ __forceinline__ void mfma_vgpr_acc(f32x16 &c, f16x8 a, f16x8 b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 
-// 8 bf16 -> 8 fp16, exact for |x| < 65504 (a bf16 significand fits in fp16's);
-// round-toward-zero saturates larger magnitudes to +-65504 instead of inf.
-__device__ __forceinline__ f16x8 bf16x8_to_f16x8(bf16x8 x) {
-  const u32x4 v = __builtin_bit_cast(u32x4, x);
-  f16x8 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[j] << 16), __uint_as_float(v[j] & 0xffff0000u));
-    r[2 * j] = h[0];
-    r[2 * j + 1] = h[1];
-  }
-  return r;
-}
 // Wait states between the last score product and any vector-ALU read of its
 // result (the hardware does not interlock this; 32 covers the 16-pass case).
 // Tied to both accumulators so no read can be scheduled above it.
 __device__ __forceinline__ void mfma_vgpr_drain(f32x16 &x, f32x16 &y) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+
+// 2 bf16 (one dword) -> 2 fp16, exact for |x| < 65504 (a bf16 significand
+// fits in fp16's); round-toward-zero saturates larger magnitudes to +-65504.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -142,13 +138,13 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 template <int B> __device__ __forceinline__ char *tile_buf() {
-  return B == 0 ? g_tile0 : (B == 1 ? g_tile1 : g_tile2);
+  return B == 0 ? g_tile0 : (B == 1 ? g_tile1 : (B == 2 ? g_tile2 : g_tile3));
 }
 template <int B> __device__ __forceinline__ char *raw_buf() {
   return B == 0 ? g_raw0 : (B == 1 ? g_raw1 : g_raw2);
 }
 template <int B> __device__ __forceinline__ uint32_t tile_lds() {
-  return B == 0 ? LDS_OFF(g_tile0) : (B == 1 ? LDS_OFF(g_tile1) : LDS_OFF(g_tile2));
+  return B == 0 ? LDS_OFF(g_tile0) : (B == 1 ? LDS_OFF(g_tile1) : (B == 2 ? LDS_OFF(g_tile2) : LDS_OFF(g_tile3)));
 }
 template <int B> __device__ __forceinline__ uint32_t raw_lds() {
   return B == 0 ? LDS_OFF(g_raw0) : (B == 1 ? LDS_OFF(g_raw1) : LDS_OFF(g_raw2));
@@ -225,9 +221,23 @@ __device__ __forceinline__ void dma_raw(uint32_t dst, uint32_t scl, const Item &
   lds_dma4(sbase, static_cast<uint32_t>(min(ln & 31, tmax) * 4), scl);
 }
 
-// Widen a raw fp8 tile into the bf16 tile layout (1280 chunks, 5 per thread)
+// Widen a bf16 tile to fp16 in place (2304 chunks of 16 bytes, 9 per thread;
+// the swizzle moves whole chunks, so it is unchanged).
+__device__ __forceinline__ void widen_bf16_inplace(char *tile, int tid_) {
+  const int tid = opaque(tid_);
+#pragma unroll
+  for (int x = 0; x < sk::TILE / 16 / 256; ++x) {
+    u32x4 *p = reinterpret_cast<u32x4 *>(tile + (tid + 256 * x) * 16);
+    u32x4 v = *p;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = bf16x2_to_f16x2(v[k]);
+    *p = v;
+  }
+}
+
+// Widen a raw fp8 tile into the fp16 tile layout (1280 chunks, 5 per thread)
 // and move its scales next to it.
-__device__ __forceinline__ void widen(char *dst, const char *raw, float *dscl, const float *rscl, int tid_) {
+__device__ __forceinline__ void widen_fp8(char *dst, const char *raw, float *dscl, const float *rscl, int tid_) {
   const int tid = opaque(tid_);
   if (tid < sk::T) dscl[tid] = rscl[tid];
 #pragma unroll
@@ -239,17 +249,20 @@ __device__ __forceinline__ void widen(char *dst, const char *raw, float *dscl, c
       u32x4 lo, hi;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        lo[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[k], 1.0f, false));
-        lo[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[k], 1.0f, true));
-        hi[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[k + 2], 1.0f, false));
-        hi[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[k + 2], 1.0f, true));
+        lo[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k], 1.0f, false));
+        lo[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k], 1.0f, true));
+        hi[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k + 2], 1.0f, false));
+        hi[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k + 2], 1.0f, true));
       }
       const int c0 = 2 * ch, c1 = 2 * ch + 1;
       *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c0 ^ swz(t))) * 16) = lo;
       *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c1 ^ swz(t))) * 16) = hi;
     } else {
+      u32x4 r;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) r[k] = bf16x2_to_f16x2(v[k]);
       const int c = 64 + (ch - 32);
-      *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c ^ swz(t))) * 16) = v;
+      *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c ^ swz(t))) * 16) = r;
     }
   }
 }
@@ -269,18 +282,18 @@ struct WaveState {
 // 16 kk + 8 half .. +7 (one 16-byte read). Value fragment n = 16 kb + db:
 // latent columns 32 db + .., tokens 16 kb + 4 (g/2) + e and + 8 (two
 // transposed 8-byte reads).
-__device__ __forceinline__ bf16x8 score_frag(const WaveState &st, const char *tb, int kk) {
-  return *reinterpret_cast<const bf16x8 *>(tb + st.sbase[kk & 3] + 128 * (kk >> 2));
+__device__ __forceinline__ f16x8 score_frag(const WaveState &st, const char *tb, int kk) {
+  return *reinterpret_cast<const f16x8 *>(tb + st.sbase[kk & 3] + 128 * (kk >> 2));
 }
-__device__ __forceinline__ bf16x8 value_frag(const WaveState &st, const char *tb, int n) {
+__device__ __forceinline__ f16x8 value_frag(const WaveState &st, const char *tb, int n) {
   const int kb = n >> 4, db = n & 15;
   const char *p0 = tb + st.pbase[db & 1][0] + sk::ROWB * (16 * kb) + 128 * (db >> 1);
   const char *p1 = tb + st.pbase[db & 1][1] + sk::ROWB * (16 * kb + 8) + 128 * (db >> 1);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(p0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(p1));
-  bf16x8 a;
-  a.lo = __builtin_bit_cast(bf16x4, lo);
-  a.hi = __builtin_bit_cast(bf16x4, hi);
+  f16x8 a;
+  a.lo = __builtin_bit_cast(f16x4, lo);
+  a.hi = __builtin_bit_cast(f16x4, hi);
   return a;
 }
 
@@ -297,13 +310,13 @@ __device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, cons
   // s = scale Sa + Sb.
   f32x16 Sa, Sb;
   {
-    bf16x8 af[3];
+    f16x8 af[3];
     af[0] = score_frag(st, tb, 0);
     af[1] = score_frag(st, tb, 1);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       if (kk + 2 < D / 16) af[(kk + 2) % 3] = score_frag(st, tb, kk + 2);
-      const f16x8 a = bf16x8_to_f16x8(af[kk % 3]);
+      const f16x8 a = af[kk % 3];
       if (FP8) {
         if (kk < DC / 16) {
           if (kk == 0) Sa = mfma_vgpr_first(a, st.qf[kk]);
@@ -323,7 +336,7 @@ __device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, cons
     mfma_vgpr_drain(Sa, Sb);
   }
   // prefetch the first value fragments under the softmax
-  bf16x8 pf[3];
+  f16x8 pf[3];
   pf[0] = value_frag(st, tb, 0);
   pf[1] = value_frag(st, tb, 1);
   float S[16];
@@ -341,13 +354,13 @@ __device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, cons
   const float m_new = mx > st.m + SLACK ? mx : st.m;
   const float alpha = exp2f(st.m - m_new);
   float psum = 0.0f;
-  bf16x8 P[2];
+  f16x8 P[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     float p = exp2f(S[r] - m_new);
     psum += p;
     if (FP8) p *= tscl[8 * (r >> 2) + 4 * half + (r & 3)];
-    P[r >> 3][r & 7] = static_cast<__bf16>(p);
+    P[r >> 3][r & 7] = static_cast<_Float16>(p);
   }
   st.l = fmaf(st.l, alpha, pair_sum(psum));
   st.m = m_new;
@@ -375,17 +388,20 @@ __device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, cons
   }
 }
 
-// One pipeline step for bf16 latents: tile i is in buffer B.
+// One pipeline step for bf16 latents (B = i % 4): after the barrier, tile
+// i+1 (landed) is widened to fp16 in place, tile i+3 is fetched into the
+// buffer tile i-1 used, and tile i (widened during step i-1) is computed.
 template <int B>
-__device__ __forceinline__ void step_bf16(WaveState &st, const Item &it, int i, int w, int lane) {
-  if (i + 1 < it.ntiles) wait_vm<sk::DMA_PER_WAVE>(); else wait_vm<0>();
+__device__ __forceinline__ void step_bf16(WaveState &st, const Item &it, int i, int w, int lane, int tid) {
+  if (i + 2 < it.ntiles) wait_vm<sk::DMA_PER_WAVE>(); else wait_vm<0>();
   __builtin_amdgcn_s_barrier();
-  if (i + 2 < it.ntiles) dma_bf16(tile_lds<(B + 2) % 3>(), it, i + 2, w, lane);
+  if (i + 1 < it.ntiles) widen_bf16_inplace(tile_buf<(B + 1) % 4>(), tid);
+  if (i + 3 < it.ntiles) dma_bf16(tile_lds<(B + 3) % 4>(), it, i + 3, w, lane);
   compute_tile<false>(st, tile_buf<B>(), nullptr, min(sk::T, it.t1 - (it.t0 + i * sk::T)));
 }
 
 // One pipeline step for fp8 latents (B3 = i % 3, B2 = i % 2): after the
-// barrier, raw tile i+1 is widened into bf16 buffer (i+1)%2, raw tile i+3 is
+// barrier, raw tile i+1 is widened into fp16 buffer (i+1)%2, raw tile i+3 is
 // fetched into the raw buffer tile i came from, and tile i is computed.
 template <int B3, int B2>
 __device__ __forceinline__ void step_fp8(WaveState &st, const Item &it, int i, int w, int lane, int tid) {
@@ -393,7 +409,7 @@ __device__ __forceinline__ void step_fp8(WaveState &st, const Item &it, int i, i
   constexpr int PER = sk::RAW_DMA_PER_WAVE + 1;
   if (i + 2 < it.ntiles) wait_vm<PER>(); else wait_vm<0>();
   __builtin_amdgcn_s_barrier();
-  if (i + 1 < it.ntiles) widen(tile_buf<N2>(), raw_buf<N3>(), g_sclbf[N2], g_scl[N3], tid);
+  if (i + 1 < it.ntiles) widen_fp8(tile_buf<N2>(), raw_buf<N3>(), g_sclbf[N2], g_scl[N3], tid);
   if (i + 3 < it.ntiles) dma_raw(raw_lds<B3>(), scl_lds<B3>(), it, i + 3, w, lane);
   compute_tile<true>(st, tile_buf<B2>(), g_sclbf[B2], min(sk::T, it.t1 - (it.t0 + i * sk::T)));
 }
@@ -440,6 +456,7 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
   } else {
     dma_bf16(tile_lds<0>(), it, 0, w, lane);
     if (it.ntiles > 1) dma_bf16(tile_lds<1>(), it, 1, w, lane);
+    if (it.ntiles > 2) dma_bf16(tile_lds<2>(), it, 2, w, lane);
   }
 
   WaveState st;
@@ -478,12 +495,12 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
         st.pbase[a][h] = tt * ROWB + 16 * ((4 * a) ^ (dd >> 3) ^ tt ^ h) + (dd & 7) * 2;
   }
 
+  // widen tile 0 before the loop; each step then widens one tile ahead
   if (FP8) {
-    // widen tile 0 before the loop; each step then widens one tile ahead
     constexpr int PER = RAW_DMA_PER_WAVE + 1;
     if (it.ntiles > 2) wait_vm<2 * PER>(); else if (it.ntiles > 1) wait_vm<PER>(); else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    widen(g_tile0, g_raw0, g_sclbf[0], g_scl[0], tid);
+    widen_fp8(g_tile0, g_raw0, g_sclbf[0], g_scl[0], tid);
     for (int i = 0; i < it.ntiles; i += 6) {
       step_fp8<0, 0>(st, it, i, w, lane, tid);
       if (i + 1 < it.ntiles) step_fp8<1, 1>(st, it, i + 1, w, lane, tid);
@@ -493,10 +510,15 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
       if (i + 5 < it.ntiles) step_fp8<2, 1>(st, it, i + 5, w, lane, tid);
     }
   } else {
-    for (int i = 0; i < it.ntiles; i += 3) {
-      step_bf16<0>(st, it, i, w, lane);
-      if (i + 1 < it.ntiles) step_bf16<1>(st, it, i + 1, w, lane);
-      if (i + 2 < it.ntiles) step_bf16<2>(st, it, i + 2, w, lane);
+    constexpr int PER = DMA_PER_WAVE;
+    if (it.ntiles > 2) wait_vm<2 * PER>(); else if (it.ntiles > 1) wait_vm<PER>(); else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    widen_bf16_inplace(g_tile0, tid);
+    for (int i = 0; i < it.ntiles; i += 4) {
+      step_bf16<0>(st, it, i, w, lane, tid);
+      if (i + 1 < it.ntiles) step_bf16<1>(st, it, i + 1, w, lane, tid);
+      if (i + 2 < it.ntiles) step_bf16<2>(st, it, i + 2, w, lane, tid);
+      if (i + 3 < it.ntiles) step_bf16<3>(st, it, i + 3, w, lane, tid);
     }
   }
 
