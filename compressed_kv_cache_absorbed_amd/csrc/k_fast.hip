@@ -7,7 +7,8 @@
 //                        (fp16, not bf16: the score's sensitivity to the
 //                        rounding of q~ is what limits accuracy on peaked rows)
 //   (the split-K kernel between them lives in k_splitk.hip)
-//   combine_fast_kernel  log-sum-exp merge of the splits, then o = W_UV o^
+//   merge_fast_kernel    log-sum-exp merge of the split partials into o^
+//   project_fast_kernel  o = W_UV o^ (the output-side absorption)
 //
 // Weight absorption ("02 — Multi-Latent Attention (MLA)", "Coste de cómputo";
 // "Atención latente de múltiples cabezas", "Información técnica"): W_UK is
@@ -153,78 +154,112 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qs
   }
 }
 
-// --------------------------------------------------------------- combine
-// Grid (H, ceil(B/32)), 256 threads. Merge each sequence's splits into the
-// latent-space output o^ (a bf16 hi + lo pair in LDS), then
-// o^T [128 v x 32 b] = W_UV,i [128 x 512] o^^T [512 x 32 b] on the matrix cores;
-// wave w owns v = 32 w .. 32 w + 31.
-__global__ __launch_bounds__(256) void combine_fast_kernel(int B, int H, const SeqInfo *__restrict__ seqs,
-                                                           const int32_t *__restrict__ dev_len,
-                                                           const float *__restrict__ opart,
-                                                           const float *__restrict__ lse,
-                                                           const uint16_t *__restrict__ w_uv, void *o,
-                                                           int o_bf16) {
+// ------------------------------------------------------------------ merge
+// Grid (batch, H/32, 4), 256 threads: sequence b, head block hb, latent
+// columns 128 q .. 128 q + 127. Log-sum-exp merge of the sequence's split
+// partials (base 2): o^ = sum_s 2^(lse_s - M) o^_s / sum_s 2^(lse_s - M).
+// In the fragment order of the partials the block is 16 KB contiguous per
+// split; thread (g = tid / 64, lane) owns the four float4 at 1024 x + 256 g +
+// 4 lane (x = 0..3), all of head hl = lane % 32. The result goes out as bf16
+// hi and lo planes (lo = bf16(o^ - hi), about 16 significant bits), laid
+// out [head][sequence][column] for the W_UV product.
+__global__ __launch_bounds__(256) void merge_fast_kernel(int B, int H, const SeqInfo *__restrict__ seqs,
+                                                         const int32_t *__restrict__ dev_len,
+                                                         const float *__restrict__ opart,
+                                                         const float *__restrict__ lse, uint16_t *__restrict__ ohat) {
   using namespace fast;
-  constexpr int OHB = DC * 2 + 16;  // bytes per o^ row in LDS (padded)
-  __shared__ __attribute__((aligned(16))) char oh[32 * OHB];
-  __shared__ __attribute__((aligned(16))) char ohl[32 * OHB];
-  const int i = blockIdx.x, b0 = blockIdx.y * 32;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-
-  // ---- merge: wave w handles sequences b0 + w, + 4, ...; lane covers 8 latent
-  // columns. o^ is kept as a bf16 pair hi + lo (lo = bf16(o^ - hi)), which
-  // carries about 16 significant bits into the W_UV product.
-  for (int sb = w; sb < 32; sb += 4) {
-    const int b = b0 + sb;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (b < B) {
-      const SeqInfo si = seqs[b];
-      if (si.item_count > 0 && dev_len[b] == si.len) {
-        float M = -INFINITY;
-        for (int s = 0; s < si.item_count; ++s) M = fmaxf(M, lse[static_cast<size_t>(si.item_begin + s) * H + i]);
-        float den = 0.0f;
-        for (int s = 0; s < si.item_count; ++s) den += exp2f(lse[static_cast<size_t>(si.item_begin + s) * H + i] - M);
-        const float inv = 1.0f / den;
-        for (int s = 0; s < si.item_count; ++s) {
-          const size_t slot = static_cast<size_t>(si.item_begin + s) * H + i;
-          const float ws = exp2f(lse[slot] - M) * inv;
-          const float4 *src = reinterpret_cast<const float4 *>(opart + slot * DC + 8 * lane);
-          const float4 x0 = src[0], x1 = src[1];
-          acc[0] = fmaf(ws, x0.x, acc[0]); acc[1] = fmaf(ws, x0.y, acc[1]);
-          acc[2] = fmaf(ws, x0.z, acc[2]); acc[3] = fmaf(ws, x0.w, acc[3]);
-          acc[4] = fmaf(ws, x1.x, acc[4]); acc[5] = fmaf(ws, x1.y, acc[5]);
-          acc[6] = fmaf(ws, x1.z, acc[6]); acc[7] = fmaf(ws, x1.w, acc[7]);
+  constexpr int SB = 4;             // splits loaded per batch
+  constexpr int TS = 128 + 4;       // LDS row stride (floats) of the [head][column] tile
+  __shared__ float tile[32 * TS];
+  const int b = blockIdx.x, hb = blockIdx.y, q = blockIdx.z;
+  const int tid = threadIdx.x, g = tid >> 6, lane = tid & 63, hl = lane & 31, half = lane >> 5;
+  const int head = 32 * hb + hl;
+  float4 acc[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) acc[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const SeqInfo si = seqs[b];
+  if (si.item_count > 0 && dev_len[b] == si.len) {
+    const float *lrow = lse + static_cast<size_t>(si.item_begin) * H + head;
+    float M = -INFINITY;
+    for (int s = 0; s < si.item_count; ++s) M = fmaxf(M, lrow[static_cast<size_t>(s) * H]);
+    if (M != -INFINITY) {
+      float den = 0.0f;
+      for (int s = 0; s < si.item_count; ++s) den += exp2f(lrow[static_cast<size_t>(s) * H] - M);
+      const float inv = 1.0f / den;
+      const size_t stride = static_cast<size_t>(H / 32) * 16 * 1024;  // floats per item
+      const float *src = opart + (static_cast<size_t>(si.item_begin) * (H / 32) + hb) * (16 * 1024) +
+                         (16 * q) * 256 + 256 * g + 4 * lane;
+      for (int s0 = 0; s0 < si.item_count; s0 += SB) {
+        float4 x[SB][4];
+        float wt[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const int s = min(s0 + u, si.item_count - 1);
+          wt[u] = s0 + u < si.item_count ? exp2f(lrow[static_cast<size_t>(s) * H] - M) * inv : 0.0f;
+#pragma unroll
+          for (int xx = 0; xx < 4; ++xx) x[u][xx] = *reinterpret_cast<const float4 *>(src + s * stride + 1024 * xx);
         }
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+#pragma unroll
+          for (int xx = 0; xx < 4; ++xx) {
+            acc[xx].x = fmaf(wt[u], x[u][xx].x, acc[xx].x);
+            acc[xx].y = fmaf(wt[u], x[u][xx].y, acc[xx].y);
+            acc[xx].z = fmaf(wt[u], x[u][xx].z, acc[xx].z);
+            acc[xx].w = fmaf(wt[u], x[u][xx].w, acc[xx].w);
+          }
       }
     }
-    bf16x8 hi, lo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      hi[e] = static_cast<__bf16>(acc[e]);
-      lo[e] = static_cast<__bf16>(acc[e] - static_cast<float>(hi[e]));
-    }
-    *reinterpret_cast<bf16x8 *>(oh + sb * OHB + 16 * lane) = hi;
-    *reinterpret_cast<bf16x8 *>(ohl + sb * OHB + 16 * lane) = lo;
   }
+  // to [head][column] in LDS: float4 x holds columns 32 x + 8 g + 4 half + e
+#pragma unroll
+  for (int xx = 0; xx < 4; ++xx)
+    *reinterpret_cast<float4 *>(tile + hl * TS + 32 * xx + 8 * g + 4 * half) = acc[xx];
   __syncthreads();
+  // thread: head hh, 16 columns from c0
+  const int hh = tid >> 3, c0 = 16 * (tid & 7);
+  bf16x8 hi[2], lo[2];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float v = tile[hh * TS + c0 + e];
+    const __bf16 h = static_cast<__bf16>(v);
+    hi[e >> 3][e & 7] = h;
+    lo[e >> 3][e & 7] = static_cast<__bf16>(v - static_cast<float>(h));
+  }
+  uint16_t *dh = ohat + (static_cast<size_t>(32 * hb + hh) * B + b) * DC + 128 * q + c0;
+  uint16_t *dl = dh + static_cast<size_t>(H) * B * DC;
+  *reinterpret_cast<bf16x8 *>(dh) = hi[0];
+  *reinterpret_cast<bf16x8 *>(dh + 8) = hi[1];
+  *reinterpret_cast<bf16x8 *>(dl) = lo[0];
+  *reinterpret_cast<bf16x8 *>(dl + 8) = lo[1];
+}
 
-  // ---- o^T [32 v x 32 b] per wave: A = W_UV,i rows (v = 32 w + l%32, c = 16 kk + 8(l/32)),
-  // B = o^^T (b = l%32, c = 16 kk + 8(l/32)) from LDS, hi and lo parts.
-  const int hl = lane & 31, half = lane >> 5;
-  const uint16_t *wrow = w_uv + (static_cast<size_t>(i) * DV + 32 * w + hl) * DC + 8 * half;
+// ---------------------------------------------------------------- project
+// Grid (H, d_v/32, ceil(B/32)), one wave: o[b, i, v] = W_UV,i[v, :] o^[b, i, :]
+// for 32 values v and 32 sequences, as D^T [32 v x 32 b] = W_UV rows (A,
+// straight from global memory) times o^^T (B: the hi and lo planes, two
+// products per k-step).
+__global__ __launch_bounds__(64) void project_fast_kernel(int B, int H, const uint16_t *__restrict__ ohat,
+                                                          const uint16_t *__restrict__ w_uv, void *o, int o_bf16) {
+  using namespace fast;
+  const int i = blockIdx.x, vb = blockIdx.y, b0 = blockIdx.z * 32;
+  const int lane = threadIdx.x, hl = lane & 31, half = lane >> 5;
+  const int b = b0 + hl;
+  const uint16_t *wrow = w_uv + (static_cast<size_t>(i) * DV + 32 * vb + hl) * DC + 8 * half;
+  const uint16_t *hrow = ohat + (static_cast<size_t>(i) * B + min(b, B - 1)) * DC + 8 * half;
+  const uint16_t *lrow = hrow + static_cast<size_t>(H) * B * DC;
   f32x16 acc = {};
 #pragma unroll 8
   for (int kk = 0; kk < DC / 16; ++kk) {
     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(wrow + 16 * kk);
-    const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(oh + hl * OHB + (16 * kk + 8 * half) * 2);
-    const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(ohl + hl * OHB + (16 * kk + 8 * half) * 2);
+    const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(hrow + 16 * kk);
+    const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(lrow + 16 * kk);
     acc = mfma32(a, bh, acc);
     acc = mfma32(a, bl, acc);
   }
-  // D: lane holds sequence b0 + l%32, v = 32 w + 8(r/4) + 4(l/32) + r%4
-  const int b = b0 + hl;
+  // D: lane holds sequence b0 + l%32, v = 32 vb + 8(r/4) + 4(l/32) + r%4
   if (b < B) {
-    const size_t base = (static_cast<size_t>(b) * H + i) * DV + 32 * w + 4 * half;
+    const size_t base = (static_cast<size_t>(b) * H + i) * DV + 32 * vb + 4 * half;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       if (o_bf16) {
@@ -266,12 +301,17 @@ hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, c
   return hipGetLastError();
 }
 
-hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const SeqInfo *seqs,
-                               const float *opart, const float *lse, const void *w_uv, void *o,
-                               mla_dtype od) {
-  combine_fast_kernel<<<dim3(d.n_heads, (c.batch + 31) / 32), 256, 0, s>>>(
-      c.batch, d.n_heads, seqs, c.seq_len, opart, lse, static_cast<const uint16_t *>(w_uv), o,
-      od == MLA_BF16 ? 1 : 0);
+hipError_t launch_merge_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const SeqInfo *seqs,
+                             const float *opart, const float *lse, uint16_t *ohat) {
+  merge_fast_kernel<<<dim3(c.batch, d.n_heads / 32, fast::DC / 128), 256, 0, s>>>(c.batch, d.n_heads, seqs, c.seq_len,
+                                                                                opart, lse, ohat);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_fast(hipStream_t s, const mla_dims &d, int32_t batch, const uint16_t *ohat,
+                               const void *w_uv, void *o, mla_dtype od) {
+  project_fast_kernel<<<dim3(d.n_heads, fast::DV / 32, (batch + 31) / 32), 64, 0, s>>>(
+      batch, d.n_heads, ohat, static_cast<const uint16_t *>(w_uv), o, od == MLA_BF16 ? 1 : 0);
   return hipGetLastError();
 }
 

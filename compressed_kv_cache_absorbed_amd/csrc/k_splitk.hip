@@ -58,6 +58,7 @@ constexpr int RAW_ROWB = 640;       // fp8 row: 512 codes + 128 bytes k_rope
 constexpr int RAW_TILE = T * RAW_ROWB;          // 20480
 constexpr int RAW_DMA_PER_WAVE = RAW_TILE / 1024 / 4;  // 5
 constexpr int SLACK = 8;            // running max is kept unless exceeded by 2^8
+constexpr int SPF = 3;              // score fragments read ahead of their product
 }  // namespace sk
 
 // fp16 tiles (four stages for bf16 latents; two for fp8 latents)
@@ -71,6 +72,13 @@ __shared__ __attribute__((aligned(1024))) char g_raw1[sk::RAW_TILE];
 __shared__ __attribute__((aligned(1024))) char g_raw2[sk::RAW_TILE];
 __shared__ __attribute__((aligned(256))) float g_scl[3][64];   // by raw buffer
 __shared__ __attribute__((aligned(256))) float g_sclbf[2][32];  // by bf16 buffer
+// P of all 128 heads (fp16, in the layout of the value product's B operand:
+// head block hb, k-step kb, lane l -> 16 bytes at 1024 (2 hb + kb) + 16 l),
+// the per-head rescale factor of the current tile, and the per-head softmax
+// denominators at the end
+__shared__ __attribute__((aligned(1024))) char g_P[8192];
+__shared__ __attribute__((aligned(256))) float g_alpha[128];
+__shared__ __attribute__((aligned(256))) float g_stat[128];
 
 namespace {
 
@@ -180,115 +188,145 @@ struct Item {
   int t0, t1, ntiles;
 };
 
-// Direct-to-LDS copy of bf16 tile `tile` into `dst` in the swizzled layout:
-// load q of wave w fills LDS bytes [1024 q, 1024 q + 1024) of the tile, lane
-// i the 16-byte chunk at physical position 64 q + i. Tokens past the item's
-// end repeat its last row (finite data; masked out of the softmax).
-__device__ __forceinline__ void dma_bf16(uint32_t dst, const Item &it, int tile, int w, int lane) {
+// Where tile `tile` of an item starts in global memory, and the last token
+// of the item relative to it (tokens past it repeat that row: finite data,
+// masked out of the softmax).
+struct TileSrc {
+  const char *base;
+  const char *sbase;  // fp8 scales
+  int stride, tmax;
+};
+__device__ __forceinline__ TileSrc tile_src(const Item &it, int tile) {
   const int ts = it.t0 + tile * sk::T;
-  const int tmax = it.t1 - 1 - ts;
-  const char *base = it.rows + (it.row0 + ts) * it.stride;
-  const int ln = opaque(lane);
-#pragma unroll
-  for (int x = 0; x < sk::DMA_PER_WAVE; ++x) {
-    const int q = sk::DMA_PER_WAVE * w + x;
-    const int P = 64 * q + ln;
-    const int t = P / sk::CH;
-    const int ch = (P - sk::CH * t) ^ swz(t);
-    const uint32_t voff = static_cast<uint32_t>(min(t, tmax) * static_cast<int>(it.stride) + ch * 16);
-    lds_dma16(base, voff, __builtin_amdgcn_readfirstlane(dst + 1024u * q));
-  }
+  TileSrc r;
+  r.base = it.rows + (it.row0 + ts) * it.stride;
+  r.sbase = reinterpret_cast<const char *>(it.scale + it.row0 + ts);
+  r.stride = static_cast<int>(it.stride);
+  r.tmax = it.t1 - 1 - ts;
+  return r;
 }
 
-// Direct-to-LDS copy of raw fp8 tile rows (640 bytes each, unswizzled) plus
-// one 4-byte scale per token (every wave loads the scales, into the same
-// place, so that every wave issues the same number of loads).
-__device__ __forceinline__ void dma_raw(uint32_t dst, uint32_t scl, const Item &it, int tile, int w, int lane) {
-  const int ts = it.t0 + tile * sk::T;
-  const int tmax = it.t1 - 1 - ts;
-  const char *base = it.rows + (it.row0 + ts) * it.stride;
-  const int ln = opaque(lane);
+// Direct-to-LDS load x (of 9) of wave w for a bf16 tile, in the swizzled
+// layout: load q = 9 w + x fills LDS bytes [1024 q, 1024 q + 1024) of the
+// tile, lane i the 16-byte chunk at physical position 64 q + i.
+__device__ __forceinline__ void dma_bf16_piece(uint32_t dst, const TileSrc &src, int w, int lane, int x) {
+  const int q = sk::DMA_PER_WAVE * w + x;
+  const int P = 64 * q + opaque(lane);
+  const int t = P / sk::CH;
+  const int ch = (P - sk::CH * t) ^ swz(t);
+  const uint32_t voff = static_cast<uint32_t>(min(t, src.tmax) * src.stride + ch * 16);
+  lds_dma16(src.base, voff, __builtin_amdgcn_readfirstlane(dst + 1024u * q));
+}
+__device__ __forceinline__ void dma_bf16(uint32_t dst, const Item &it, int tile, int w, int lane) {
+  const TileSrc src = tile_src(it, tile);
 #pragma unroll
-  for (int x = 0; x < sk::RAW_DMA_PER_WAVE; ++x) {
+  for (int x = 0; x < sk::DMA_PER_WAVE; ++x) dma_bf16_piece(dst, src, w, lane, x);
+}
+
+// Direct-to-LDS load x (of 6) of wave w for a raw fp8 tile: x < 5 copies
+// rows (640 bytes each, unswizzled, 40 chunks of 16 bytes), x = 5 the
+// per-token scales (every wave loads them, into the same place, so that
+// every wave issues the same number of loads).
+__device__ __forceinline__ void dma_raw_piece(uint32_t dst, uint32_t scl, const TileSrc &src, int w, int lane, int x) {
+  const int ln = opaque(lane);
+  if (x < sk::RAW_DMA_PER_WAVE) {
     const int q = sk::RAW_DMA_PER_WAVE * w + x;
-    const int P = 64 * q + ln;             // chunk of 16 bytes, 40 per row
+    const int P = 64 * q + ln;
     const int t = P / 40;
     const int ch = P - 40 * t;
-    const uint32_t voff = static_cast<uint32_t>(min(t, tmax) * static_cast<int>(it.stride) + ch * 16);
-    lds_dma16(base, voff, __builtin_amdgcn_readfirstlane(dst + 1024u * q));
+    const uint32_t voff = static_cast<uint32_t>(min(t, src.tmax) * src.stride + ch * 16);
+    lds_dma16(src.base, voff, __builtin_amdgcn_readfirstlane(dst + 1024u * q));
+  } else {
+    lds_dma4(src.sbase, static_cast<uint32_t>(min(ln & 31, src.tmax) * 4), scl);
   }
-  const char *sbase = reinterpret_cast<const char *>(it.scale + it.row0 + ts);
-  lds_dma4(sbase, static_cast<uint32_t>(min(ln & 31, tmax) * 4), scl);
+}
+__device__ __forceinline__ void dma_raw(uint32_t dst, uint32_t scl, const Item &it, int tile, int w, int lane) {
+  const TileSrc src = tile_src(it, tile);
+#pragma unroll
+  for (int x = 0; x <= sk::RAW_DMA_PER_WAVE; ++x) dma_raw_piece(dst, scl, src, w, lane, x);
 }
 
-// Widen a bf16 tile to fp16 in place (2304 chunks of 16 bytes, 9 per thread;
-// the swizzle moves whole chunks, so it is unchanged).
+// Widening a bf16 tile to fp16 in place: 2304 chunks of 16 bytes, 9 per
+// thread (chunk tid + 256 x); the swizzle moves whole chunks, so it is
+// unchanged. Split into load and convert-store so the two can be spread
+// over a matrix-core loop.
+__device__ __forceinline__ u32x4 widen_bf16_load(const char *tile, int tid, int x) {
+  return *reinterpret_cast<const u32x4 *>(tile + (tid + 256 * x) * 16);
+}
+__device__ __forceinline__ void widen_bf16_store(char *tile, int tid, int x, u32x4 v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] = bf16x2_to_f16x2(v[k]);
+  *reinterpret_cast<u32x4 *>(tile + (tid + 256 * x) * 16) = v;
+}
 __device__ __forceinline__ void widen_bf16_inplace(char *tile, int tid_) {
   const int tid = opaque(tid_);
 #pragma unroll
-  for (int x = 0; x < sk::TILE / 16 / 256; ++x) {
-    u32x4 *p = reinterpret_cast<u32x4 *>(tile + (tid + 256 * x) * 16);
-    u32x4 v = *p;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = bf16x2_to_f16x2(v[k]);
-    *p = v;
-  }
+  for (int x = 0; x < sk::TILE / 16 / 256; ++x) widen_bf16_store(tile, tid, x, widen_bf16_load(tile, tid, x));
 }
 
-// Widen a raw fp8 tile into the fp16 tile layout (1280 chunks, 5 per thread)
-// and move its scales next to it.
+// Widening a raw fp8 tile into the fp16 tile layout: 1280 raw chunks, 5 per
+// thread (chunk q = tid + 256 x, token q / 40, chunk q % 40 of the row);
+// a code chunk becomes two fp16 chunks, a k_rope chunk one.
+__device__ __forceinline__ u32x4 widen_fp8_load(const char *raw, int tid, int x) {
+  return *reinterpret_cast<const u32x4 *>(raw + (tid + 256 * x) * 16);
+}
+__device__ __forceinline__ void widen_fp8_store(char *dst, int tid, int x, u32x4 v) {
+  const int q = tid + 256 * x;
+  const int t = q / 40, ch = q - 40 * t;
+  if (ch < 32) {
+    u32x4 lo, hi;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      lo[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k], 1.0f, false));
+      lo[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k], 1.0f, true));
+      hi[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k + 2], 1.0f, false));
+      hi[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k + 2], 1.0f, true));
+    }
+    const int c0 = 2 * ch, c1 = 2 * ch + 1;
+    *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c0 ^ swz(t))) * 16) = lo;
+    *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c1 ^ swz(t))) * 16) = hi;
+  } else {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = bf16x2_to_f16x2(v[k]);
+    const int c = 64 + (ch - 32);
+    *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c ^ swz(t))) * 16) = r;
+  }
+}
 __device__ __forceinline__ void widen_fp8(char *dst, const char *raw, float *dscl, const float *rscl, int tid_) {
   const int tid = opaque(tid_);
   if (tid < sk::T) dscl[tid] = rscl[tid];
 #pragma unroll
-  for (int x = 0; x < sk::RAW_TILE / 16 / 256; ++x) {
-    const int q = tid + 256 * x;
-    const int t = q / 40, ch = q - 40 * t;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(raw + q * 16);
-    if (ch < 32) {
-      u32x4 lo, hi;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        lo[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k], 1.0f, false));
-        lo[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k], 1.0f, true));
-        hi[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k + 2], 1.0f, false));
-        hi[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k + 2], 1.0f, true));
-      }
-      const int c0 = 2 * ch, c1 = 2 * ch + 1;
-      *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c0 ^ swz(t))) * 16) = lo;
-      *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c1 ^ swz(t))) * 16) = hi;
-    } else {
-      u32x4 r;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) r[k] = bf16x2_to_f16x2(v[k]);
-      const int c = 64 + (ch - 32);
-      *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c ^ swz(t))) * 16) = r;
-    }
-  }
+  for (int x = 0; x < sk::RAW_TILE / 16 / 256; ++x) widen_fp8_store(dst, tid, x, widen_fp8_load(raw, tid, x));
 }
 
-// Per-lane state of one wave: Q fragments, the output accumulator, softmax
-// statistics and the lane's LDS base addresses.
+// Per-lane state of one wave. Wave w scores heads 32 w .. 32 w + 31 (its
+// Q fragments and softmax statistics) and accumulates latent columns
+// 128 w .. 128 w + 127 of the output for all 128 heads: O[4 j + hb] holds
+// columns 128 w + 32 j .. +31 of head block hb.
 struct WaveState {
   f16x8 qf[sk::D / 16];   // absorbed query (fp16), B operand of the scores
   f32x16 O[sk::DC / 32];
   float m, l;
   int sbase[4];     // score A-fragment bases, by kk % 4
-  int pbase[2][2];  // value A-fragment bases, by (db % 2, second read)
-  int half;
+  int pbase[2][2];  // value A-fragment bases, by (j % 2, second read)
+  int half, hl, w, lane;
 };
 
-// A-fragment reads. Score fragment kk: token hl, latent/rope dims
-// 16 kk + 8 half .. +7 (one 16-byte read). Value fragment n = 16 kb + db:
-// latent columns 32 db + .., tokens 16 kb + 4 (g/2) + e and + 8 (two
-// transposed 8-byte reads).
+// Fragment reads. Score A fragment kk: token hl, latent/rope dims
+// 16 kk + 8 half .. +7 (one 16-byte read). Value A fragment (j, kb): latent
+// columns 128 w + 32 j + .., tokens 16 kb + 4 (g/2) + e and + 8 (two
+// transposed 8-byte reads). Value B fragment (hb, kb): P of head block hb,
+// k-step kb, as the scoring wave held it.
 __device__ __forceinline__ f16x8 score_frag(const WaveState &st, const char *tb, int kk) {
   return *reinterpret_cast<const f16x8 *>(tb + st.sbase[kk & 3] + 128 * (kk >> 2));
 }
-__device__ __forceinline__ f16x8 value_frag(const WaveState &st, const char *tb, int n) {
-  const int kb = n >> 4, db = n & 15;
-  const char *p0 = tb + st.pbase[db & 1][0] + sk::ROWB * (16 * kb) + 128 * (db >> 1);
-  const char *p1 = tb + st.pbase[db & 1][1] + sk::ROWB * (16 * kb + 8) + 128 * (db >> 1);
+__device__ __forceinline__ f16x8 p_frag(const WaveState &st, int hb, int kb) {
+  return *reinterpret_cast<const f16x8 *>(g_P + 16 * st.lane + 1024 * (2 * hb + kb));
+}
+__device__ __forceinline__ f16x8 value_frag(const WaveState &st, const char *tb, int j, int kb) {
+  const char *p0 = tb + st.pbase[j & 1][0] + sk::ROWB * (16 * kb) + 128 * (j >> 1);
+  const char *p1 = tb + st.pbase[j & 1][1] + sk::ROWB * (16 * kb + 8) + 128 * (j >> 1);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(p0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(p1));
   f16x8 a;
@@ -297,12 +335,66 @@ __device__ __forceinline__ f16x8 value_frag(const WaveState &st, const char *tb,
   return a;
 }
 
+// Work a step hides under the matrix-core loops of the tile it computes:
+// score_step(kk) runs after score product kk, value_step(n) after value
+// product n; each issues at most one load or one convert-and-store.
+//
+// bf16 latents: the 9 direct loads of tile i+3 (one every fourth score
+// product) and the widening of tile i+1 (one chunk every third value
+// product: load, then convert and store two products later).
+template <int DMA_BUF, int WIDEN_BUF>
+struct HideBf16 {
+  TileSrc src;
+  int w, lane, tid;
+  bool dma_on, widen_on;
+  u32x4 v;
+  __device__ __forceinline__ void score_step(int kk) {
+    if (kk % 4 == 0 && kk / 4 < sk::DMA_PER_WAVE && dma_on)
+      dma_bf16_piece(tile_lds<DMA_BUF>(), src, w, lane, kk / 4);
+  }
+  __device__ __forceinline__ void value_step(int n) {
+    constexpr int NX = sk::TILE / 16 / 256;
+    const int x = n / 3;
+    if (x < NX && widen_on) {
+      if (n % 3 == 0) v = widen_bf16_load(tile_buf<WIDEN_BUF>(), tid, x);
+      if (n % 3 == 2) widen_bf16_store(tile_buf<WIDEN_BUF>(), tid, x, v);
+    }
+  }
+};
+
+// fp8 latents: the 6 direct loads of raw tile i+3 (one every sixth score
+// product) and the widening of raw tile i+1 into fp16 buffer (i+1) % 2 (one
+// raw chunk every sixth value product, converted three products later; the
+// scales move with the last one).
+template <int DMA_RAW, int WIDEN_RAW, int WIDEN_BUF>
+struct HideFp8 {
+  TileSrc src;
+  int w, lane, tid;
+  bool dma_on, widen_on;
+  u32x4 v;
+  __device__ __forceinline__ void score_step(int kk) {
+    if (kk % 6 == 0 && kk / 6 <= sk::RAW_DMA_PER_WAVE && dma_on)
+      dma_raw_piece(raw_lds<DMA_RAW>(), scl_lds<DMA_RAW>(), src, w, lane, kk / 6);
+  }
+  __device__ __forceinline__ void value_step(int n) {
+    constexpr int NX = sk::RAW_TILE / 16 / 256;
+    const int x = n / 6;
+    if (x < NX && widen_on) {
+      if (n % 6 == 0) v = widen_fp8_load(raw_buf<WIDEN_RAW>(), tid, x);
+      if (n % 6 == 3) widen_fp8_store(tile_buf<WIDEN_BUF>(), tid, x, v);
+    }
+    if (n == 2 * (sk::DC / 32) - 1 && widen_on && tid < sk::T) g_sclbf[WIDEN_BUF][tid] = g_scl[WIDEN_RAW][tid];
+  }
+};
+
 // One tile: both contractions are software-pipelined by hand (fragment reads
-// run two steps ahead of the matrix-core op that consumes them) and each step
-// is fenced with a scheduling barrier, so the compiler keeps the order and the
-// register footprint small instead of hoisting every read.
-template <bool FP8>
-__device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, const float *tscl, int valid) {
+// run ahead of the matrix-core op that consumes them: three steps for the
+// scores, two for the values) and each step is fenced with a scheduling
+// barrier, so the compiler keeps the order and the register footprint small
+// instead of hoisting every read. The hidden work of the step sits after
+// each product, where it runs while the matrix core is busy.
+template <bool FP8, class Hide>
+__device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, const float *tscl, int valid, Hide &hide) {
   using namespace sk;
   const int half = st.half;
   // ---- S^T = K Q^T. bf16: two alternating chains over all 36 k-steps.
@@ -310,13 +402,13 @@ __device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, cons
   // s = scale Sa + Sb.
   f32x16 Sa, Sb;
   {
-    f16x8 af[3];
-    af[0] = score_frag(st, tb, 0);
-    af[1] = score_frag(st, tb, 1);
+    f16x8 af[SPF + 1];
+#pragma unroll
+    for (int j = 0; j < SPF; ++j) af[j] = score_frag(st, tb, j);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      if (kk + 2 < D / 16) af[(kk + 2) % 3] = score_frag(st, tb, kk + 2);
-      const f16x8 a = af[kk % 3];
+      if (kk + SPF < D / 16) af[(kk + SPF) % (SPF + 1)] = score_frag(st, tb, kk + SPF);
+      const f16x8 a = af[kk % (SPF + 1)];
       if (FP8) {
         if (kk < DC / 16) {
           if (kk == 0) Sa = mfma_vgpr_first(a, st.qf[kk]);
@@ -331,87 +423,129 @@ __device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, cons
         else if (kk & 1) mfma_vgpr_acc(Sb, a, st.qf[kk]);
         else mfma_vgpr_acc(Sa, a, st.qf[kk]);
       }
+      hide.score_step(kk);
       __builtin_amdgcn_sched_barrier(0);
     }
     mfma_vgpr_drain(Sa, Sb);
   }
-  // prefetch the first value fragments under the softmax
-  f16x8 pf[3];
-  pf[0] = value_frag(st, tb, 0);
-  pf[1] = value_frag(st, tb, 1);
   float S[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int tok = 8 * (r >> 2) + 4 * half + (r & 3);
-    const float s = FP8 ? fmaf(Sa[r], tscl[tok], Sb[r]) : Sa[r] + Sb[r];
-    S[r] = tok < valid ? s : -INFINITY;
-  }
-  // ---- online softmax (this lane's head: 16 tokens here, 16 in lane ^ 32)
-  float mx = S[0];
+  for (int r = 0; r < 16; ++r) S[r] = FP8 ? fmaf(Sa[r], tscl[8 * (r >> 2) + 4 * half + (r & 3)], Sb[r]) : Sa[r] + Sb[r];
+  if (valid < T) {  // the item's last tile only
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + 4 * half + (r & 3) >= valid) S[r] = -INFINITY;
+  }
+  // ---- online softmax (this lane's head: 16 tokens here, 16 in lane ^ 32).
+  // Scores are in log2 units; exp2 of a value below -126 may flush to zero,
+  // which is below the fp16 resolution of P anyway.
+  float mx = fmaxf(S[0], S[1]);
+#pragma unroll
+  for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(S[r], S[r + 1]));
   mx = pair_max(mx);
   const float m_new = mx > st.m + SLACK ? mx : st.m;
-  const float alpha = exp2f(st.m - m_new);
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   float psum = 0.0f;
   f16x8 P[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    float p = exp2f(S[r] - m_new);
+    float p = __builtin_amdgcn_exp2f(S[r] - m_new);
     psum += p;
     if (FP8) p *= tscl[8 * (r >> 2) + 4 * half + (r & 3)];
     P[r >> 3][r & 7] = static_cast<_Float16>(p);
   }
   st.l = fmaf(st.l, alpha, pair_sum(psum));
   st.m = m_new;
-  if (__any(alpha != 1.0f)) {
+  // ---- hand P and alpha of this wave's heads to every wave
+  *reinterpret_cast<f16x8 *>(g_P + 16 * st.lane + 1024 * (2 * st.w)) = P[0];
+  *reinterpret_cast<f16x8 *>(g_P + 16 * st.lane + 1024 * (2 * st.w + 1)) = P[1];
+  if (half == 0) g_alpha[32 * st.w + st.hl] = alpha;
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- O^T += C^T P^T over this wave's 128 latent columns, all heads:
+  // k-step kb, column block j, head block hb. The fragments of the next
+  // k-step are read during the second half of the current one.
+  f16x8 fa[2][4], fb[2][4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) fb[0][hb] = p_frag(st, hb, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fa[0][j] = value_frag(st, tb, j, 0);
+  float al[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) al[hb] = g_alpha[32 * hb + st.hl];
+  if (__any(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
     // one 16-register block at a time through VGPRs, back into AGPRs
 #pragma unroll
-    for (int db = 0; db < DC / 32; ++db) {
-      f32x16 t = st.O[db];
+    for (int x = 0; x < DC / 32; ++x) {
+      f32x16 t = st.O[x];
       asm volatile("" : "+v"(t));
-      t *= alpha;
-      st.O[db] = t;
-      asm volatile("" : "+a"(st.O[db]));
+      t *= al[x & 3];
+      st.O[x] = t;
+      asm volatile("" : "+a"(st.O[x]));
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  // ---- O^T += C^T P^T, fragment n = 16 kb + db (consecutive ops hit
-  // different accumulators)
 #pragma unroll
-  for (int n = 0; n < 2 * (DC / 32); ++n) {
-    if (n + 2 < 2 * (DC / 32)) pf[(n + 2) % 3] = value_frag(st, tb, n + 2);
-    const int kb = n >> 4, db = n & 15;
-    st.O[db] = mfma32(pf[n % 3], P[kb], st.O[db]);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      const int j = idx >> 2, hb = idx & 3;
+      if (kb == 0 && idx >= 8) {
+        if (idx < 12) fb[1][idx - 8] = p_frag(st, idx - 8, 1);
+        else fa[1][idx - 12] = value_frag(st, tb, idx - 12, 1);
+      }
+      st.O[4 * j + hb] = mfma32(fa[kb][j], fb[kb][hb], st.O[4 * j + hb]);
+      hide.value_step(16 * kb + idx);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
-// One pipeline step for bf16 latents (B = i % 4): after the barrier, tile
-// i+1 (landed) is widened to fp16 in place, tile i+3 is fetched into the
-// buffer tile i-1 used, and tile i (widened during step i-1) is computed.
-template <int B>
-__device__ __forceinline__ void step_bf16(WaveState &st, const Item &it, int i, int w, int lane, int tid) {
-  if (i + 2 < it.ntiles) wait_vm<sk::DMA_PER_WAVE>(); else wait_vm<0>();
-  __builtin_amdgcn_s_barrier();
-  if (i + 1 < it.ntiles) widen_bf16_inplace(tile_buf<(B + 1) % 4>(), tid);
-  if (i + 3 < it.ntiles) dma_bf16(tile_lds<(B + 3) % 4>(), it, i + 3, w, lane);
-  compute_tile<false>(st, tile_buf<B>(), nullptr, min(sk::T, it.t1 - (it.t0 + i * sk::T)));
+// vmcnt(n) and lgkmcnt(0): this wave's copies into the tile the next step
+// widens have landed, and its own LDS writes are done, before the barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
-// One pipeline step for fp8 latents (B3 = i % 3, B2 = i % 2): after the
-// barrier, raw tile i+1 is widened into fp16 buffer (i+1)%2, raw tile i+3 is
-// fetched into the raw buffer tile i came from, and tile i is computed.
+// One pipeline step for bf16 latents (B = i % 4). After the barrier every
+// wave's copies of tile i+1 have landed and tile i is widened; the step
+// computes tile i while widening tile i+1 in place and fetching tile i+3
+// into the buffer tile i-1 used.
+template <int B>
+__device__ __forceinline__ void step_bf16(WaveState &st, const Item &it, int i, int w, int lane, int tid) {
+  if (i + 2 < it.ntiles) wait_vm_lds<sk::DMA_PER_WAVE>(); else wait_vm_lds<0>();
+  __builtin_amdgcn_s_barrier();
+  HideBf16<(B + 3) % 4, (B + 1) % 4> h;
+  h.src = tile_src(it, i + 3);
+  h.w = w;
+  h.lane = lane;
+  h.tid = opaque(tid);
+  h.dma_on = i + 3 < it.ntiles;
+  h.widen_on = i + 1 < it.ntiles;
+  compute_tile<false>(st, tile_buf<B>(), nullptr, min(sk::T, it.t1 - (it.t0 + i * sk::T)), h);
+}
+
+// One pipeline step for fp8 latents (B3 = i % 3, B2 = i % 2): computes tile
+// i (fp16 buffer B2) while widening raw tile i+1 into fp16 buffer (i+1) % 2
+// and fetching raw tile i+3 into the raw buffer tile i came from.
 template <int B3, int B2>
 __device__ __forceinline__ void step_fp8(WaveState &st, const Item &it, int i, int w, int lane, int tid) {
   constexpr int N3 = (B3 + 1) % 3, N2 = (B2 + 1) % 2;
   constexpr int PER = sk::RAW_DMA_PER_WAVE + 1;
-  if (i + 2 < it.ntiles) wait_vm<PER>(); else wait_vm<0>();
+  if (i + 2 < it.ntiles) wait_vm_lds<PER>(); else wait_vm_lds<0>();
   __builtin_amdgcn_s_barrier();
-  if (i + 1 < it.ntiles) widen_fp8(tile_buf<N2>(), raw_buf<N3>(), g_sclbf[N2], g_scl[N3], tid);
-  if (i + 3 < it.ntiles) dma_raw(raw_lds<B3>(), scl_lds<B3>(), it, i + 3, w, lane);
-  compute_tile<true>(st, tile_buf<B2>(), g_sclbf[B2], min(sk::T, it.t1 - (it.t0 + i * sk::T)));
+  HideFp8<B3, N3, N2> h;
+  h.src = tile_src(it, i + 3);
+  h.w = w;
+  h.lane = lane;
+  h.tid = opaque(tid);
+  h.dma_on = i + 3 < it.ntiles;
+  h.widen_on = i + 1 < it.ntiles;
+  compute_tile<true>(st, tile_buf<B2>(), g_sclbf[B2], min(sk::T, it.t1 - (it.t0 + i * sk::T)), h);
 }
 
 template <bool FP8>
@@ -428,14 +562,16 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
   const int hl = lane & 31, half = lane >> 5;
   const int head = blockIdx.y * 128 + 32 * w + hl;
   const WorkItem wi = items[k];
-  float *op = opart + (static_cast<size_t>(k) * H + head) * DC;
+  // this workgroup's 128 heads of item k: 4 head blocks of 64 KB in the
+  // fragment order of the partials
+  float *ob = opart + (static_cast<size_t>(k) * (H / 32) + blockIdx.y * 4) * (16 * 1024);
 
   const bool ok = c.seq_len[wi.b] == seqs[wi.b].len && wi.t0 >= 0 && wi.t0 < wi.t1 &&
                   wi.t1 <= c.seq_cap[wi.b] && static_cast<int64_t>(c.seq_start[wi.b]) >= 0 &&
                   static_cast<int64_t>(c.seq_start[wi.b]) + wi.t1 <= c.n_rows;
   if (!ok) {
     if (tid == 0 && blockIdx.y == 0) set_status(status, MLA_ERR_PLAN);
-    for (int x = half * 4; x < DC; x += 8) *reinterpret_cast<float4 *>(op + x) = make_float4(0, 0, 0, 0);
+    for (int x = tid; x < 4 * 16 * 256; x += 256) reinterpret_cast<float4 *>(ob)[x] = make_float4(0, 0, 0, 0);
     if (half == 0) lse[static_cast<size_t>(k) * H + head] = -INFINITY;
     return;
   }
@@ -461,6 +597,9 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
 
   WaveState st;
   st.half = half;
+  st.hl = hl;
+  st.w = w;
+  st.lane = lane;
   {
     const uint16_t *qrow = Q + (static_cast<size_t>(wi.b) * H + head) * D + 8 * half;
 #pragma unroll
@@ -482,8 +621,8 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
   }
   // value A fragment (transposed read): 16-lane group g, lane j in it points at
   // token 16 kb + 8 h + tt (tt = 4 (g/2) + j/4), latent column 32 db + dd
-  // (dd = 16 (g%2) + 4 (j%4)); its chunk 4 db + dd/8 lands at
-  //   128 (db / 2) + 16 ((4 (db % 2)) ^ (dd / 8) ^ tt ^ h)  within the row.
+  // (db = 4 w + jb, dd = 16 (g%2) + 4 (j%4)); its chunk 4 db + dd/8 lands at
+  //   256 w + 128 (jb / 2) + 16 ((4 (jb % 2)) ^ (dd / 8) ^ tt ^ h)  within the row.
   {
     const int g = (lane >> 4) & 3, j = lane & 15;
     const int tt = 4 * (g >> 1) + (j >> 2);
@@ -492,7 +631,7 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        st.pbase[a][h] = tt * ROWB + 16 * ((4 * a) ^ (dd >> 3) ^ tt ^ h) + (dd & 7) * 2;
+        st.pbase[a][h] = tt * ROWB + 256 * w + 16 * ((4 * a) ^ (dd >> 3) ^ tt ^ h) + (dd & 7) * 2;
   }
 
   // widen tile 0 before the loop; each step then widens one tile ahead
@@ -522,18 +661,30 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
     }
   }
 
-  // ---- normalised partial and log-sum-exp (base 2) of this head
-  const float inv = 1.0f / st.l;
+  // ---- normalised partials and log-sum-exp (base 2): each wave writes its
+  // 128 latent columns of all 128 heads, dividing by the denominators the
+  // scoring waves hand over
+  if (half == 0) {
+    g_stat[32 * w + hl] = st.l;
+    lse[static_cast<size_t>(k) * H + head] = st.m + log2f(st.l);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  // register group g4 of accumulator (j, hb) is one 1 KB run: head block
+  // hb, latent block 4 w + j
 #pragma unroll
-  for (int db = 0; db < DC / 32; ++db) {
+  for (int hb = 0; hb < 4; ++hb) {
+    const float inv = 1.0f / g_stat[32 * hb + hl];
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = 32 * db + 8 * g4 + 4 * half;
-      *reinterpret_cast<float4 *>(op + d) = make_float4(st.O[db][4 * g4] * inv, st.O[db][4 * g4 + 1] * inv,
-                                                        st.O[db][4 * g4 + 2] * inv, st.O[db][4 * g4 + 3] * inv);
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x16 &x = st.O[4 * j + hb];
+        *reinterpret_cast<float4 *>(ob + ((hb * 16 + 4 * w + j) * 4 + g4) * 256 + 4 * lane) =
+            make_float4(x[4 * g4] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv);
+      }
     }
   }
-  if (half == 0) lse[static_cast<size_t>(k) * H + head] = st.m + log2f(st.l);
 }
 
 }  // namespace
