@@ -67,7 +67,8 @@ static bool force_generic() {
 bool decode_fast_path(const mla_dims &d, const mla_cache &c, mla_dtype q_w_dtype) {
   return !force_generic() && d.d_c == fast::DC && d.d_rope == fast::DR && d.d_nope == fast::DNOPE && d.d_v == fast::DV &&
          d.n_heads % (fast::HPW * fast::WAVES) == 0 && q_w_dtype == MLA_BF16 &&
-         (c.latent_dtype == MLA_BF16 || c.latent_dtype == MLA_FP8_E4M3) && c.rope_dtype == MLA_BF16;
+         (c.latent_dtype == MLA_BF16 || c.latent_dtype == MLA_FP8_E4M3) && c.rope_dtype == MLA_BF16 &&
+         c.row_stride <= (int64_t{1} << 26);  // the split-K copies use 32-bit offsets within a tile
 }
 
 namespace {

@@ -1,30 +1,37 @@
 // Split-K flash-decode over the latent cache (the hot loop of MLA decode).
 //
-// One workgroup per work item (sequence b, tokens [t0, t1)) and 128 heads:
-// 4 waves x 32 heads. For every tile of 32 cached tokens
-//   S^T [32 tok x 32 heads]  = K [32 x 576] Q^T [576 x 32]        (matrix cores)
+// One workgroup per work item (sequence b, tokens [t0, t1)) and 128 heads,
+// four waves. For every tile of 32 cached tokens
+//   S^T [32 tok x 32 heads] = K [32 x 576] Q^T [576 x 32]   wave w: heads 32 w ..
 //   online softmax per head, base 2 (Q is pre-scaled by scale * log2 e)
-//   O^T [512 x 32 heads]    += C^T [512 x 32 tok] P^T [32 tok x 32] (matrix cores)
+//   O^T [128 x 128 heads]  += C^T [128 x 32 tok] P^T [32 tok x 128]
+//                                                     wave w: latent columns 128 w ..
 // where K = [c_kv | k_rope] rows and C = the c_kv part of the same rows: the
 // score is the content term plus the positional term ("DeepSeek MLA" card),
 // and both products read the one tile, reused by all 128 heads, because W_UK
 // is already folded into Q and W_UV is applied after the loop ("02 —
-// Multi-Latent Attention (MLA)", "Coste de cómputo").
+// Multi-Latent Attention (MLA)", "Coste de cómputo"). Each wave scores its
+// own 32 heads, then hands P (fp16) and the rescale factors to every wave
+// through LDS, and accumulates its quarter of the latent columns for all
+// heads: each value fragment is read once and used by four products.
 //
 // Arithmetic: both products take fp16 operands with fp32 accumulation. The
 // absorbed query arrives in fp16; cached bf16 (or e4m3) values are widened to
 // fp16 exactly (any bf16 value below 65504 in magnitude, every e4m3 value).
 //
 // Memory pipeline: each tile is copied global -> LDS with direct-to-LDS loads
-// (global_load_lds_dwordx4, no registers), issued three tiles ahead; after a
-// bare s_barrier plus an explicit vmcnt wait, all waves widen the next tile in
-// LDS while computing the current one. The tile loop is unrolled by the buffer
-// count so every LDS address is a per-lane base plus a constant.
+// (global_load_lds_dwordx4, no registers), issued three tiles ahead and
+// spread over the score products; the widening of the next tile is spread
+// over both products. A bare s_barrier plus explicit waits separates
+// the steps. The tile loop is unrolled by the buffer count so every LDS
+// address is a per-lane base plus a constant.
 //
-// LDS tile layout (16-bit elements): token t occupies 1152 bytes = 72 chunks
-// of 16 bytes; chunk ch of token t sits at position ch ^ swz(t) (XOR on the
-// low three bits, which keeps it inside its group of 8) to spread the
-// fragment reads of both products over the banks.
+// LDS tile layout (16-bit elements), chosen so that both fragment reads are
+// free of bank conflicts and every copy is a plain row copy:
+//   latent: token t at 1072 t (1024 bytes of data + 48 of padding; the odd
+//           stride of 67 chunks of 16 bytes spreads tokens over the banks),
+//   k_rope: token t at 128 t in a region of its own, chunk c of the row at
+//           position c ^ ((t >> 1) & 7).
 //
 // fp8 latents: raw rows [512 e4m3 codes | 64 bf16 k_rope] (640 bytes) are
 // loaded into a raw buffer and widened into the tile layout above; the
@@ -41,44 +48,43 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-#define LDS_VOID(p) ((__attribute__((address_space(3))) void *)(p))
 #define LDS_S16X4(p) ((__attribute__((address_space(3))) s16x4 *)(p))
 // LDS byte offset of a __shared__ array (a link-time constant when applied
 // to the array itself).
 #define LDS_OFF(arr) static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char *)(arr)))
 
 namespace sk {
-constexpr int DC = 512, DR = 64, D = 576;
-constexpr int CH = 72;              // 16-byte chunks per bf16 token row
-constexpr int ROWB = 1152;          // bytes per bf16 token row
-constexpr int T = kTile;            // 32 tokens per tile
-constexpr int TILE = T * ROWB;      // 36864 bytes
-constexpr int DMA_PER_WAVE = TILE / 1024 / 4;  // 9 direct loads of 1 KB per wave
-constexpr int RAW_ROWB = 640;       // fp8 row: 512 codes + 128 bytes k_rope
-constexpr int RAW_TILE = T * RAW_ROWB;          // 20480
+constexpr int DC = 512, D = 576;
+constexpr int T = kTile;             // 32 tokens per tile
+constexpr int LROW = 1072;           // latent row stride in LDS (bytes)
+constexpr int LTILE = T * LROW;      // 34304
+constexpr int RTILE = T * 128;       // 4096: k_rope rows
+constexpr int RAW_ROWB = 640;        // fp8 row: 512 codes + 128 bytes k_rope
+constexpr int RAW_TILE = T * RAW_ROWB;                 // 20480
 constexpr int RAW_DMA_PER_WAVE = RAW_TILE / 1024 / 4;  // 5
-constexpr int SLACK = 8;            // running max is kept unless exceeded by 2^8
-constexpr int SPF = 3;              // score fragments read ahead of their product
+constexpr int SLACK = 8;             // running max is kept unless exceeded by 2^8
+constexpr int SPF = 3;               // score fragments read ahead of their product
+
+// LDS map. bf16 latents: four fp16 tiles. fp8 latents: two fp16 tiles, three
+// raw tiles and their per-token scales. Both: the P exchange (8 KB), the
+// per-head rescale factors and the final denominators.
+template <bool FP8> struct Map {
+  static constexpr int NBUF = FP8 ? 2 : 4;
+  static constexpr int lat(int b) { return LTILE * b; }
+  static constexpr int rope(int b) { return LTILE * NBUF + RTILE * b; }
+  static constexpr int raw(int r) { return LTILE * NBUF + RTILE * NBUF + RAW_TILE * r; }
+  static constexpr int scl(int r) { return raw(3) + 256 * r; }
+  static constexpr int sclbf(int b) { return scl(3) + 128 * b; }
+  static constexpr int px() { return FP8 ? sclbf(2) : rope(NBUF); }
+  static constexpr int alpha() { return px() + 8192; }
+  static constexpr int stat() { return alpha() + 512; }
+  static constexpr int end() { return stat() + 512; }
+};
+constexpr int LDS_BYTES = Map<false>::end() > Map<true>::end() ? Map<false>::end() : Map<true>::end();
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 }  // namespace sk
 
-// fp16 tiles (four stages for bf16 latents; two for fp8 latents)
-__shared__ __attribute__((aligned(1024))) char g_tile0[sk::TILE];
-__shared__ __attribute__((aligned(1024))) char g_tile1[sk::TILE];
-__shared__ __attribute__((aligned(1024))) char g_tile2[sk::TILE];
-__shared__ __attribute__((aligned(1024))) char g_tile3[sk::TILE];
-// raw fp8 tiles and per-token scales (fp8 latents only)
-__shared__ __attribute__((aligned(1024))) char g_raw0[sk::RAW_TILE];
-__shared__ __attribute__((aligned(1024))) char g_raw1[sk::RAW_TILE];
-__shared__ __attribute__((aligned(1024))) char g_raw2[sk::RAW_TILE];
-__shared__ __attribute__((aligned(256))) float g_scl[3][64];   // by raw buffer
-__shared__ __attribute__((aligned(256))) float g_sclbf[2][32];  // by bf16 buffer
-// P of all 128 heads (fp16, in the layout of the value product's B operand:
-// head block hb, k-step kb, lane l -> 16 bytes at 1024 (2 hb + kb) + 16 l),
-// the per-head rescale factor of the current tile, and the per-head softmax
-// denominators at the end
-__shared__ __attribute__((aligned(1024))) char g_P[8192];
-__shared__ __attribute__((aligned(256))) float g_alpha[128];
-__shared__ __attribute__((aligned(256))) float g_stat[128];
+__shared__ __attribute__((aligned(1024))) char g_lds[sk::LDS_BYTES];
 
 namespace {
 
@@ -111,6 +117,9 @@ __device__ __forceinline__ void mfma_vgpr_acc(f32x16 &c, f16x8 a, f16x8 b) {
 __device__ __forceinline__ void mfma_vgpr_drain(f32x16 &x, f32x16 &y) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
+__device__ __forceinline__ void mfma_vgpr_drain(f32x16 &x) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
+}
 
 // 2 bf16 (one dword) -> 2 fp16, exact for |x| < 65504 (a bf16 significand
 // fits in fp16's); round-toward-zero saturates larger magnitudes to +-65504.
@@ -128,7 +137,8 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ int swz(int t) { return (t & 7) ^ ((t >> 3) & 1); }
+// k_rope chunk swizzle: chunk c of token t's row sits at c ^ rsw(t).
+__device__ __forceinline__ int rsw(int t) { return (t >> 1) & 7; }
 
 // A copy of a thread index the compiler cannot see through, so per-tile
 // address arithmetic is recomputed in place instead of hoisted into live
@@ -144,22 +154,14 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-
-template <int B> __device__ __forceinline__ char *tile_buf() {
-  return B == 0 ? g_tile0 : (B == 1 ? g_tile1 : (B == 2 ? g_tile2 : g_tile3));
+// vmcnt(n) and lgkmcnt(0): this wave's copies into the tile the next step
+// widens have landed, and its own LDS writes are done, before the barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
-template <int B> __device__ __forceinline__ char *raw_buf() {
-  return B == 0 ? g_raw0 : (B == 1 ? g_raw1 : g_raw2);
-}
-template <int B> __device__ __forceinline__ uint32_t tile_lds() {
-  return B == 0 ? LDS_OFF(g_tile0) : (B == 1 ? LDS_OFF(g_tile1) : (B == 2 ? LDS_OFF(g_tile2) : LDS_OFF(g_tile3)));
-}
-template <int B> __device__ __forceinline__ uint32_t raw_lds() {
-  return B == 0 ? LDS_OFF(g_raw0) : (B == 1 ? LDS_OFF(g_raw1) : LDS_OFF(g_raw2));
-}
-template <int B> __device__ __forceinline__ uint32_t scl_lds() {
-  return LDS_OFF(g_scl) + 256u * B;
-}
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 // Direct-to-LDS loads (global_load_lds_dword / _dwordx4, SGPR base + 32-bit
 // lane offset): lane i's 4 / 16 bytes from base + voff land at LDS byte
@@ -181,6 +183,7 @@ __device__ __forceinline__ void lds_dma4(const char *base, uint32_t voff, uint32
                : "v"(voff), "s"(base), "s"(lds_addr)
                : "memory", "m0");
 }
+
 struct Item {
   const char *rows;
   const float *scale;
@@ -188,89 +191,116 @@ struct Item {
   int t0, t1, ntiles;
 };
 
-// Where tile `tile` of an item starts in global memory, and the last token
-// of the item relative to it (tokens past it repeat that row: finite data,
-// masked out of the softmax).
+// Where tile `tile` of an item starts in global memory, and its last valid
+// token (tokens past it repeat that row: finite data, masked out of the
+// softmax).
 struct TileSrc {
-  const char *base;
+  const char *base;   // row of the tile's first token
   const char *sbase;  // fp8 scales
-  int stride, tmax;
+  int64_t stride;
+  int tmax;
 };
 __device__ __forceinline__ TileSrc tile_src(const Item &it, int tile) {
   const int ts = it.t0 + tile * sk::T;
   TileSrc r;
   r.base = it.rows + (it.row0 + ts) * it.stride;
   r.sbase = reinterpret_cast<const char *>(it.scale + it.row0 + ts);
-  r.stride = static_cast<int>(it.stride);
+  r.stride = it.stride;
   r.tmax = it.t1 - 1 - ts;
   return r;
 }
 
-// Direct-to-LDS load x (of 9) of wave w for a bf16 tile, in the swizzled
-// layout: load q = 9 w + x fills LDS bytes [1024 q, 1024 q + 1024) of the
-// tile, lane i the 16-byte chunk at physical position 64 q + i.
-__device__ __forceinline__ void dma_bf16_piece(uint32_t dst, const TileSrc &src, int w, int lane, int x) {
-  const int q = sk::DMA_PER_WAVE * w + x;
-  const int P = 64 * q + opaque(lane);
-  const int t = P / sk::CH;
-  const int ch = (P - sk::CH * t) ^ swz(t);
-  const uint32_t voff = static_cast<uint32_t>(min(t, src.tmax) * src.stride + ch * 16);
-  lds_dma16(src.base, voff, __builtin_amdgcn_readfirstlane(dst + 1024u * q));
+// bf16 tile copy, 9 loads per wave (w uniform): x < 8 copies the 1024 latent
+// bytes of token 8 w + x into its LDS row (lane i: bytes 16 i .. 16 i + 15);
+// x = 8 copies the k_rope parts of tokens 8 w .. 8 w + 7 (lane i: token
+// 8 w + i / 8, physical chunk i % 8, which holds chunk (i % 8) ^ rsw(token)).
+template <int B>
+__device__ __forceinline__ void dma_bf16_piece(const TileSrc &src, int w, int lane, int x) {
+  using M = sk::Map<false>;
+  const uint32_t lds0 = LDS_OFF(g_lds);
+  if (x < 8) {
+    const int t = 8 * w + x;
+    const char *row = src.base + static_cast<int64_t>(min(t, src.tmax)) * src.stride;
+    lds_dma16(row, static_cast<uint32_t>(16 * lane), lds0 + M::lat(B) + sk::LROW * t);
+  } else {
+    const int ln = opaque(lane);
+    const int t = 8 * w + (ln >> 3);
+    const uint32_t voff = static_cast<uint32_t>(min(t, src.tmax)) * static_cast<uint32_t>(src.stride) + 1024u +
+                          16u * static_cast<uint32_t>((ln & 7) ^ rsw(t));
+    lds_dma16(src.base, voff, lds0 + M::rope(B) + 1024 * w);
+  }
 }
-__device__ __forceinline__ void dma_bf16(uint32_t dst, const Item &it, int tile, int w, int lane) {
+template <int B>
+__device__ __forceinline__ void dma_bf16(const Item &it, int tile, int w, int lane) {
   const TileSrc src = tile_src(it, tile);
 #pragma unroll
-  for (int x = 0; x < sk::DMA_PER_WAVE; ++x) dma_bf16_piece(dst, src, w, lane, x);
+  for (int x = 0; x < 9; ++x) dma_bf16_piece<B>(src, w, lane, x);
 }
 
-// Direct-to-LDS load x (of 6) of wave w for a raw fp8 tile: x < 5 copies
-// rows (640 bytes each, unswizzled, 40 chunks of 16 bytes), x = 5 the
-// per-token scales (every wave loads them, into the same place, so that
-// every wave issues the same number of loads).
-__device__ __forceinline__ void dma_raw_piece(uint32_t dst, uint32_t scl, const TileSrc &src, int w, int lane, int x) {
+// Raw fp8 tile copy, 6 loads per wave: x < 5 copies rows (640 bytes each,
+// unswizzled, 40 chunks of 16 bytes), x = 5 the per-token scales (every wave
+// loads them, into the same place, so that every wave issues the same number
+// of loads).
+template <int R>
+__device__ __forceinline__ void dma_raw_piece(const TileSrc &src, int w, int lane, int x) {
+  using M = sk::Map<true>;
+  const uint32_t lds0 = LDS_OFF(g_lds);
   const int ln = opaque(lane);
   if (x < sk::RAW_DMA_PER_WAVE) {
     const int q = sk::RAW_DMA_PER_WAVE * w + x;
     const int P = 64 * q + ln;
     const int t = P / 40;
     const int ch = P - 40 * t;
-    const uint32_t voff = static_cast<uint32_t>(min(t, src.tmax) * src.stride + ch * 16);
-    lds_dma16(src.base, voff, __builtin_amdgcn_readfirstlane(dst + 1024u * q));
+    const uint32_t voff = static_cast<uint32_t>(min(t, src.tmax) * static_cast<int>(src.stride) + ch * 16);
+    lds_dma16(src.base, voff, __builtin_amdgcn_readfirstlane(lds0 + M::raw(R) + 1024u * q));
   } else {
-    lds_dma4(src.sbase, static_cast<uint32_t>(min(ln & 31, src.tmax) * 4), scl);
+    lds_dma4(src.sbase, static_cast<uint32_t>(min(ln & 31, src.tmax) * 4), lds0 + M::scl(R));
   }
 }
-__device__ __forceinline__ void dma_raw(uint32_t dst, uint32_t scl, const Item &it, int tile, int w, int lane) {
+template <int R>
+__device__ __forceinline__ void dma_raw(const Item &it, int tile, int w, int lane) {
   const TileSrc src = tile_src(it, tile);
 #pragma unroll
-  for (int x = 0; x <= sk::RAW_DMA_PER_WAVE; ++x) dma_raw_piece(dst, scl, src, w, lane, x);
+  for (int x = 0; x <= sk::RAW_DMA_PER_WAVE; ++x) dma_raw_piece<R>(src, w, lane, x);
 }
 
-// Widening a bf16 tile to fp16 in place: 2304 chunks of 16 bytes, 9 per
-// thread (chunk tid + 256 x); the swizzle moves whole chunks, so it is
-// unchanged. Split into load and convert-store so the two can be spread
-// over a matrix-core loop.
-__device__ __forceinline__ u32x4 widen_bf16_load(const char *tile, int tid, int x) {
-  return *reinterpret_cast<const u32x4 *>(tile + (tid + 256 * x) * 16);
+// Widening a bf16 tile to fp16 in place, 9 chunks of 16 bytes per thread:
+// x < 8: latent token (tid / 64) + 4 x, bytes 16 (tid % 64) ..; x = 8: k_rope
+// chunk tid. Split into load and convert-store so the two can be spread over
+// a matrix-core loop.
+template <int B>
+__device__ __forceinline__ char *widen_bf16_addr(int tid, int x) {
+  using M = sk::Map<false>;
+  return x < 8 ? g_lds + M::lat(B) + sk::LROW * ((tid >> 6) + 4 * x) + 16 * (tid & 63)
+               : g_lds + M::rope(B) + 16 * tid;
 }
-__device__ __forceinline__ void widen_bf16_store(char *tile, int tid, int x, u32x4 v) {
+template <int B>
+__device__ __forceinline__ u32x4 widen_bf16_load(int tid, int x) {
+  return *reinterpret_cast<const u32x4 *>(widen_bf16_addr<B>(tid, x));
+}
+template <int B>
+__device__ __forceinline__ void widen_bf16_store(int tid, int x, u32x4 v) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) v[k] = bf16x2_to_f16x2(v[k]);
-  *reinterpret_cast<u32x4 *>(tile + (tid + 256 * x) * 16) = v;
+  *reinterpret_cast<u32x4 *>(widen_bf16_addr<B>(tid, x)) = v;
 }
-__device__ __forceinline__ void widen_bf16_inplace(char *tile, int tid_) {
+template <int B>
+__device__ __forceinline__ void widen_bf16_inplace(int tid_) {
   const int tid = opaque(tid_);
 #pragma unroll
-  for (int x = 0; x < sk::TILE / 16 / 256; ++x) widen_bf16_store(tile, tid, x, widen_bf16_load(tile, tid, x));
+  for (int x = 0; x < 9; ++x) widen_bf16_store<B>(tid, x, widen_bf16_load<B>(tid, x));
 }
 
-// Widening a raw fp8 tile into the fp16 tile layout: 1280 raw chunks, 5 per
-// thread (chunk q = tid + 256 x, token q / 40, chunk q % 40 of the row);
-// a code chunk becomes two fp16 chunks, a k_rope chunk one.
-__device__ __forceinline__ u32x4 widen_fp8_load(const char *raw, int tid, int x) {
-  return *reinterpret_cast<const u32x4 *>(raw + (tid + 256 * x) * 16);
+// Widening a raw fp8 tile into an fp16 tile: 1280 raw chunks, 5 per thread
+// (chunk q = tid + 256 x: token q / 40, chunk q % 40 of the row); a code
+// chunk becomes two latent fp16 chunks, a k_rope chunk one.
+template <int R>
+__device__ __forceinline__ u32x4 widen_fp8_load(int tid, int x) {
+  return *reinterpret_cast<const u32x4 *>(g_lds + sk::Map<true>::raw(R) + (tid + 256 * x) * 16);
 }
-__device__ __forceinline__ void widen_fp8_store(char *dst, int tid, int x, u32x4 v) {
+template <int B>
+__device__ __forceinline__ void widen_fp8_store(int tid, int x, u32x4 v) {
+  using M = sk::Map<true>;
   const int q = tid + 256 * x;
   const int t = q / 40, ch = q - 40 * t;
   if (ch < 32) {
@@ -282,22 +312,24 @@ __device__ __forceinline__ void widen_fp8_store(char *dst, int tid, int x, u32x4
       hi[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k + 2], 1.0f, false));
       hi[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k + 2], 1.0f, true));
     }
-    const int c0 = 2 * ch, c1 = 2 * ch + 1;
-    *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c0 ^ swz(t))) * 16) = lo;
-    *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c1 ^ swz(t))) * 16) = hi;
+    char *row = g_lds + M::lat(B) + sk::LROW * t + 32 * ch;
+    *reinterpret_cast<u32x4 *>(row) = lo;
+    *reinterpret_cast<u32x4 *>(row + 16) = hi;
   } else {
     u32x4 r;
 #pragma unroll
     for (int k = 0; k < 4; ++k) r[k] = bf16x2_to_f16x2(v[k]);
-    const int c = 64 + (ch - 32);
-    *reinterpret_cast<u32x4 *>(dst + (t * sk::CH + (c ^ swz(t))) * 16) = r;
+    *reinterpret_cast<u32x4 *>(g_lds + M::rope(B) + 128 * t + 16 * ((ch - 32) ^ rsw(t))) = r;
   }
 }
-__device__ __forceinline__ void widen_fp8(char *dst, const char *raw, float *dscl, const float *rscl, int tid_) {
+template <int R, int B>
+__device__ __forceinline__ void widen_fp8(int tid_) {
+  using M = sk::Map<true>;
   const int tid = opaque(tid_);
-  if (tid < sk::T) dscl[tid] = rscl[tid];
+  if (tid < sk::T)
+    reinterpret_cast<float *>(g_lds + M::sclbf(B))[tid] = reinterpret_cast<const float *>(g_lds + M::scl(R))[tid];
 #pragma unroll
-  for (int x = 0; x < sk::RAW_TILE / 16 / 256; ++x) widen_fp8_store(dst, tid, x, widen_fp8_load(raw, tid, x));
+  for (int x = 0; x < sk::RAW_TILE / 16 / 256; ++x) widen_fp8_store<B>(tid, x, widen_fp8_load<R>(tid, x));
 }
 
 // Per-lane state of one wave. Wave w scores heads 32 w .. 32 w + 31 (its
@@ -308,25 +340,34 @@ struct WaveState {
   f16x8 qf[sk::D / 16];   // absorbed query (fp16), B operand of the scores
   f32x16 O[sk::DC / 32];
   float m, l;
-  int sbase[4];     // score A-fragment bases, by kk % 4
-  int pbase[2][2];  // value A-fragment bases, by (j % 2, second read)
+  int sl, sl2;   // latent score-fragment base (tiles 0, 1) and its copy for tiles 2, 3
+  int sr[4];     // k_rope score-fragment bases, by k-step
+  int vl, vl2;   // value-fragment base (tiles 0, 1) and its copy for tiles 2, 3
   int half, hl, w, lane;
 };
 
-// Fragment reads. Score A fragment kk: token hl, latent/rope dims
-// 16 kk + 8 half .. +7 (one 16-byte read). Value A fragment (j, kb): latent
-// columns 128 w + 32 j + .., tokens 16 kb + 4 (g/2) + e and + 8 (two
-// transposed 8-byte reads). Value B fragment (hb, kb): P of head block hb,
-// k-step kb, as the scoring wave held it.
-__device__ __forceinline__ f16x8 score_frag(const WaveState &st, const char *tb, int kk) {
-  return *reinterpret_cast<const f16x8 *>(tb + st.sbase[kk & 3] + 128 * (kk >> 2));
+// Fragment reads. Score A fragment kk: token hl, dims 16 kk + 8 half .. +7
+// (one 16-byte read; latent for kk < 32, k_rope after). Value A fragment
+// (j, kb): latent columns 128 w + 32 j + .., tokens 16 kb + 4 (g/2) + e and
+// + 8 (two transposed 8-byte reads). Value B fragment (hb, kb): P of head
+// block hb, k-step kb, as the scoring wave held it.
+template <bool FP8, int B>
+__device__ __forceinline__ f16x8 score_frag(const WaveState &st, int kk) {
+  using M = sk::Map<FP8>;
+  const char *p = kk < 32 ? (B < 2 ? g_lds + st.sl + M::lat(B) : g_lds + st.sl2 + (M::lat(B) - M::lat(2))) + 32 * kk
+                          : g_lds + st.sr[kk - 32] + (M::rope(B) - M::rope(0));
+  return *reinterpret_cast<const f16x8 *>(p);
 }
+template <bool FP8>
 __device__ __forceinline__ f16x8 p_frag(const WaveState &st, int hb, int kb) {
-  return *reinterpret_cast<const f16x8 *>(g_P + 16 * st.lane + 1024 * (2 * hb + kb));
+  return *reinterpret_cast<const f16x8 *>(g_lds + sk::Map<FP8>::px() + 16 * st.lane + 1024 * (2 * hb + kb));
 }
-__device__ __forceinline__ f16x8 value_frag(const WaveState &st, const char *tb, int j, int kb) {
-  const char *p0 = tb + st.pbase[j & 1][0] + sk::ROWB * (16 * kb) + 128 * (j >> 1);
-  const char *p1 = tb + st.pbase[j & 1][1] + sk::ROWB * (16 * kb + 8) + 128 * (j >> 1);
+template <bool FP8, int B>
+__device__ __forceinline__ f16x8 value_frag(const WaveState &st, int j, int kb) {
+  using M = sk::Map<FP8>;
+  const char *p0 = (B < 2 ? g_lds + st.vl + M::lat(B) : g_lds + st.vl2 + (M::lat(B) - M::lat(2))) +
+                   sk::LROW * 16 * kb + 64 * j;
+  const char *p1 = p0 + sk::LROW * 8;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(p0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(p1));
   f16x8 a;
@@ -340,8 +381,11 @@ __device__ __forceinline__ f16x8 value_frag(const WaveState &st, const char *tb,
 // product n; each issues at most one load or one convert-and-store.
 //
 // bf16 latents: the 9 direct loads of tile i+3 (one every fourth score
-// product) and the widening of tile i+1 (one chunk every third value
-// product: load, then convert and store two products later).
+// product) and the widening of tile i+1, 9 chunks per thread: chunks 0..4
+// under the score products (load at 7 x + 2, convert and store four
+// products later), chunks 5..8 under the value products (load at
+// 8 (x - 5), store four products later). Spreading it keeps the vector-ALU
+// work next to each matrix-core op small enough to run in its shadow.
 template <int DMA_BUF, int WIDEN_BUF>
 struct HideBf16 {
   TileSrc src;
@@ -349,15 +393,18 @@ struct HideBf16 {
   bool dma_on, widen_on;
   u32x4 v;
   __device__ __forceinline__ void score_step(int kk) {
-    if (kk % 4 == 0 && kk / 4 < sk::DMA_PER_WAVE && dma_on)
-      dma_bf16_piece(tile_lds<DMA_BUF>(), src, w, lane, kk / 4);
+    if (kk % 4 == 0 && kk / 4 < 9 && dma_on) dma_bf16_piece<DMA_BUF>(src, w, lane, kk / 4);
+    if (kk >= 2 && (kk - 2) / 7 < 5 && widen_on) {
+      const int x = (kk - 2) / 7, ph = (kk - 2) % 7;
+      if (ph == 0) v = widen_bf16_load<WIDEN_BUF>(tid, x);
+      if (ph == 4) widen_bf16_store<WIDEN_BUF>(tid, x, v);
+    }
   }
   __device__ __forceinline__ void value_step(int n) {
-    constexpr int NX = sk::TILE / 16 / 256;
-    const int x = n / 3;
-    if (x < NX && widen_on) {
-      if (n % 3 == 0) v = widen_bf16_load(tile_buf<WIDEN_BUF>(), tid, x);
-      if (n % 3 == 2) widen_bf16_store(tile_buf<WIDEN_BUF>(), tid, x, v);
+    const int x = 5 + n / 8, ph = n % 8;
+    if (x < 9 && widen_on) {
+      if (ph == 0) v = widen_bf16_load<WIDEN_BUF>(tid, x);
+      if (ph == 4) widen_bf16_store<WIDEN_BUF>(tid, x, v);
     }
   }
 };
@@ -373,41 +420,46 @@ struct HideFp8 {
   bool dma_on, widen_on;
   u32x4 v;
   __device__ __forceinline__ void score_step(int kk) {
-    if (kk % 6 == 0 && kk / 6 <= sk::RAW_DMA_PER_WAVE && dma_on)
-      dma_raw_piece(raw_lds<DMA_RAW>(), scl_lds<DMA_RAW>(), src, w, lane, kk / 6);
+    if (kk % 6 == 0 && kk / 6 <= sk::RAW_DMA_PER_WAVE && dma_on) dma_raw_piece<DMA_RAW>(src, w, lane, kk / 6);
   }
   __device__ __forceinline__ void value_step(int n) {
+    using M = sk::Map<true>;
     constexpr int NX = sk::RAW_TILE / 16 / 256;
     const int x = n / 6;
     if (x < NX && widen_on) {
-      if (n % 6 == 0) v = widen_fp8_load(raw_buf<WIDEN_RAW>(), tid, x);
-      if (n % 6 == 3) widen_fp8_store(tile_buf<WIDEN_BUF>(), tid, x, v);
+      if (n % 6 == 0) v = widen_fp8_load<WIDEN_RAW>(tid, x);
+      if (n % 6 == 3) widen_fp8_store<WIDEN_BUF>(tid, x, v);
     }
-    if (n == 2 * (sk::DC / 32) - 1 && widen_on && tid < sk::T) g_sclbf[WIDEN_BUF][tid] = g_scl[WIDEN_RAW][tid];
+    if (n == 2 * (sk::DC / 32) - 1 && widen_on && tid < sk::T)
+      reinterpret_cast<float *>(g_lds + M::sclbf(WIDEN_BUF))[tid] =
+          reinterpret_cast<const float *>(g_lds + M::scl(WIDEN_RAW))[tid];
   }
 };
 
-// One tile: both contractions are software-pipelined by hand (fragment reads
-// run ahead of the matrix-core op that consumes them: three steps for the
-// scores, two for the values) and each step is fenced with a scheduling
-// barrier, so the compiler keeps the order and the register footprint small
-// instead of hoisting every read. The hidden work of the step sits after
-// each product, where it runs while the matrix core is busy.
-template <bool FP8, class Hide>
-__device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, const float *tscl, int valid, Hide &hide) {
+// One tile (fp16 buffer B): both contractions are software-pipelined by hand
+// (fragment reads run ahead of the matrix-core op that consumes them) and
+// each step is fenced with a scheduling barrier, so the compiler keeps the
+// order and the register footprint small instead of hoisting every read. The
+// hidden work of the step sits after each product, where it runs while the
+// matrix core is busy.
+template <bool FP8, int B, class Hide>
+__device__ __forceinline__ void compute_tile(WaveState &st, int valid, Hide &hide) {
   using namespace sk;
+  using M = Map<FP8>;
   const int half = st.half;
-  // ---- S^T = K Q^T. bf16: two alternating chains over all 36 k-steps.
+  const float *tscl = reinterpret_cast<const float *>(g_lds + M::sclbf(B));
+  // ---- S^T = K Q^T. bf16: one chain over all 36 k-steps (back-to-back
+  // accumulation into the same registers runs at the full matrix-core rate).
   // fp8: Sa accumulates the 32 latent k-steps, Sb the 4 RoPE k-steps;
   // s = scale Sa + Sb.
   f32x16 Sa, Sb;
   {
     f16x8 af[SPF + 1];
 #pragma unroll
-    for (int j = 0; j < SPF; ++j) af[j] = score_frag(st, tb, j);
+    for (int j = 0; j < SPF; ++j) af[j] = score_frag<FP8, B>(st, j);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      if (kk + SPF < D / 16) af[(kk + SPF) % (SPF + 1)] = score_frag(st, tb, kk + SPF);
+      if (kk + SPF < D / 16) af[(kk + SPF) % (SPF + 1)] = score_frag<FP8, B>(st, kk + SPF);
       const f16x8 a = af[kk % (SPF + 1)];
       if (FP8) {
         if (kk < DC / 16) {
@@ -419,19 +471,19 @@ __device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, cons
         }
       } else {
         if (kk == 0) Sa = mfma_vgpr_first(a, st.qf[kk]);
-        else if (kk == 1) Sb = mfma_vgpr_first(a, st.qf[kk]);
-        else if (kk & 1) mfma_vgpr_acc(Sb, a, st.qf[kk]);
         else mfma_vgpr_acc(Sa, a, st.qf[kk]);
       }
       hide.score_step(kk);
       __builtin_amdgcn_sched_barrier(0);
     }
-    mfma_vgpr_drain(Sa, Sb);
+    if (FP8) mfma_vgpr_drain(Sa, Sb);
+    else mfma_vgpr_drain(Sa);
   }
   float S[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) S[r] = FP8 ? fmaf(Sa[r], tscl[8 * (r >> 2) + 4 * half + (r & 3)], Sb[r]) : Sa[r] + Sb[r];
-  if (valid < T) {  // the item's last tile only
+  for (int r = 0; r < 16; ++r) S[r] = FP8 ? fmaf(Sa[r], tscl[8 * (r >> 2) + 4 * half + (r & 3)], Sb[r]) : Sa[r];
+  if (valid < T) {  // the item's last tile only (a real branch: the asm cannot be speculated)
+    asm volatile("; tail mask");
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       if (8 * (r >> 2) + 4 * half + (r & 3) >= valid) S[r] = -INFINITY;
@@ -457,10 +509,11 @@ __device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, cons
   st.l = fmaf(st.l, alpha, pair_sum(psum));
   st.m = m_new;
   // ---- hand P and alpha of this wave's heads to every wave
-  *reinterpret_cast<f16x8 *>(g_P + 16 * st.lane + 1024 * (2 * st.w)) = P[0];
-  *reinterpret_cast<f16x8 *>(g_P + 16 * st.lane + 1024 * (2 * st.w + 1)) = P[1];
-  if (half == 0) g_alpha[32 * st.w + st.hl] = alpha;
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  char *px = g_lds + M::px() + 16 * st.lane + 2048 * st.w;
+  *reinterpret_cast<f16x8 *>(px) = P[0];
+  *reinterpret_cast<f16x8 *>(px + 1024) = P[1];
+  if (half == 0) reinterpret_cast<float *>(g_lds + M::alpha())[32 * st.w + st.hl] = alpha;
+  wait_lds();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   // ---- O^T += C^T P^T over this wave's 128 latent columns, all heads:
@@ -468,12 +521,12 @@ __device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, cons
   // k-step are read during the second half of the current one.
   f16x8 fa[2][4], fb[2][4];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) fb[0][hb] = p_frag(st, hb, 0);
+  for (int hb = 0; hb < 4; ++hb) fb[0][hb] = p_frag<FP8>(st, hb, 0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fa[0][j] = value_frag(st, tb, j, 0);
+  for (int j = 0; j < 4; ++j) fa[0][j] = value_frag<FP8, B>(st, j, 0);
   float al[4];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) al[hb] = g_alpha[32 * hb + st.hl];
+  for (int hb = 0; hb < 4; ++hb) al[hb] = reinterpret_cast<const float *>(g_lds + M::alpha())[32 * hb + st.hl];
   if (__any(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
     // one 16-register block at a time through VGPRs, back into AGPRs
 #pragma unroll
@@ -493,8 +546,8 @@ __device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, cons
     for (int idx = 0; idx < 16; ++idx) {
       const int j = idx >> 2, hb = idx & 3;
       if (kb == 0 && idx >= 8) {
-        if (idx < 12) fb[1][idx - 8] = p_frag(st, idx - 8, 1);
-        else fa[1][idx - 12] = value_frag(st, tb, idx - 12, 1);
+        if (idx < 12) fb[1][idx - 8] = p_frag<FP8>(st, idx - 8, 1);
+        else fa[1][idx - 12] = value_frag<FP8, B>(st, idx - 12, 1);
       }
       st.O[4 * j + hb] = mfma32(fa[kb][j], fb[kb][hb], st.O[4 * j + hb]);
       hide.value_step(16 * kb + idx);
@@ -503,21 +556,13 @@ __device__ __forceinline__ void compute_tile(WaveState &st, const char *tb, cons
   }
 }
 
-// vmcnt(n) and lgkmcnt(0): this wave's copies into the tile the next step
-// widens have landed, and its own LDS writes are done, before the barrier.
-template <int N>
-__device__ __forceinline__ void wait_vm_lds() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
-}
-
 // One pipeline step for bf16 latents (B = i % 4). After the barrier every
 // wave's copies of tile i+1 have landed and tile i is widened; the step
 // computes tile i while widening tile i+1 in place and fetching tile i+3
 // into the buffer tile i-1 used.
 template <int B>
 __device__ __forceinline__ void step_bf16(WaveState &st, const Item &it, int i, int w, int lane, int tid) {
-  if (i + 2 < it.ntiles) wait_vm_lds<sk::DMA_PER_WAVE>(); else wait_vm_lds<0>();
+  if (i + 2 < it.ntiles) wait_vm_lds<9>(); else wait_vm_lds<0>();
   __builtin_amdgcn_s_barrier();
   HideBf16<(B + 3) % 4, (B + 1) % 4> h;
   h.src = tile_src(it, i + 3);
@@ -526,7 +571,7 @@ __device__ __forceinline__ void step_bf16(WaveState &st, const Item &it, int i, 
   h.tid = opaque(tid);
   h.dma_on = i + 3 < it.ntiles;
   h.widen_on = i + 1 < it.ntiles;
-  compute_tile<false>(st, tile_buf<B>(), nullptr, min(sk::T, it.t1 - (it.t0 + i * sk::T)), h);
+  compute_tile<false, B>(st, min(sk::T, it.t1 - (it.t0 + i * sk::T)), h);
 }
 
 // One pipeline step for fp8 latents (B3 = i % 3, B2 = i % 2): computes tile
@@ -545,7 +590,7 @@ __device__ __forceinline__ void step_fp8(WaveState &st, const Item &it, int i, i
   h.tid = opaque(tid);
   h.dma_on = i + 3 < it.ntiles;
   h.widen_on = i + 1 < it.ntiles;
-  compute_tile<true>(st, tile_buf<B2>(), g_sclbf[B2], min(sk::T, it.t1 - (it.t0 + i * sk::T)), h);
+  compute_tile<true, B2>(st, min(sk::T, it.t1 - (it.t0 + i * sk::T)), h);
 }
 
 template <bool FP8>
@@ -557,8 +602,10 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
                                                         float *__restrict__ lse,
                                                         int32_t *__restrict__ status) {
   using namespace sk;
+  using M = Map<FP8>;
   const int k = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane & 31, half = lane >> 5;
   const int head = blockIdx.y * 128 + 32 * w + hl;
   const WorkItem wi = items[k];
@@ -586,13 +633,13 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
 
   // prologue loads first, so they overlap the Q fetch
   if (FP8) {
-    dma_raw(raw_lds<0>(), scl_lds<0>(), it, 0, w, lane);
-    if (it.ntiles > 1) dma_raw(raw_lds<1>(), scl_lds<1>(), it, 1, w, lane);
-    if (it.ntiles > 2) dma_raw(raw_lds<2>(), scl_lds<2>(), it, 2, w, lane);
+    dma_raw<0>(it, 0, w, lane);
+    if (it.ntiles > 1) dma_raw<1>(it, 1, w, lane);
+    if (it.ntiles > 2) dma_raw<2>(it, 2, w, lane);
   } else {
-    dma_bf16(tile_lds<0>(), it, 0, w, lane);
-    if (it.ntiles > 1) dma_bf16(tile_lds<1>(), it, 1, w, lane);
-    if (it.ntiles > 2) dma_bf16(tile_lds<2>(), it, 2, w, lane);
+    dma_bf16<0>(it, 0, w, lane);
+    if (it.ntiles > 1) dma_bf16<1>(it, 1, w, lane);
+    if (it.ntiles > 2) dma_bf16<2>(it, 2, w, lane);
   }
 
   WaveState st;
@@ -612,26 +659,21 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
   }
   st.m = -INFINITY;
   st.l = 0.0f;
-  // score A fragment for kk: token hl, chunk 2 kk + half ->
-  //   hl*1152 + 128 (kk / 4) + 16 ((2 (kk % 4)) ^ (half ^ swz(hl)))
-  {
-    const int s1 = half ^ swz(hl);
+  // score A fragment kk: token hl, 16-byte chunk 2 kk + half of the latent
+  // row, or chunk 2 (kk - 32) + half of the k_rope row (swizzled)
+  st.sl = LROW * hl + 16 * half;
+  st.sl2 = st.sl + M::lat(2);
 #pragma unroll
-    for (int j2 = 0; j2 < 4; ++j2) st.sbase[j2] = hl * ROWB + 16 * ((2 * j2) ^ s1);
-  }
+  for (int j = 0; j < 4; ++j) st.sr[j] = M::rope(0) + 128 * hl + 16 * ((2 * j + half) ^ rsw(hl));
   // value A fragment (transposed read): 16-lane group g, lane j in it points at
-  // token 16 kb + 8 h + tt (tt = 4 (g/2) + j/4), latent column 32 db + dd
-  // (db = 4 w + jb, dd = 16 (g%2) + 4 (j%4)); its chunk 4 db + dd/8 lands at
-  //   256 w + 128 (jb / 2) + 16 ((4 (jb % 2)) ^ (dd / 8) ^ tt ^ h)  within the row.
+  // token 16 kb + 8 h + tt (tt = 4 (g/2) + j/4), latent column 128 w + 32 jb + dd
+  // (dd = 16 (g%2) + 4 (j%4))
   {
     const int g = (lane >> 4) & 3, j = lane & 15;
     const int tt = 4 * (g >> 1) + (j >> 2);
     const int dd = 16 * (g & 1) + 4 * (j & 3);
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        st.pbase[a][h] = tt * ROWB + 256 * w + 16 * ((4 * a) ^ (dd >> 3) ^ tt ^ h) + (dd & 7) * 2;
+    st.vl = LROW * tt + 2 * (128 * w + dd);
+    st.vl2 = st.vl + M::lat(2);
   }
 
   // widen tile 0 before the loop; each step then widens one tile ahead
@@ -639,7 +681,7 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
     constexpr int PER = RAW_DMA_PER_WAVE + 1;
     if (it.ntiles > 2) wait_vm<2 * PER>(); else if (it.ntiles > 1) wait_vm<PER>(); else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    widen_fp8(g_tile0, g_raw0, g_sclbf[0], g_scl[0], tid);
+    widen_fp8<0, 0>(tid);
     for (int i = 0; i < it.ntiles; i += 6) {
       step_fp8<0, 0>(st, it, i, w, lane, tid);
       if (i + 1 < it.ntiles) step_fp8<1, 1>(st, it, i + 1, w, lane, tid);
@@ -649,10 +691,9 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
       if (i + 5 < it.ntiles) step_fp8<2, 1>(st, it, i + 5, w, lane, tid);
     }
   } else {
-    constexpr int PER = DMA_PER_WAVE;
-    if (it.ntiles > 2) wait_vm<2 * PER>(); else if (it.ntiles > 1) wait_vm<PER>(); else wait_vm<0>();
+    if (it.ntiles > 2) wait_vm<18>(); else if (it.ntiles > 1) wait_vm<9>(); else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    widen_bf16_inplace(g_tile0, tid);
+    widen_bf16_inplace<0>(tid);
     for (int i = 0; i < it.ntiles; i += 4) {
       step_bf16<0>(st, it, i, w, lane, tid);
       if (i + 1 < it.ntiles) step_bf16<1>(st, it, i + 1, w, lane, tid);
@@ -664,17 +705,18 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
   // ---- normalised partials and log-sum-exp (base 2): each wave writes its
   // 128 latent columns of all 128 heads, dividing by the denominators the
   // scoring waves hand over
+  float *gstat = reinterpret_cast<float *>(g_lds + M::stat());
   if (half == 0) {
-    g_stat[32 * w + hl] = st.l;
+    gstat[32 * w + hl] = st.l;
     lse[static_cast<size_t>(k) * H + head] = st.m + log2f(st.l);
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  wait_lds();
   __builtin_amdgcn_s_barrier();
   // register group g4 of accumulator (j, hb) is one 1 KB run: head block
   // hb, latent block 4 w + j
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
-    const float inv = 1.0f / g_stat[32 * hb + hl];
+    const float inv = 1.0f / gstat[32 * hb + hl];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
