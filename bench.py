@@ -39,6 +39,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     p.add_argument("--extra", action="store_true", help="also time the uniform 8192-token batch")
+    p.add_argument("--calib-mib", type=int, default=0,
+                   help="first run one plain device copy of this many MiB (mla_calib_copy), a kernel of known "
+                        "traffic for scaling hardware byte counters")
     return p.parse_args()
 
 
@@ -174,6 +177,13 @@ def main():
     import compressed_kv_cache_absorbed_amd as m
     m.load()
     torch.cuda.set_device(0)
+    if a.calib_mib > 0:
+        nb = a.calib_mib << 20
+        src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        m.mla_calib_copy(dst, src, nb)
+        torch.cuda.synchronize()
+        del src, dst
     res = run_workload(m, torch, a.workload, a.steps, a.warmup)
     case = res["case"]
     gbs = res["cache_bytes"] / (res["ms_step"] * 1e-3) / 1e9

@@ -296,24 +296,21 @@ hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, c
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  absorb_fast_kernel<<<dim3(d.n_heads, (batch + 31) / 32), 256, shm, s>>>(
-      batch, d.n_heads, d.softmax_scale * kLog2e, d.rope_base, static_cast<const uint16_t *>(q_nope),
-      static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seqs, q_out);
-  return hipGetLastError();
+  return launch_kernel(absorb_fast_kernel, dim3(d.n_heads, (batch + 31) / 32), 256, shm, s, batch, d.n_heads,
+                       d.softmax_scale * kLog2e, d.rope_base, static_cast<const uint16_t *>(q_nope),
+                       static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seqs, q_out);
 }
 
 hipError_t launch_merge_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const SeqInfo *seqs,
                              const float *opart, const float *lse, uint16_t *ohat) {
-  merge_fast_kernel<<<dim3(c.batch, d.n_heads / 32, fast::DC / 128), 256, 0, s>>>(c.batch, d.n_heads, seqs, c.seq_len,
-                                                                                opart, lse, ohat);
-  return hipGetLastError();
+  return launch_kernel(merge_fast_kernel, dim3(c.batch, d.n_heads / 32, fast::DC / 128), 256, 0, s, c.batch,
+                       d.n_heads, seqs, c.seq_len, opart, lse, ohat);
 }
 
 hipError_t launch_project_fast(hipStream_t s, const mla_dims &d, int32_t batch, const uint16_t *ohat,
                                const void *w_uv, void *o, mla_dtype od) {
-  project_fast_kernel<<<dim3(d.n_heads, fast::DV / 32, (batch + 31) / 32), 64, 0, s>>>(
-      batch, d.n_heads, ohat, static_cast<const uint16_t *>(w_uv), o, od == MLA_BF16 ? 1 : 0);
-  return hipGetLastError();
+  return launch_kernel(project_fast_kernel, dim3(d.n_heads, fast::DV / 32, (batch + 31) / 32), 64, 0, s, batch,
+                       d.n_heads, ohat, static_cast<const uint16_t *>(w_uv), o, od == MLA_BF16 ? 1 : 0);
 }
 
 }  // namespace mla

@@ -254,27 +254,24 @@ __global__ __launch_bounds__(256) void copy_kernel(uint4 *__restrict__ dst, cons
 }  // namespace
 
 hipError_t launch_init(hipStream_t s, int32_t *status) {
-  init_kernel<<<1, 64, 0, s>>>(status);
-  return hipGetLastError();
+  return launch_kernel(init_kernel, 1, 64, 0, s, status);
 }
 
 hipError_t launch_append_generic(hipStream_t s, const mla_dims &d, const mla_cache &c, const void *h,
                                  int32_t n_new, const void *w_dkv, const void *w_kr, mla_dtype act,
                                  int32_t *status) {
   const size_t shm = sizeof(float) * (d.d_model + d.d_c + d.d_rope + 4);
-  append_generic_kernel<<<dim3(c.batch, n_new), 256, shm, s>>>(d, c, h, n_new, w_dkv, w_kr, act, status);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_kernel(append_generic_kernel, dim3(c.batch, n_new), 256, shm, s, d, c, h, n_new, w_dkv,
+                               w_kr, act, status);
   if (e != hipSuccess) return e;
-  advance_len_kernel<<<(c.batch + 255) / 256, 256, 0, s>>>(c, n_new);
-  return hipGetLastError();
+  return launch_kernel(advance_len_kernel, (c.batch + 255) / 256, 256, 0, s, c, n_new);
 }
 
 hipError_t launch_absorb_generic(hipStream_t s, const mla_dims &d, int32_t batch, const void *q_nope,
                                  const void *q_rope, const int32_t *q_pos, const void *w_uk,
                                  mla_dtype qw, const SeqInfo *seqs, float *q_out) {
-  absorb_generic_kernel<<<dim3(batch, d.n_heads), 256, sizeof(float) * d.d_nope, s>>>(
-      d, q_nope, q_rope, q_pos, w_uk, qw, seqs, q_out);
-  return hipGetLastError();
+  return launch_kernel(absorb_generic_kernel, dim3(batch, d.n_heads), 256, sizeof(float) * d.d_nope, s, d, q_nope,
+                       q_rope, q_pos, w_uk, qw, seqs, q_out);
 }
 
 hipError_t launch_decode_generic(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,
@@ -282,21 +279,19 @@ hipError_t launch_decode_generic(hipStream_t s, const mla_dims &d, const mla_cac
                                  float *opart, float *lse, int32_t *status) {
   if (n_items == 0) return hipSuccess;
   const size_t shm = sizeof(float) * (d.d_c + d.d_rope + 256 + 4);
-  decode_generic_kernel<<<dim3(n_items, d.n_heads), 256, shm, s>>>(d, c, items, seqs, q, opart, lse, status);
-  return hipGetLastError();
+  return launch_kernel(decode_generic_kernel, dim3(n_items, d.n_heads), 256, shm, s, d, c, items, seqs, q, opart,
+                       lse, status);
 }
 
 hipError_t launch_combine_generic(hipStream_t s, const mla_dims &d, const mla_cache &c,
                                   const SeqInfo *seqs, const float *opart, const float *lse,
                                   const void *w_uv, mla_dtype qw, void *o, mla_dtype od) {
-  combine_generic_kernel<<<dim3(c.batch, d.n_heads), 256, sizeof(float) * d.d_c, s>>>(
-      d, c, seqs, opart, lse, w_uv, qw, o, od);
-  return hipGetLastError();
+  return launch_kernel(combine_generic_kernel, dim3(c.batch, d.n_heads), 256, sizeof(float) * d.d_c, s, d, c, seqs,
+                       opart, lse, w_uv, qw, o, od);
 }
 
 hipError_t launch_copy(hipStream_t s, void *dst, const void *src, size_t n16) {
-  copy_kernel<<<2048, 256, 0, s>>>(static_cast<uint4 *>(dst), static_cast<const uint4 *>(src), n16);
-  return hipGetLastError();
+  return launch_kernel(copy_kernel, 2048, 256, 0, s, static_cast<uint4 *>(dst), static_cast<const uint4 *>(src), n16);
 }
 
 }  // namespace mla

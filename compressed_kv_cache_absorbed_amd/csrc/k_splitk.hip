@@ -737,10 +737,8 @@ hipError_t launch_decode_fast(hipStream_t s, const mla_dims &d, const mla_cache 
   if (n_items == 0) return hipSuccess;
   const dim3 grid(n_items, d.n_heads / 128);
   if (c.latent_dtype == MLA_FP8_E4M3)
-    splitk_kernel<true><<<grid, 256, 0, s>>>(c, d.n_heads, items, seqs, q, opart, lse, status);
-  else
-    splitk_kernel<false><<<grid, 256, 0, s>>>(c, d.n_heads, items, seqs, q, opart, lse, status);
-  return hipGetLastError();
+    return launch_kernel(splitk_kernel<true>, grid, 256, 0, s, c, d.n_heads, items, seqs, q, opart, lse, status);
+  return launch_kernel(splitk_kernel<false>, grid, 256, 0, s, c, d.n_heads, items, seqs, q, opart, lse, status);
 }
 
 }  // namespace mla

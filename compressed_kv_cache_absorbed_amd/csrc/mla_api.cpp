@@ -70,8 +70,9 @@ struct Profiler {
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
     return e;
   }
-  hipEvent_t pending_a = nullptr;
+  hipEvent_t pending_a = nullptr, pending_b = nullptr;
   int pending_kernel = -1;
+  bool taken = false;
 };
 Profiler &prof() {
   static Profiler *p = new Profiler();
@@ -95,33 +96,47 @@ const char *kKernelNames[K_COUNT] = {
 
 namespace mla {
 
-void prof_before(hipStream_t s, int kernel_id) {
+void prof_before(hipStream_t, int kernel_id) {
   Profiler &p = prof();
   std::lock_guard<std::mutex> g(p.mu);
   if (!p.on || static_cast<int>(p.recs.size()) >= p.max_records) return;
   hipEvent_t a = p.get();
-  if (!a) return;
-  if (hipEventRecord(a, s) != hipSuccess) {
-    p.pool.push_back(a);
+  hipEvent_t b = a ? p.get() : nullptr;
+  if (!b) {
+    if (a) p.pool.push_back(a);
     return;
   }
   p.pending_a = a;
+  p.pending_b = b;
   p.pending_kernel = kernel_id;
+  p.taken = false;
 }
 
-void prof_after(hipStream_t s, int kernel_id) {
+bool prof_take(hipEvent_t *start, hipEvent_t *stop) {
   Profiler &p = prof();
   std::lock_guard<std::mutex> g(p.mu);
-  if (!p.on || !p.pending_a || p.pending_kernel != kernel_id) return;
-  hipEvent_t b = p.get();
-  if (b && hipEventRecord(b, s) == hipSuccess) {
-    p.recs.push_back({kernel_id, p.pending_a, b});
+  if (!p.on || !p.pending_a || p.taken) return false;
+  *start = p.pending_a;
+  *stop = p.pending_b;
+  p.taken = true;
+  return true;
+}
+
+// A call that launched nothing (or whose launch failed) leaves no record; a
+// call that launched several kernels is timed over its first one.
+void prof_after(hipStream_t, int kernel_id) {
+  Profiler &p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  if (!p.pending_a || p.pending_kernel != kernel_id) return;
+  if (p.taken && p.on) {
+    p.recs.push_back({kernel_id, p.pending_a, p.pending_b});
   } else {
     p.pool.push_back(p.pending_a);
-    if (b) p.pool.push_back(b);
+    p.pool.push_back(p.pending_b);
   }
-  p.pending_a = nullptr;
+  p.pending_a = p.pending_b = nullptr;
   p.pending_kernel = -1;
+  p.taken = false;
 }
 
 DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items) {

@@ -2,6 +2,7 @@
 // kernel sources. Not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -141,8 +142,28 @@ hipError_t launch_project_fast(hipStream_t s, const mla_dims &d, int32_t batch, 
 
 hipError_t launch_copy(hipStream_t s, void *dst, const void *src, size_t n16);
 
-// Profiling hooks used by the launch wrappers in mla_api.cpp.
+// Profiling hooks used by the launch wrappers in mla_api.cpp. While a
+// profiled call is pending, prof_take() hands its start/stop events to the
+// first kernel launched through launch_kernel(), which has the dispatch
+// itself record them (kernel-precise, like a kernel trace).
 void prof_before(hipStream_t s, int kernel_id);
 void prof_after(hipStream_t s, int kernel_id);
+bool prof_take(hipEvent_t *start, hipEvent_t *stop);
+
+template <class T> struct same_type { using type = T; };
+
+// Every kernel of the library is launched through this (arguments are
+// converted to the kernel's own parameter types first).
+template <typename... KArgs>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shm, hipStream_t s,
+                                typename same_type<KArgs>::type... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (prof_take(&a, &b)) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, s, a, b, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shm, s, args...);
+  }
+  return hipGetLastError();
+}
 
 }  // namespace mla
