@@ -38,7 +38,8 @@ def parse():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
-    p.add_argument("--extra", action="store_true", help="also time the uniform 8192-token batch")
+    p.add_argument("--extra", action="store_true",
+                   help="also time the other workloads (uniform 8K batch, one 4K sequence, 4 x 128K, fp8 + append)")
     p.add_argument("--calib-mib", type=int, default=0,
                    help="first run one plain device copy of this many MiB (mla_calib_copy), a kernel of known "
                         "traffic for scaling hardware byte counters")
@@ -66,31 +67,54 @@ def measured_traffic(bytes_alg):
     return t.get("bytes_per_launch")
 
 
+DT = {"f32": 0, "bf16": 1, "fp8": 2}
+
+
 def run_workload(m, torch, name, steps, warmup):
+    """Times `steps` decode steps of one workload (after `warmup` untimed ones).
+    A step is one mla_decode call, or one mla_append_decode call for the
+    workload that appends a token per sequence; that step also restores
+    seq_len first (a 4-byte-per-sequence device copy) so every step appends
+    at the same place."""
     import mla_synth
     from mla_synth.device import upload
 
     case = mla_synth.workload(name)
-    assert case.latent_dtype == "bf16"
     dev = torch.device("cuda", 0)
     t = upload(case, dev)
-    d = m.dims(case.H, case.d_c, case.d_rope, case.d_nope, case.d_v, 0, case.softmax_scale, case.rope_base)
-    cache_bytes = int(case.lens.sum()) * case.row_bytes
-    weight_bytes = 2 * case.H * case.d_c * 128 * 2
+    d = m.dims(case.H, case.d_c, case.d_rope, case.d_nope, case.d_v, case.d_model, case.softmax_scale,
+               case.rope_base)
+    lens = case.lens + case.n_new
+    cache_bytes = int(lens.sum()) * case.row_bytes
+    weight_bytes = 2 * case.H * case.d_c * case.d_nope * 2
     # enough copies that a step's inputs were last touched >= 768 MB of traffic ago
     ncopy = max(2, math.ceil(768e6 / (cache_bytes + weight_bytes)) + 1)
-    rows = [t["rows"]] + [t["rows"].clone() for _ in range(ncopy - 1)]
-    wuk = [t["w_uk"]] + [t["w_uk"].clone() for _ in range(ncopy - 1)]
-    wuv = [t["w_uv"]] + [t["w_uv"].clone() for _ in range(ncopy - 1)]
-    caches = [m.cache(r, case.row_stride, 1, 1, t["seq_start"], t["seq_cap"], t["seq_len"]) for r in rows]
-    plan = m.mla_plan_create(d, case.lens.tolist(), 0)
-    ws = torch.empty(m.mla_decode_workspace_bytes(d, plan), dtype=torch.uint8, device=dev)
+
+    def copies(x):
+        return None if x is None else [x] + [x.clone() for _ in range(ncopy - 1)]
+
+    rows, scale, wuk, wuv = copies(t["rows"]), copies(t["scale"]), copies(t["w_uk"]), copies(t["w_uv"])
+    lat, rope = DT[case.latent_dtype], DT[case.rope_dtype]
+    caches = [m.cache(rows[j], case.row_stride, lat, rope, t["seq_start"], t["seq_cap"], t["seq_len"],
+                      None if scale is None else scale[j]) for j in range(ncopy)]
+    plan = m.mla_plan_create(d, lens.tolist(), 0)
+    nbytes = m.mla_decode_workspace_bytes(d, plan)
+    if case.n_new:
+        nbytes = max(nbytes, m.mla_append_workspace_bytes(d, case.B, case.n_new))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     m.mla_workspace_init(ws)
     o = torch.empty((case.B, case.H, case.d_v), dtype=torch.bfloat16, device=dev)
+    len0 = t["seq_len"].clone()
+    act = DT[case.act_dtype]
 
     def step(k):
         j = k % ncopy
-        m.mla_decode(d, caches[j], plan, t["q_nope"], t["q_rope"], None, wuk[j], wuv[j], 1, o, 1, ws)
+        if case.n_new:
+            t["seq_len"].copy_(len0)
+            m.mla_append_decode(d, caches[j], plan, t["h"], case.n_new, t["w_dkv"], t["w_kr"], t["q_nope"],
+                                t["q_rope"], None, wuk[j], wuv[j], act, o, 1, ws)
+        else:
+            m.mla_decode(d, caches[j], plan, t["q_nope"], t["q_rope"], None, wuk[j], wuv[j], act, o, 1, ws)
 
     for k in range(warmup):
         step(k)
@@ -106,11 +130,27 @@ def run_workload(m, torch, name, steps, warmup):
     prof = m.mla_prof_end()
     assert m.mla_device_error(ws) == 0
     ms_step = (t1 - t0) * 1e3 / steps
-    kms, kn = prof["decode_bf16"]
+    kname = "decode_fp8" if case.latent_dtype == "fp8" else "decode_bf16"
+    kms, kn = prof[kname]
     splitk_ms = kms / kn
     return dict(case=case, t=t, o=o, d=d, plan=plan, cache_bytes=cache_bytes, ms_step=ms_step,
-                splitk_ms=splitk_ms, prof={k: v[0] / v[1] for k, v in prof.items()},
+                splitk_ms=splitk_ms, splitk_name=kname, prof={k: v[0] / v[1] for k, v in prof.items()},
                 n_items=plan.n_items, ncopy=ncopy)
+
+
+def workload_summary(res):
+    """One line per extra workload: step and split-K rates, per-kernel times."""
+    case = res["case"]
+    flops = 2.0 * case.H * (2 * case.d_c + case.d_rope) * float((case.lens + case.n_new).sum())
+    return {"batch": case.B, "cache_tokens": int((case.lens + case.n_new).sum()),
+            "latent_dtype": case.latent_dtype, "appends": int(case.n_new),
+            "ms_per_step": round(res["ms_step"], 5),
+            "tokens_per_s": round(case.B / (res["ms_step"] * 1e-3), 1),
+            "cache_GBs_step": round(res["cache_bytes"] / (res["ms_step"] * 1e-3) / 1e9, 2),
+            "splitk_GBs": round(res["cache_bytes"] / (res["splitk_ms"] * 1e-3) / 1e9, 2),
+            "splitk_hbm_frac": round(res["cache_bytes"] / (res["splitk_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "splitk_mfma_frac_fp16": round(flops / (res["splitk_ms"] * 1e-3) / 2.5e15, 4),
+            "kernel_ms": {k: round(v, 5) for k, v in res["prof"].items()}}
 
 
 def sampled_parity(res, n=8):
@@ -218,10 +258,12 @@ def main():
                      "per_launch_bytes": res["cache_bytes"], "avg_launch_ms": round(res["splitk_ms"], 5)},
     }
     if a.extra:
-        r8 = run_workload(m, torch, "v3_b32_8k", a.steps, a.warmup)
-        out["uniform_8k"] = {"value": round(r8["cache_bytes"] / (r8["ms_step"] * 1e-3) / 1e9, 2), "unit": "GB/s",
-                             "splitk_GBs": round(r8["cache_bytes"] / (r8["splitk_ms"] * 1e-3) / 1e9, 2),
-                             "ms_per_step": round(r8["ms_step"], 5)}
+        out["other_workloads"] = {}
+        for name in ("v3_b32_8k", "v3_b1_4k", "v3_b4_128k", "v3_b128_fp8"):
+            r = run_workload(m, torch, name, a.steps, a.warmup)
+            out["other_workloads"][name] = workload_summary(r)
+            del r
+            torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(res, a.cpu_seconds)
     print(json.dumps(out), flush=True)

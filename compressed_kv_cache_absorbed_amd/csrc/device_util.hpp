@@ -48,12 +48,18 @@ __device__ __forceinline__ int elem_bytes(mla_dtype t) {
 }
 
 // RoPE angle pos * base^(-2j/d) and its cosine/sine, formed in fp64 so large
-// positions (131071 and beyond) keep full fp32 accuracy.
+// positions (131071 and beyond) keep full fp32 accuracy. The angle is first
+// reduced to [-pi, pi] by a - k 2 pi with 2 pi split into two doubles (the
+// fused multiply-add keeps k * hi exact; accurate to ~1e-15 for |k| < 2^30),
+// so the sine and cosine only ever see a small argument.
 __device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, int d, float base, float *c, float *s) {
-  double theta = pow(static_cast<double>(base), -2.0 * j / d);
-  double a = static_cast<double>(pos) * theta;
+  const double theta = pow(static_cast<double>(base), -2.0 * j / d);
+  const double a = static_cast<double>(pos) * theta;
+  const double k = rint(a * 0.15915494309189535);  // 1 / (2 pi)
+  double r = fma(-k, 6.283185307179586, a);          // 2 pi, high part
+  r = fma(-k, 2.4492935982947064e-16, r);            // 2 pi, low part
   double sd, cd;
-  sincos(a, &sd, &cd);
+  sincos(r, &sd, &cd);
   *c = static_cast<float>(cd);
   *s = static_cast<float>(sd);
 }
@@ -87,6 +93,34 @@ __device__ __forceinline__ float block_max_256(float v, float *red) {
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Finish one appended row from its fp32 projections outv[0 .. d_c + d_rope)
+// (already in LDS, k_rope part rotated): round to the storage dtypes and
+// store it at `row`. fp8 latents get the per-token scale amax / 448 (1 for a
+// zero row). Called by all 256 threads of the block; `red` is 4 floats of LDS.
+__device__ __forceinline__ void store_appended_row(const mla_dims &d, const mla_cache &c, int64_t row,
+                                                   const float *outv, float *red) {
+  const int tid = threadIdx.x;
+  char *rowp = static_cast<char *>(c.rows) + row * c.row_stride;
+  if (c.latent_dtype == MLA_FP8_E4M3) {
+    float am = 0.0f;
+    for (int k = tid; k < d.d_c; k += 256) am = fmaxf(am, fabsf(outv[k]));
+    am = block_max_256(am, red);
+    const float s = am > 0.0f ? am / kFp8Max : 1.0f;
+    for (int k = tid; k < d.d_c; k += 256) reinterpret_cast<uint8_t *>(rowp)[k] = f32_to_fp8(outv[k] / s);
+    if (tid == 0) c.scale[row] = s;
+  } else if (c.latent_dtype == MLA_BF16) {
+    for (int k = tid; k < d.d_c; k += 256) reinterpret_cast<uint16_t *>(rowp)[k] = f32_to_bf16_bits(outv[k]);
+  } else {
+    for (int k = tid; k < d.d_c; k += 256) reinterpret_cast<float *>(rowp)[k] = outv[k];
+  }
+  char *rp = rowp + static_cast<int64_t>(d.d_c) * elem_bytes(c.latent_dtype);
+  if (c.rope_dtype == MLA_BF16) {
+    for (int k = tid; k < d.d_rope; k += 256) reinterpret_cast<uint16_t *>(rp)[k] = f32_to_bf16_bits(outv[d.d_c + k]);
+  } else {
+    for (int k = tid; k < d.d_rope; k += 256) reinterpret_cast<float *>(rp)[k] = outv[d.d_c + k];
+  }
 }
 
 // First error wins.

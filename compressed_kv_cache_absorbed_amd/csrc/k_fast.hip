@@ -7,6 +7,8 @@
 //                        (fp16, not bf16: the score's sensitivity to the
 //                        rounding of q~ is what limits accuracy on peaked rows)
 //   (the split-K kernel between them lives in k_splitk.hip)
+//   append_gemm_kernel   [c ; k_r] = [W_DKV ; W_KR] h for the new tokens (K-split)
+//   append_finish_kernel sum of the splits, RoPE, rounding / fp8 scale, row store
 //   merge_fast_kernel    log-sum-exp merge of the split partials into o^
 //   project_fast_kernel  o = W_UV o^ (the output-side absorption)
 //
@@ -51,6 +53,8 @@ constexpr int DNOPE = 128;     // query no-RoPE width
 constexpr int DV = 128;        // value head width
 constexpr int HPW = 32;        // heads per wave of the split-K kernel
 constexpr int WAVES = 4;       // its waves: 128 heads per workgroup
+constexpr int APPEND_KS = 512;     // d_model inputs per K-split of the append GEMM
+constexpr int APPEND_NMAX = 1024;  // largest d_c + d_rope the append finish holds in LDS
 }  // namespace fast
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -156,83 +160,78 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qs
 }
 
 // ------------------------------------------------------------------ merge
-// Grid (batch, H/32, 4), 256 threads: sequence b, head block hb, latent
-// columns 128 q .. 128 q + 127. Log-sum-exp merge of the sequence's split
+// Grid (batch, H/32, d_c/32), 256 threads: sequence b, head block hb,
+// latent block db (32 columns). Log-sum-exp merge of the sequence's split
 // partials (base 2): o^ = sum_s 2^(lse_s - M) o^_s / sum_s 2^(lse_s - M).
-// In the fragment order of the partials the block is 16 KB contiguous per
-// split; thread (g = tid / 64, lane) owns the four float4 at 1024 x + 256 g +
-// 4 lane (x = 0..3), all of head hl = lane % 32. The result goes out as bf16
-// hi and lo planes (lo = bf16(o^ - hi), about 16 significant bits), laid
-// out [head][sequence][column] for the W_UV product.
+// In the fragment order of the partials the (hb, db) block is 4 KB
+// contiguous per split; thread (g = tid / 64, lane) owns the float4 at
+// 256 g + 4 lane of it (head hl = lane % 32, columns 8 g + 4 (lane / 32) ..),
+// and keeps 8 splits' loads in flight. The result goes out as bf16 hi and
+// lo planes (lo = bf16(o^ - hi), about 16 significant bits), laid out
+// [head][sequence][column] for the W_UV product, through an LDS transpose.
 __global__ __launch_bounds__(256) void merge_fast_kernel(int B, int H, const SeqInfo *__restrict__ seqs,
                                                          const int32_t *__restrict__ dev_len,
                                                          const float *__restrict__ opart,
                                                          const float *__restrict__ lse, uint16_t *__restrict__ ohat) {
   using namespace fast;
-  constexpr int SB = 4;             // splits loaded per batch
-  constexpr int TS = 128 + 4;       // LDS row stride (floats) of the [head][column] tile
-  __shared__ float tile[32 * TS];
-  const int b = blockIdx.x, hb = blockIdx.y, q = blockIdx.z;
+  constexpr int SB = 8;  // splits loaded per batch
+  __shared__ float tile[32 * 33];
+  const int b = blockIdx.x, hb = blockIdx.y, db = blockIdx.z;
   const int tid = threadIdx.x, g = tid >> 6, lane = tid & 63, hl = lane & 31, half = lane >> 5;
   const int head = 32 * hb + hl;
-  float4 acc[4];
-#pragma unroll
-  for (int x = 0; x < 4; ++x) acc[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const SeqInfo si = seqs[b];
   if (si.item_count > 0 && dev_len[b] == si.len) {
+    const int S = si.item_count;
     const float *lrow = lse + static_cast<size_t>(si.item_begin) * H + head;
     float M = -INFINITY;
-    for (int s = 0; s < si.item_count; ++s) M = fmaxf(M, lrow[static_cast<size_t>(s) * H]);
+    for (int s = 0; s < S; ++s) M = fmaxf(M, lrow[static_cast<size_t>(s) * H]);
     if (M != -INFINITY) {
       float den = 0.0f;
-      for (int s = 0; s < si.item_count; ++s) den += exp2f(lrow[static_cast<size_t>(s) * H] - M);
+      for (int s = 0; s < S; ++s) den += exp2f(lrow[static_cast<size_t>(s) * H] - M);
       const float inv = 1.0f / den;
       const size_t stride = static_cast<size_t>(H / 32) * 16 * 1024;  // floats per item
-      const float *src = opart + (static_cast<size_t>(si.item_begin) * (H / 32) + hb) * (16 * 1024) +
-                         (16 * q) * 256 + 256 * g + 4 * lane;
-      for (int s0 = 0; s0 < si.item_count; s0 += SB) {
-        float4 x[SB][4];
+      const float *src = opart + (static_cast<size_t>(si.item_begin) * (H / 32) + hb) * (16 * 1024) + 1024 * db +
+                         256 * g + 4 * lane;
+      for (int s0 = 0; s0 < S; s0 += SB) {
+        float4 x[SB];
         float wt[SB];
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
-          const int s = min(s0 + u, si.item_count - 1);
-          wt[u] = s0 + u < si.item_count ? exp2f(lrow[static_cast<size_t>(s) * H] - M) * inv : 0.0f;
-#pragma unroll
-          for (int xx = 0; xx < 4; ++xx) x[u][xx] = *reinterpret_cast<const float4 *>(src + s * stride + 1024 * xx);
+          const int s = min(s0 + u, S - 1);
+          wt[u] = s0 + u < S ? exp2f(lrow[static_cast<size_t>(s) * H] - M) * inv : 0.0f;
+          x[u] = *reinterpret_cast<const float4 *>(src + s * stride);
         }
 #pragma unroll
-        for (int u = 0; u < SB; ++u)
-#pragma unroll
-          for (int xx = 0; xx < 4; ++xx) {
-            acc[xx].x = fmaf(wt[u], x[u][xx].x, acc[xx].x);
-            acc[xx].y = fmaf(wt[u], x[u][xx].y, acc[xx].y);
-            acc[xx].z = fmaf(wt[u], x[u][xx].z, acc[xx].z);
-            acc[xx].w = fmaf(wt[u], x[u][xx].w, acc[xx].w);
-          }
+        for (int u = 0; u < SB; ++u) {
+          acc.x = fmaf(wt[u], x[u].x, acc.x);
+          acc.y = fmaf(wt[u], x[u].y, acc.y);
+          acc.z = fmaf(wt[u], x[u].z, acc.z);
+          acc.w = fmaf(wt[u], x[u].w, acc.w);
+        }
       }
     }
   }
-  // to [head][column] in LDS: float4 x holds columns 32 x + 8 g + 4 half + e
-#pragma unroll
-  for (int xx = 0; xx < 4; ++xx)
-    *reinterpret_cast<float4 *>(tile + hl * TS + 32 * xx + 8 * g + 4 * half) = acc[xx];
+  float *trow = tile + hl * 33 + 8 * g + 4 * half;
+  trow[0] = acc.x;
+  trow[1] = acc.y;
+  trow[2] = acc.z;
+  trow[3] = acc.w;
   __syncthreads();
-  // thread: head hh, 16 columns from c0
-  const int hh = tid >> 3, c0 = 16 * (tid & 7);
-  bf16x8 hi[2], lo[2];
+  if (tid < 128) {  // head hh, 8 columns from c0
+    const int hh = tid >> 2, c0 = 8 * (tid & 3);
+    bf16x8 hi, lo;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float v = tile[hh * TS + c0 + e];
-    const __bf16 h = static_cast<__bf16>(v);
-    hi[e >> 3][e & 7] = h;
-    lo[e >> 3][e & 7] = static_cast<__bf16>(v - static_cast<float>(h));
+    for (int e = 0; e < 8; ++e) {
+      const float v = tile[hh * 33 + c0 + e];
+      const __bf16 h = static_cast<__bf16>(v);
+      hi[e] = h;
+      lo[e] = static_cast<__bf16>(v - static_cast<float>(h));
+    }
+    uint16_t *dh = ohat + (static_cast<size_t>(32 * hb + hh) * B + b) * DC + 32 * db + c0;
+    *reinterpret_cast<bf16x8 *>(dh) = hi;
+    *reinterpret_cast<bf16x8 *>(dh + static_cast<size_t>(H) * B * DC) = lo;
   }
-  uint16_t *dh = ohat + (static_cast<size_t>(32 * hb + hh) * B + b) * DC + 128 * q + c0;
-  uint16_t *dl = dh + static_cast<size_t>(H) * B * DC;
-  *reinterpret_cast<bf16x8 *>(dh) = hi[0];
-  *reinterpret_cast<bf16x8 *>(dh + 8) = hi[1];
-  *reinterpret_cast<bf16x8 *>(dl) = lo[0];
-  *reinterpret_cast<bf16x8 *>(dl + 8) = lo[1];
 }
 
 // ---------------------------------------------------------------- project
@@ -276,13 +275,110 @@ __global__ __launch_bounds__(64) void project_fast_kernel(int B, int H, const ui
   }
 }
 
+// ----------------------------------------------------------------- append
+// The down-projection of the new tokens, [c ; k_r] = [W_DKV ; W_KR] h ("02 —
+// Multi-Latent Attention (MLA)", "La compresión de MLA"; the RoPE key
+// projection, "Truco de codificación posicional"), as a K-split GEMM on the
+// matrix cores. Grid (N/32, ceil(T/32), d_model/512), one wave: a 32 token x
+// 32 output tile over 512 of the d_model inputs, D = h W^T with A = h rows
+// (token m0 + l%32, k = 16 kk + 8(l/32) ..) and B = weight rows (output
+// n0 + l%32, same k), both read straight from global memory. The fp32 tile
+// goes to partial[ks][token][output]; append_finish_kernel sums the splits.
+__global__ __launch_bounds__(64) void append_gemm_kernel(int T, int d_c, int d_model, const uint16_t *__restrict__ h,
+                                                         const uint16_t *__restrict__ w_dkv,
+                                                         const uint16_t *__restrict__ w_kr,
+                                                         float *__restrict__ partial) {
+  using namespace fast;
+  const int nt = blockIdx.x, mt = blockIdx.y, ks = blockIdx.z;
+  const int N = gridDim.x * 32;
+  const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
+  const int m = min(mt * 32 + l32, T - 1);
+  const int n = nt * 32 + l32;
+  const size_t k0 = static_cast<size_t>(ks) * APPEND_KS + 8 * half;
+  const uint16_t *arow = h + static_cast<size_t>(m) * d_model + k0;
+  const uint16_t *brow = (n < d_c ? w_dkv + static_cast<size_t>(n) * d_model
+                                  : w_kr + static_cast<size_t>(n - d_c) * d_model) + k0;
+  f32x16 acc = {};
+#pragma unroll 8
+  for (int kk = 0; kk < APPEND_KS / 16; ++kk) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(arow + 16 * kk);
+    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(brow + 16 * kk);
+    acc = mfma32(a, b, acc);
+  }
+  // D: lane l, register r holds token m0 + 8(r/4) + 4(l/32) + r%4, output n
+  float *out = partial + static_cast<size_t>(ks) * T * N;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int mm = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+    if (mm < T) out[static_cast<size_t>(mm) * N + n] = acc[r];
+  }
+}
+
+// Grid (batch * n_new), 256 threads: token t = b n_new + j goes to row
+// seq_start[b] + seq_len[b] + j at position seq_len[b] + j. Sums the K-split
+// partials, rotates the k_r part at that position, rounds to the storage
+// dtypes and writes the row; a sequence without room for all n_new tokens
+// is left untouched and reported (MLA_ERR_CAPACITY), as on the generic path.
+__global__ __launch_bounds__(256) void append_finish_kernel(mla_dims d, mla_cache c, int32_t n_new, int ksplit,
+                                                            const float *__restrict__ partial,
+                                                            int32_t *__restrict__ status) {
+  using namespace fast;
+  __shared__ float outv[APPEND_NMAX];
+  __shared__ float red[4];
+  const int t = blockIdx.x, T = gridDim.x;
+  const int b = t / n_new, j = t - b * n_new;
+  const int tid = threadIdx.x;
+  const int N = d.d_c + d.d_rope;
+  const int32_t len = c.seq_len[b];
+  const int64_t pos = static_cast<int64_t>(len) + j;
+  const int64_t row = static_cast<int64_t>(c.seq_start[b]) + pos;
+  if (len < 0 || static_cast<int64_t>(len) + n_new > c.seq_cap[b] || row < 0 || row >= c.n_rows) {
+    if (tid == 0 && j == 0) set_status(status, MLA_ERR_CAPACITY);
+    return;
+  }
+  for (int n = tid; n < N; n += 256) {
+    float acc = 0.0f;
+    for (int ks = 0; ks < ksplit; ++ks) acc += partial[(static_cast<size_t>(ks) * T + t) * N + n];
+    outv[n] = acc;
+  }
+  __syncthreads();
+  for (int p = tid; p < d.d_rope / 2; p += 256) {
+    float cs, sn;
+    rope_cos_sin(pos, p, d.d_rope, d.rope_base, &cs, &sn);
+    const float x0 = outv[d.d_c + 2 * p], x1 = outv[d.d_c + 2 * p + 1];
+    outv[d.d_c + 2 * p] = x0 * cs - x1 * sn;
+    outv[d.d_c + 2 * p + 1] = x0 * sn + x1 * cs;
+  }
+  __syncthreads();
+  store_appended_row(d, c, row, outv, red);
+}
+
 }  // namespace
 
-bool append_fast_path(const mla_dims &, int32_t, mla_dtype) { return false; }
+bool append_fast_shape(const mla_dims &d, int32_t tokens) {
+  const int n = d.d_c + d.d_rope;
+  return tokens > 0 && n % 32 == 0 && n <= fast::APPEND_NMAX && d.d_model >= fast::APPEND_KS &&
+         d.d_model % fast::APPEND_KS == 0;
+}
 
-hipError_t launch_append_fast(hipStream_t, const mla_dims &, const mla_cache &, const void *, int32_t,
-                              const void *, const void *, float *, int, int32_t *) {
-  return hipErrorNotSupported;
+bool append_fast_path(const mla_dims &d, int32_t tokens, mla_dtype act) {
+  return !force_generic() && act == MLA_BF16 && append_fast_shape(d, tokens);
+}
+
+hipError_t launch_append_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const void *h, int32_t n_new,
+                              const void *w_dkv, const void *w_kr, float *partial, int ksplit, int32_t *) {
+  const int T = c.batch * n_new, N = d.d_c + d.d_rope;
+  if (ksplit * fast::APPEND_KS != d.d_model) return hipErrorInvalidValue;
+  return launch_kernel(append_gemm_kernel, dim3(N / 32, (T + 31) / 32, ksplit), 64, 0, s, T, d.d_c, d.d_model,
+                       static_cast<const uint16_t *>(h), static_cast<const uint16_t *>(w_dkv),
+                       static_cast<const uint16_t *>(w_kr), partial);
+}
+
+hipError_t launch_append_finish(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_new,
+                                const float *partial, int ksplit, int32_t *status) {
+  hipError_t e = launch_kernel(append_finish_kernel, c.batch * n_new, 256, 0, s, d, c, n_new, ksplit, partial, status);
+  if (e != hipSuccess) return e;
+  return launch_advance_len(s, c, n_new);
 }
 
 hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, const void *q_nope,
@@ -303,7 +399,7 @@ hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, c
 
 hipError_t launch_merge_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const SeqInfo *seqs,
                              const float *opart, const float *lse, uint16_t *ohat) {
-  return launch_kernel(merge_fast_kernel, dim3(c.batch, d.n_heads / 32, fast::DC / 128), 256, 0, s, c.batch,
+  return launch_kernel(merge_fast_kernel, dim3(c.batch, d.n_heads / 32, fast::DC / 32), 256, 0, s, c.batch,
                        d.n_heads, seqs, c.seq_len, opart, lse, ohat);
 }
 

@@ -65,25 +65,7 @@ __global__ __launch_bounds__(256) void append_generic_kernel(mla_dims d, mla_cac
   }
   __syncthreads();
 
-  char *rowp = static_cast<char *>(c.rows) + row * c.row_stride;
-  if (c.latent_dtype == MLA_FP8_E4M3) {
-    float am = 0.0f;
-    for (int k = tid; k < d.d_c; k += 256) am = fmaxf(am, fabsf(outv[k]));
-    am = block_max_256(am, red);
-    const float s = am > 0.0f ? am / kFp8Max : 1.0f;
-    for (int k = tid; k < d.d_c; k += 256) reinterpret_cast<uint8_t *>(rowp)[k] = f32_to_fp8(outv[k] / s);
-    if (tid == 0) c.scale[row] = s;
-  } else if (c.latent_dtype == MLA_BF16) {
-    for (int k = tid; k < d.d_c; k += 256) reinterpret_cast<uint16_t *>(rowp)[k] = f32_to_bf16_bits(outv[k]);
-  } else {
-    for (int k = tid; k < d.d_c; k += 256) reinterpret_cast<float *>(rowp)[k] = outv[k];
-  }
-  char *rp = rowp + static_cast<int64_t>(d.d_c) * elem_bytes(c.latent_dtype);
-  if (c.rope_dtype == MLA_BF16) {
-    for (int k = tid; k < d.d_rope; k += 256) reinterpret_cast<uint16_t *>(rp)[k] = f32_to_bf16_bits(outv[d.d_c + k]);
-  } else {
-    for (int k = tid; k < d.d_rope; k += 256) reinterpret_cast<float *>(rp)[k] = outv[d.d_c + k];
-  }
+  store_appended_row(d, c, row, outv, red);
 }
 
 __global__ void advance_len_kernel(mla_cache c, int32_t n_new) {
@@ -257,6 +239,10 @@ hipError_t launch_init(hipStream_t s, int32_t *status) {
   return launch_kernel(init_kernel, 1, 64, 0, s, status);
 }
 
+hipError_t launch_advance_len(hipStream_t s, const mla_cache &c, int32_t n_new) {
+  return launch_kernel(advance_len_kernel, (c.batch + 255) / 256, 256, 0, s, c, n_new);
+}
+
 hipError_t launch_append_generic(hipStream_t s, const mla_dims &d, const mla_cache &c, const void *h,
                                  int32_t n_new, const void *w_dkv, const void *w_kr, mla_dtype act,
                                  int32_t *status) {
@@ -264,7 +250,7 @@ hipError_t launch_append_generic(hipStream_t s, const mla_dims &d, const mla_cac
   hipError_t e = launch_kernel(append_generic_kernel, dim3(c.batch, n_new), 256, shm, s, d, c, h, n_new, w_dkv,
                                w_kr, act, status);
   if (e != hipSuccess) return e;
-  return launch_kernel(advance_len_kernel, (c.batch + 255) / 256, 256, 0, s, c, n_new);
+  return launch_advance_len(s, c, n_new);
 }
 
 hipError_t launch_absorb_generic(hipStream_t s, const mla_dims &d, int32_t batch, const void *q_nope,

@@ -163,7 +163,7 @@ AppendWs append_ws_layout(const mla_dims &d, int32_t batch, int32_t n_new) {
   size_t off = kStatusBytes;
   w.partial = off;
   const int64_t tokens = static_cast<int64_t>(batch) * n_new;
-  if (append_fast_path(d, static_cast<int32_t>(std::min<int64_t>(tokens, INT32_MAX)), MLA_BF16)) {
+  if (append_fast_shape(d, static_cast<int32_t>(std::min<int64_t>(tokens, INT32_MAX)))) {
     w.ksplit = std::max(1, d.d_model / 512);
     off = align_up(off + sizeof(float) * w.ksplit * tokens * (d.d_c + d.d_rope), 256);
   }
@@ -205,7 +205,9 @@ mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32
     maxlen = std::max<int64_t>(maxlen, host_lens[b]);
     nonempty += host_lens[b] > 0;
   }
+  int64_t min_tiles = 1;
   if (n_workers == 0) {
+    min_tiles = 8;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
@@ -230,7 +232,7 @@ mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32
       const int64_t mid = (lo + hi) / 2;
       if (count(mid * T) <= target) hi = mid; else lo = mid + 1;
     }
-    C = lo * T;
+    C = std::max(lo, min_tiles) * T;
   }
 
   std::vector<WorkItem> items;
@@ -366,10 +368,10 @@ static mla_status do_append(const mla_dims *dims, const mla_cache *cache, const 
   int32_t *status = static_cast<int32_t *>(ws);
   if (append_fast_path(*dims, cache->batch * n_new, act)) {
     const AppendWs w = append_ws_layout(*dims, cache->batch, n_new);
+    float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + w.partial);
     MLA_LAUNCH(s, K_APPEND_GEMM,
-               launch_append_fast(s, *dims, *cache, h, n_new, w_dkv, w_kr,
-                                  reinterpret_cast<float *>(static_cast<char *>(ws) + w.partial),
-                                  w.ksplit, status));
+               launch_append_fast(s, *dims, *cache, h, n_new, w_dkv, w_kr, partial, w.ksplit, status));
+    MLA_LAUNCH(s, K_APPEND_FINISH, launch_append_finish(s, *dims, *cache, n_new, partial, w.ksplit, status));
   } else {
     MLA_LAUNCH(s, K_APPEND_GENERIC,
                launch_append_generic(s, *dims, *cache, h, n_new, w_dkv, w_kr, act, status));

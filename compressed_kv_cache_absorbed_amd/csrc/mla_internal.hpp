@@ -105,6 +105,9 @@ AppendWs append_ws_layout(const mla_dims &d, int32_t batch, int32_t n_new);
 // Which decode implementation handles these arguments.
 bool decode_fast_path(const mla_dims &d, const mla_cache &c, mla_dtype q_w_dtype);
 bool append_fast_path(const mla_dims &d, int32_t tokens, mla_dtype act_w_dtype);
+// The shapes the matrix-core append handles (the workspace is sized for it
+// whenever the shape qualifies, whatever the dtype or environment).
+bool append_fast_shape(const mla_dims &d, int32_t tokens);
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error. All take the stream first.
@@ -117,6 +120,9 @@ hipError_t launch_append_generic(hipStream_t s, const mla_dims &d, const mla_cac
 hipError_t launch_append_fast(hipStream_t s, const mla_dims &d, const mla_cache &c,
                               const void *h, int32_t n_new, const void *w_dkv, const void *w_kr,
                               float *partial, int ksplit, int32_t *status);
+hipError_t launch_append_finish(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_new,
+                                const float *partial, int ksplit, int32_t *status);
+hipError_t launch_advance_len(hipStream_t s, const mla_cache &c, int32_t n_new);
 
 hipError_t launch_absorb_generic(hipStream_t s, const mla_dims &d, int32_t batch,
                                  const void *q_nope, const void *q_rope, const int32_t *q_pos,

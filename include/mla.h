@@ -135,7 +135,11 @@ mla_status mla_append(const mla_dims *dims, const mla_cache *cache, const void *
  * Split-K over the sequence is not on the pages; it is exact by the
  * log-sum-exp identity (the combine step). n_workers is the number of
  * concurrent work items to aim for; 0 means "derive from the current HIP
- * device" (one per compute unit). The plan is deterministic in its inputs
+ * device" (one per compute unit), and then no item is made shorter than
+ * 256 tokens unless its sequence is (a few long items beat many one-tile
+ * ones whose partial results cost more to write and merge than they save).
+ * With an explicit n_workers the chunks are as short as that count needs
+ * (one 32-token tile at the least). The plan is deterministic in its inputs
  * and reusable across layers and calls with the same lengths. Returns
  * MLA_ERR_INVALID_ARG for batch < 1, a negative length or a null pointer. */
 mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32_t batch,

@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from tests.helpers import (GpuRun, TOL_BF16_REL, TOL_FP8_REL, make, oracle_decode, rel_rms_err,
-                           to_np)
+from tests.helpers import (GpuRun, TOL_BF16_REL, TOL_FP8_REL, make, oracle_append, oracle_decode,
+                           rel_rms_err, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -109,3 +109,64 @@ def test_fast_spiky_rows(gpu):
     run = GpuRun(gpu, case)
     o = to_np(run.decode())
     check(case, o, TOL_BF16_REL)
+
+
+@pytest.mark.parametrize("latent", ["f32", "bf16", "fp8"])
+def test_fast_append_rows_and_canary(gpu, latent, monkeypatch):
+    """The matrix-core append (bf16 h and weights, d_model a multiple of
+    512): rows land exactly at seq_start + seq_len + j (one sequence at a
+    position near 70000), every other byte stays as it was, values and fp8
+    scales match the oracle's own append within one storage step, and the
+    result equals the generic append's up to that rounding."""
+    rope = "f32" if latent == "f32" else "bf16"
+    case = make(B=5, lens=("list", [3, 0, 70001, 40, 31]), n_new=3, d_model=1024, extra_cap=1, gap_rows=2,
+                latent_dtype=latent, rope_dtype=rope, act_dtype="bf16", seed=56, **V3)
+    run = GpuRun(gpu, case)
+    valid = np.zeros(case.n_rows, dtype=bool)
+    for b in range(case.B):
+        valid[case.seq_start[b]:case.seq_start[b] + case.lens[b]] = True
+    vmask = torch.from_numpy(valid).to(run.t["rows"].device)
+    run.t["rows"].copy_(torch.where(vmask[:, None], run.t["rows"], torch.full_like(run.t["rows"], 0xA5)))
+    before = run.t["rows"].cpu().numpy().copy()
+    if run.t["scale"] is not None:
+        run.t["scale"].fill_(-7.0)
+    run.append()
+    assert run.status() == 0
+    after = run.t["rows"].cpu().numpy()
+    assert np.array_equal(run.t["seq_len"].cpu().numpy(), case.lens + 3)
+    ap = oracle_append(case)
+    rows = ap["rows"].reshape(-1)
+    written = np.zeros(case.n_rows, dtype=bool)
+    written[rows] = True
+    for b in range(case.B):
+        r0 = case.seq_start[b] + case.lens[b]
+        assert np.all(written[r0:r0 + 3])
+    assert np.array_equal(after[~written], before[~written])
+    from oracle import mla as omla
+    scale = run.t["scale"].cpu().numpy() if run.t["scale"] is not None else None
+    C, R = omla.decode_rows(after[rows], latent, rope, case.d_c, case.d_rope, None if scale is None else scale[rows])
+    refC = ap["c"].reshape(len(rows), -1)
+    refR = ap["k_rope"].reshape(len(rows), -1)
+    if latent == "fp8":
+        s_ref = ap["scale"].reshape(-1)
+        assert np.allclose(scale[rows], s_ref, rtol=1e-5, atol=0)
+        step = np.maximum(np.abs(refC) * 2.0 ** -3, s_ref[:, None].astype(np.float64) * 2.0 ** -9)
+        assert np.all(np.abs(C - refC) <= step * 1.0001)
+        untouched = np.ones(case.n_rows, dtype=bool)
+        untouched[rows] = False
+        assert np.all(scale[untouched] == -7.0)
+    elif latent == "bf16":
+        assert np.all(np.abs(C - refC) <= np.abs(refC) * 2.0 ** -7 + 1e-30)
+    else:
+        assert np.max(np.abs(C - refC)) <= 1e-5 * np.max(np.abs(refC))
+    tol_r = 2.0 ** -7 if rope == "bf16" else 1e-5
+    assert np.all(np.abs(R - refR) <= np.abs(refR) * tol_r + 1e-6)
+    # the generic append of the same tokens agrees within the same rounding
+    run2 = GpuRun(gpu, case)
+    monkeypatch.setenv("MLA_FORCE_GENERIC", "1")
+    run2.append()
+    monkeypatch.delenv("MLA_FORCE_GENERIC")
+    assert run2.status() == 0
+    C2, R2 = omla.decode_rows(run2.t["rows"].cpu().numpy()[rows], latent, rope, case.d_c, case.d_rope,
+                              None if scale is None else run2.t["scale"].cpu().numpy()[rows])
+    assert np.max(np.abs(C2 - C)) <= np.max(np.abs(refC)) * (2.0 ** -3 if latent == "fp8" else 2.0 ** -7)
