@@ -210,6 +210,25 @@ __device__ __forceinline__ TileSrc tile_src(const Item &it, int tile) {
   return r;
 }
 
+// Source of the k_rope copy of wave w: lane i reads chunk (i % 8) ^ rsw(t)
+// of token t = 8 w + i / 8, clamped to the item's last token. The base is
+// the wave's first (clamped) row, so the lane offset stays within 8 rows and
+// never goes negative, also for a tile past the item's end (tmax < 0).
+struct RopeSrc {
+  const char *base;
+  uint32_t voff;
+};
+__device__ __forceinline__ RopeSrc rope_src(const TileSrc &src, int w, int lane) {
+  const int ln = opaque(lane);
+  const int t = 8 * w + (ln >> 3);
+  const int t0 = min(8 * w, src.tmax);
+  RopeSrc r;
+  r.base = src.base + static_cast<int64_t>(t0) * src.stride;
+  r.voff = static_cast<uint32_t>(min(t, src.tmax) - t0) * static_cast<uint32_t>(src.stride) + 1024u +
+           16u * static_cast<uint32_t>((ln & 7) ^ rsw(t));
+  return r;
+}
+
 // bf16 tile copy, 9 loads per wave (w uniform): x < 8 copies the 1024 latent
 // bytes of token 8 w + x into its LDS row (lane i: bytes 16 i .. 16 i + 15);
 // x = 8 copies the k_rope parts of tokens 8 w .. 8 w + 7 (lane i: token
@@ -223,11 +242,8 @@ __device__ __forceinline__ void dma_bf16_piece(const TileSrc &src, int w, int la
     const char *row = src.base + static_cast<int64_t>(min(t, src.tmax)) * src.stride;
     lds_dma16(row, static_cast<uint32_t>(16 * lane), lds0 + M::lat(B) + sk::LROW * t);
   } else {
-    const int ln = opaque(lane);
-    const int t = 8 * w + (ln >> 3);
-    const uint32_t voff = static_cast<uint32_t>(min(t, src.tmax)) * static_cast<uint32_t>(src.stride) + 1024u +
-                          16u * static_cast<uint32_t>((ln & 7) ^ rsw(t));
-    lds_dma16(src.base, voff, lds0 + M::rope(B) + 1024 * w);
+    const RopeSrc r = rope_src(src, w, lane);
+    lds_dma16(r.base, r.voff, lds0 + M::rope(B) + 1024 * w);
   }
 }
 template <int B>
@@ -386,15 +402,32 @@ __device__ __forceinline__ f16x8 value_frag(const WaveState &st, int j, int kb) 
 // products later), chunks 5..8 under the value products (load at
 // 8 (x - 5), store four products later). Spreading it keeps the vector-ALU
 // work next to each matrix-core op small enough to run in its shadow.
+//
+// Both run unconditionally, also in an item's last steps: a copy of a tile
+// past the item's end re-reads its last row (in bounds, cached) into a
+// buffer nobody reads any more, and the widening of such a tile rewrites
+// that dead buffer. Branch-free steps let the compiler count outstanding
+// LDS operations exactly, so no wait drains the fragment prefetch. The
+// latent copy's source row pointer advances by the stride per row (no
+// multiply), and stops at the item's last row.
 template <int DMA_BUF, int WIDEN_BUF>
 struct HideBf16 {
-  TileSrc src;
+  const char *row;        // latent source of the next copy
+  const char *rope_base;  // the k_rope copy's base row (rope_src)
+  int64_t stride;
+  int lim;                // rows 8 w + x with x <= lim exist; later ones repeat the last
+  uint32_t rope_voff;     // this lane's k_rope source offset from rope_base
   int w, lane, tid;
-  bool dma_on, widen_on;
   u32x4 v;
   __device__ __forceinline__ void score_step(int kk) {
-    if (kk % 4 == 0 && kk / 4 < 9 && dma_on) dma_bf16_piece<DMA_BUF>(src, w, lane, kk / 4);
-    if (kk >= 2 && (kk - 2) / 7 < 5 && widen_on) {
+    using M = sk::Map<false>;
+    if (kk % 4 == 0 && kk / 4 < 8) {
+      const int x = kk / 4;
+      lds_dma16(row, static_cast<uint32_t>(16 * lane), LDS_OFF(g_lds) + M::lat(DMA_BUF) + sk::LROW * (8 * w + x));
+      row += x + 1 <= lim ? stride : 0;
+    }
+    if (kk == 32) lds_dma16(rope_base, rope_voff, LDS_OFF(g_lds) + M::rope(DMA_BUF) + 1024 * w);
+    if (kk >= 2 && (kk - 2) / 7 < 5) {
       const int x = (kk - 2) / 7, ph = (kk - 2) % 7;
       if (ph == 0) v = widen_bf16_load<WIDEN_BUF>(tid, x);
       if (ph == 4) widen_bf16_store<WIDEN_BUF>(tid, x, v);
@@ -402,7 +435,7 @@ struct HideBf16 {
   }
   __device__ __forceinline__ void value_step(int n) {
     const int x = 5 + n / 8, ph = n % 8;
-    if (x < 9 && widen_on) {
+    if (x < 9) {
       if (ph == 0) v = widen_bf16_load<WIDEN_BUF>(tid, x);
       if (ph == 4) widen_bf16_store<WIDEN_BUF>(tid, x, v);
     }
@@ -562,15 +595,21 @@ __device__ __forceinline__ void compute_tile(WaveState &st, int valid, Hide &hid
 // into the buffer tile i-1 used.
 template <int B>
 __device__ __forceinline__ void step_bf16(WaveState &st, const Item &it, int i, int w, int lane, int tid) {
-  if (i + 2 < it.ntiles) wait_vm_lds<9>(); else wait_vm_lds<0>();
+  wait_vm_lds<9>();  // every step issues 9 copies; the previous step's may still fly
   __builtin_amdgcn_s_barrier();
   HideBf16<(B + 3) % 4, (B + 1) % 4> h;
-  h.src = tile_src(it, i + 3);
+  const TileSrc src = tile_src(it, i + 3);
+  h.stride = src.stride;
+  h.lim = src.tmax - 8 * w;
+  h.row = src.base + static_cast<int64_t>(min(8 * w, src.tmax)) * src.stride;
+  {
+    const RopeSrc r = rope_src(src, w, lane);
+    h.rope_base = r.base;
+    h.rope_voff = r.voff;
+  }
   h.w = w;
   h.lane = lane;
   h.tid = opaque(tid);
-  h.dma_on = i + 3 < it.ntiles;
-  h.widen_on = i + 1 < it.ntiles;
   compute_tile<false, B>(st, min(sk::T, it.t1 - (it.t0 + i * sk::T)), h);
 }
 
@@ -637,9 +676,9 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
     if (it.ntiles > 1) dma_raw<1>(it, 1, w, lane);
     if (it.ntiles > 2) dma_raw<2>(it, 2, w, lane);
   } else {
-    dma_bf16<0>(it, 0, w, lane);
-    if (it.ntiles > 1) dma_bf16<1>(it, 1, w, lane);
-    if (it.ntiles > 2) dma_bf16<2>(it, 2, w, lane);
+    dma_bf16<0>(it, 0, w, lane);  // tiles past the end re-read the last row, like the steps
+    dma_bf16<1>(it, 1, w, lane);
+    dma_bf16<2>(it, 2, w, lane);
   }
 
   WaveState st;
@@ -691,7 +730,7 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
       if (i + 5 < it.ntiles) step_fp8<2, 1>(st, it, i + 5, w, lane, tid);
     }
   } else {
-    if (it.ntiles > 2) wait_vm<18>(); else if (it.ntiles > 1) wait_vm<9>(); else wait_vm<0>();
+    wait_vm<18>();
     __builtin_amdgcn_s_barrier();
     widen_bf16_inplace<0>(tid);
     for (int i = 0; i < it.ntiles; i += 4) {
@@ -702,6 +741,7 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
     }
   }
 
+  wait_vm<0>();  // no copy may still be landing in LDS when the workgroup ends
   // ---- normalised partials and log-sum-exp (base 2): each wave writes its
   // 128 latent columns of all 128 heads, dividing by the denominators the
   // scoring waves hand over
