@@ -38,6 +38,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -78,9 +79,12 @@ bool decode_fast_path(const mla_dims &d, const mla_cache &c, mla_dtype q_w_dtype
 namespace {
 
 // ----------------------------------------------------------------- absorb
-// Grid (H, ceil(B/32)), 256 threads. W_UK,i [128 x 512] is staged in LDS
-// (128 KB) and read transposed as the A operand of q~^T = W_UK,i^T q_nope^T.
-// Each wave owns 128 latent columns (4 blocks of 32) for 32 sequences.
+// Grid (H, 4, ceil(B/32)), 256 threads: head i, latent quarter cq (columns
+// 128 cq .. +127), 32 sequences. The quarter of W_UK,i [128 n x 128 c] is
+// staged in LDS with a 288-byte row stride (rows 32 bytes apart in the banks,
+// so the transposed reads below are conflict-free) and read transposed as the
+// A operand of q~^T = W_UK,i^T q_nope^T; wave w owns columns 32 w of the
+// quarter. The quarter also rotates RoPE pairs 8 cq .. 8 cq + 7 of q_rope.
 __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qscale, float rope_base,
                                                           const uint16_t *__restrict__ q_nope,
                                                           const uint16_t *__restrict__ q_rope,
@@ -89,28 +93,35 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qs
                                                           const SeqInfo *__restrict__ seqs,
                                                           uint16_t *__restrict__ Q) {
   using namespace fast;
-  extern __shared__ __attribute__((aligned(16))) char smem[];  // [128][512] bf16
-  const int i = blockIdx.x, b0 = blockIdx.y * 32;
+  constexpr int WROW = 288;  // LDS bytes per W row (128 columns = 256 bytes + 32)
+  __shared__ __attribute__((aligned(16))) char smem[DNOPE * WROW];
+  const int i = blockIdx.x, cq = blockIdx.y, b0 = blockIdx.z * 32;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const uint16_t *W = w_uk + static_cast<size_t>(i) * DNOPE * DC;
-  // 128 KB of weights: 8192 chunks of 16 bytes, 32 per thread
-  for (int q = tid; q < DNOPE * DC / 8; q += 256)
-    *reinterpret_cast<u32x4 *>(smem + q * 16) = *reinterpret_cast<const u32x4 *>(W + q * 8);
-
-  // RoPE part: thread per (sequence, pair) within this sequence tile
-  for (int x = tid; x < 32 * (DR / 2); x += 256) {
-    const int bb = b0 + x / (DR / 2), p = x % (DR / 2);
-    if (bb >= B) continue;
-    const size_t bi = static_cast<size_t>(bb) * H + i;
-    const int64_t P = q_pos ? q_pos[bb] : static_cast<int64_t>(seqs[bb].len) - 1;
-    float cs, sn;
-    rope_cos_sin(P, p, DR, rope_base, &cs, &sn);
-    const float x0 = bf16_bits_to_f32(q_rope[bi * DR + 2 * p]);
-    const float x1 = bf16_bits_to_f32(q_rope[bi * DR + 2 * p + 1]);
-    Q[bi * D + DC + 2 * p] = __builtin_bit_cast(uint16_t, static_cast<_Float16>((x0 * cs - x1 * sn) * qscale));
-    Q[bi * D + DC + 2 * p + 1] = __builtin_bit_cast(uint16_t, static_cast<_Float16>((x0 * sn + x1 * cs) * qscale));
+  const uint16_t *W = w_uk + static_cast<size_t>(i) * DNOPE * DC + 128 * cq;
+  // 32 KB of weights: 128 rows x 16 chunks of 16 bytes, 8 per thread
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const int q = tid + 256 * x, n = q >> 4, ch = q & 15;
+    *reinterpret_cast<u32x4 *>(smem + n * WROW + 16 * ch) = *reinterpret_cast<const u32x4 *>(W + n * DC + 8 * ch);
   }
-  __syncthreads();
+
+  // RoPE: thread (sequence b0 + tid / 8, pair 8 cq + tid % 8)
+  {
+    const int bb = b0 + (tid >> 3), p = 8 * cq + (tid & 7);
+    if (bb < B) {
+      const size_t bi = static_cast<size_t>(bb) * H + i;
+      const int64_t P = q_pos ? q_pos[bb] : static_cast<int64_t>(seqs[bb].len) - 1;
+      float cs, sn;
+      rope_cos_sin(P, p, DR, rope_base, &cs, &sn);
+      const uint32_t xr = *reinterpret_cast<const uint32_t *>(q_rope + bi * DR + 2 * p);
+      const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(xr & 0xffffu));
+      const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(xr >> 16));
+      f16x2 r;
+      r[0] = static_cast<_Float16>((x0 * cs - x1 * sn) * qscale);
+      r[1] = static_cast<_Float16>((x0 * sn + x1 * cs) * qscale);
+      *reinterpret_cast<f16x2 *>(Q + bi * D + DC + 2 * p) = r;
+    }
+  }
 
   // B operand: q_nope^T [16 n x 32 b]: lane holds sequence b0 + l%32, n = 16 kk + 8(l/32) .. +7
   const int bb = b0 + (lane & 31);
@@ -124,37 +135,35 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qs
       qb[kk] = bf16x8{};
     }
   }
+  __syncthreads();
   // A operand: W^T [32 c x 16 n] via transposed LDS reads of W [n][c], with
   // the same contiguous k order as the B operand: in 16-lane group g the
   // lanes take c = c0 + 16(g%2) + i and n = 16 kk + 8(g/2) + e, e = 0..3 from
   // the first read and 4..7 from the second; source lane j points at
   // W[16 kk + 8(g/2) + j/4 (+4)][c0 + 16(g%2) + 4(j%4)].
   const int g = (lane >> 4) & 3, j = lane & 15;
+  const int c0 = 32 * w;
+  f32x16 acc = {};
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int c0 = 128 * w + 32 * cb;
-    f32x16 acc = {};
+  for (int kk = 0; kk < DNOPE / 16; ++kk) {
+    const int n0 = 16 * kk + 8 * (g >> 1) + (j >> 2);
+    const int cc = c0 + 16 * (g & 1) + 4 * (j & 3);
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, smem + n0 * WROW + cc * 2));
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, smem + (n0 + 4) * WROW + cc * 2));
+    bf16x8 a;
+    a.lo = __builtin_bit_cast(bf16x4, lo);
+    a.hi = __builtin_bit_cast(bf16x4, hi);
+    acc = mfma32(a, qb[kk], acc);
+  }
+  // D [32 c x 32 b]: lane holds sequence b0 + l%32, c = c0 + 8(r/4) + 4(l/32) + r%4
+  if (bb < B) {
+    uint16_t *dst = Q + (static_cast<size_t>(bb) * H + i) * D + 128 * cq + c0 + 4 * (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < DNOPE / 16; ++kk) {
-      const int n0 = 16 * kk + 8 * (g >> 1) + (j >> 2);
-      const int cc = c0 + 16 * (g & 1) + 4 * (j & 3);
-      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, smem + (n0 * DC + cc) * 2));
-      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, smem + ((n0 + 4) * DC + cc) * 2));
-      bf16x8 a;
-      a.lo = __builtin_bit_cast(bf16x4, lo);
-      a.hi = __builtin_bit_cast(bf16x4, hi);
-      acc = mfma32(a, qb[kk], acc);
-    }
-    // D [32 c x 32 b]: lane holds sequence b0 + l%32, c = c0 + 8(r/4) + 4(l/32) + r%4
-    if (bb < B) {
-      uint16_t *dst = Q + (static_cast<size_t>(bb) * H + i) * D + c0 + 4 * (lane >> 5);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      f16x4 v;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f16x4 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = static_cast<_Float16>(acc[4 * g4 + r] * qscale);
-        *reinterpret_cast<f16x4 *>(dst + 8 * g4) = v;
-      }
+      for (int r = 0; r < 4; ++r) v[r] = static_cast<_Float16>(acc[4 * g4 + r] * qscale);
+      *reinterpret_cast<f16x4 *>(dst + 8 * g4) = v;
     }
   }
 }
@@ -384,16 +393,8 @@ hipError_t launch_append_finish(hipStream_t s, const mla_dims &d, const mla_cach
 hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, const void *q_nope,
                               const void *q_rope, const int32_t *q_pos, const void *w_uk,
                               const SeqInfo *seqs, uint16_t *q_out) {
-  const size_t shm = fast::DNOPE * fast::DC * 2;  // 128 KB
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(absorb_fast_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  return launch_kernel(absorb_fast_kernel, dim3(d.n_heads, (batch + 31) / 32), 256, shm, s, batch, d.n_heads,
-                       d.softmax_scale * kLog2e, d.rope_base, static_cast<const uint16_t *>(q_nope),
+  return launch_kernel(absorb_fast_kernel, dim3(d.n_heads, fast::DC / 128, (batch + 31) / 32), 256, 0, s, batch,
+                       d.n_heads, d.softmax_scale * kLog2e, d.rope_base, static_cast<const uint16_t *>(q_nope),
                        static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seqs, q_out);
 }
 

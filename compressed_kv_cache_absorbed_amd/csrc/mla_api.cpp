@@ -4,10 +4,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "mla_internal.hpp"
@@ -272,6 +274,8 @@ mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32
   p->chunk = static_cast<int32_t>(C);
   p->n_workers = n_workers;
   p->lens.assign(host_lens, host_lens + batch);
+  static std::atomic<uint64_t> next_id{1};
+  p->id = next_id.fetch_add(1);
   p->host_block_bytes = sizeof(WorkItem) * kept.size() + sizeof(SeqInfo) * batch;
   void *blk = nullptr;
   if (hipHostMalloc(&blk, p->host_block_bytes, hipHostMallocDefault) == hipSuccess && blk) {
@@ -323,8 +327,42 @@ size_t mla_decode_workspace_bytes(const mla_dims *dims, const mla_plan *plan) {
   return decode_ws_layout(*dims, plan->batch, plan->n_items).total;
 }
 
+// The device copy of a plan's work list lives in the workspace. A decode
+// whose workspace already holds the copy of the same plan (made by an
+// earlier call on it, and not overwritten since) skips the upload: one fewer
+// copy per step. mla_workspace_init and the matrix-core append (whose
+// partial products share that region) forget the workspace's entry.
+namespace {
+struct PlanCopies {
+  std::mutex mu;
+  std::unordered_map<const void *, uint64_t> last;
+};
+PlanCopies &plan_copies() {
+  static PlanCopies *p = new PlanCopies();
+  return *p;
+}
+}  // namespace
+
+static bool plan_copy_current(const void *ws, uint64_t id) {
+  PlanCopies &c = plan_copies();
+  std::lock_guard<std::mutex> g(c.mu);
+  auto it = c.last.find(ws);
+  return it != c.last.end() && it->second == id;
+}
+static void plan_copy_record(const void *ws, uint64_t id) {
+  PlanCopies &c = plan_copies();
+  std::lock_guard<std::mutex> g(c.mu);
+  c.last[ws] = id;
+}
+static void plan_copy_forget(const void *ws) {
+  PlanCopies &c = plan_copies();
+  std::lock_guard<std::mutex> g(c.mu);
+  c.last.erase(ws);
+}
+
 mla_status mla_workspace_init(void *ws, size_t ws_bytes, void *stream) {
   if (!ws || ws_bytes < kStatusBytes || !aligned16(ws)) return MLA_ERR_INVALID_ARG;
+  plan_copy_forget(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   MLA_LAUNCH(s, K_INIT, launch_init(s, static_cast<int32_t *>(ws)));
   return MLA_OK;
@@ -369,6 +407,7 @@ static mla_status do_append(const mla_dims *dims, const mla_cache *cache, const 
   if (append_fast_path(*dims, cache->batch * n_new, act)) {
     const AppendWs w = append_ws_layout(*dims, cache->batch, n_new);
     float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + w.partial);
+    plan_copy_forget(ws);  // the partial products overwrite the plan's copy
     MLA_LAUNCH(s, K_APPEND_GEMM,
                launch_append_fast(s, *dims, *cache, h, n_new, w_dkv, w_kr, partial, w.ksplit, status));
     MLA_LAUNCH(s, K_APPEND_FINISH, launch_append_finish(s, *dims, *cache, n_new, partial, w.ksplit, status));
@@ -422,8 +461,11 @@ static mla_status do_decode(const mla_dims *dims, const mla_cache *cache, const 
   int32_t *status = reinterpret_cast<int32_t *>(base + w.status);
   WorkItem *items = reinterpret_cast<WorkItem *>(base + w.items);
   SeqInfo *seqs = reinterpret_cast<SeqInfo *>(base + w.seqs);
-  if (hipMemcpyAsync(items, plan->host_block, plan->host_block_bytes, hipMemcpyHostToDevice, s) != hipSuccess)
-    return MLA_ERR_HIP;
+  if (!plan_copy_current(ws, plan->id)) {
+    if (hipMemcpyAsync(items, plan->host_block, plan->host_block_bytes, hipMemcpyHostToDevice, s) != hipSuccess)
+      return MLA_ERR_HIP;
+    plan_copy_record(ws, plan->id);
+  }
   float *opart = reinterpret_cast<float *>(base + w.opart);
   float *lse = reinterpret_cast<float *>(base + w.lse);
   if (decode_fast_path(*dims, *cache, qw)) {

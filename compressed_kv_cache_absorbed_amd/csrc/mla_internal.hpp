@@ -56,6 +56,7 @@ struct mla_plan {
   int32_t n_items = 0;
   int32_t chunk = 0;
   int32_t n_workers = 0;
+  uint64_t id = 0;             // unique per plan made in this process
   void *host_block = nullptr;  // pinned: [n_items WorkItem][batch SeqInfo]
   size_t host_block_bytes = 0;
   bool pinned = false;

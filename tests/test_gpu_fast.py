@@ -170,3 +170,31 @@ def test_fast_append_rows_and_canary(gpu, latent, monkeypatch):
     C2, R2 = omla.decode_rows(run2.t["rows"].cpu().numpy()[rows], latent, rope, case.d_c, case.d_rope,
                               None if scale is None else run2.t["scale"].cpu().numpy()[rows])
     assert np.max(np.abs(C2 - C)) <= np.max(np.abs(refC)) * (2.0 ** -3 if latent == "fp8" else 2.0 ** -7)
+
+
+def test_plan_copy_reuse_and_invalidation(gpu):
+    """A workspace keeps the device copy of the last plan it ran, so a second
+    decode with the same plan skips the upload. An append through the same
+    workspace overwrites that copy and must force the next decode to upload
+    the plan again: decode cache A, append into cache B with the shared
+    workspace, decode A again with the same plan -> identical outputs."""
+    case_a = v3_case([300, 77, 1025], seed=57)
+    case_b = make(B=2, lens=("list", [5, 9]), n_new=2, d_model=512, latent_dtype="bf16", rope_dtype="bf16",
+                  act_dtype="bf16", seed=58, **V3)
+    run_a = GpuRun(gpu, case_a)
+    run_b = GpuRun(gpu, case_b)
+    plan_a = run_a.plan(n_workers=8)
+    o1 = to_np(run_a.decode(plan=plan_a))
+    o2 = to_np(run_a.decode(plan=plan_a))
+    assert np.array_equal(o1, o2)
+    need = max(run_a.ws.numel(), gpu.mla_append_workspace_bytes(run_b.d, case_b.B, case_b.n_new))
+    if run_a.ws.numel() < need:
+        run_a.ws = torch.empty(need, dtype=torch.uint8, device=run_a.ws.device)
+        gpu.mla_workspace_init(run_a.ws)
+        o1 = to_np(run_a.decode(plan=plan_a))
+    run_b.ws = run_a.ws
+    run_b.append()
+    assert run_b.status() == 0
+    o3 = to_np(run_a.decode(plan=plan_a))
+    assert np.array_equal(o1, o3)
+    check(case_a, o3, TOL_BF16_REL)
