@@ -172,15 +172,15 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qs
 // Grid (batch, H/32, d_c/32), 256 threads: sequence b, head block hb,
 // latent block db (32 columns). Log-sum-exp merge of the sequence's split
 // partials (base 2): o^ = sum_s 2^(lse_s - M) o^_s / sum_s 2^(lse_s - M).
-// In the fragment order of the partials the (hb, db) block is 4 KB
-// contiguous per split; thread (g = tid / 64, lane) owns the float4 at
+// In the fragment order of the (fp16) partials the (hb, db) block is 2 KB
+// contiguous per split; thread (g = tid / 64, lane) owns the four values at
 // 256 g + 4 lane of it (head hl = lane % 32, columns 8 g + 4 (lane / 32) ..),
 // and keeps 8 splits' loads in flight. The result goes out as bf16 hi and
 // lo planes (lo = bf16(o^ - hi), about 16 significant bits), laid out
 // [head][sequence][column] for the W_UV product, through an LDS transpose.
 __global__ __launch_bounds__(256) void merge_fast_kernel(int B, int H, const SeqInfo *__restrict__ seqs,
                                                          const int32_t *__restrict__ dev_len,
-                                                         const float *__restrict__ opart,
+                                                         const uint16_t *__restrict__ opart,
                                                          const float *__restrict__ lse, uint16_t *__restrict__ ohat) {
   using namespace fast;
   constexpr int SB = 8;  // splits loaded per batch
@@ -199,24 +199,24 @@ __global__ __launch_bounds__(256) void merge_fast_kernel(int B, int H, const Seq
       float den = 0.0f;
       for (int s = 0; s < S; ++s) den += exp2f(lrow[static_cast<size_t>(s) * H] - M);
       const float inv = 1.0f / den;
-      const size_t stride = static_cast<size_t>(H / 32) * 16 * 1024;  // floats per item
-      const float *src = opart + (static_cast<size_t>(si.item_begin) * (H / 32) + hb) * (16 * 1024) + 1024 * db +
-                         256 * g + 4 * lane;
+      const size_t stride = static_cast<size_t>(H / 32) * 16 * 1024;  // elements per item
+      const uint16_t *src = opart + (static_cast<size_t>(si.item_begin) * (H / 32) + hb) * (16 * 1024) + 1024 * db +
+                            256 * g + 4 * lane;
       for (int s0 = 0; s0 < S; s0 += SB) {
-        float4 x[SB];
+        f16x4 x[SB];
         float wt[SB];
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
           const int s = min(s0 + u, S - 1);
           wt[u] = s0 + u < S ? exp2f(lrow[static_cast<size_t>(s) * H] - M) * inv : 0.0f;
-          x[u] = *reinterpret_cast<const float4 *>(src + s * stride);
+          x[u] = *reinterpret_cast<const f16x4 *>(src + s * stride);
         }
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
-          acc.x = fmaf(wt[u], x[u].x, acc.x);
-          acc.y = fmaf(wt[u], x[u].y, acc.y);
-          acc.z = fmaf(wt[u], x[u].z, acc.z);
-          acc.w = fmaf(wt[u], x[u].w, acc.w);
+          acc.x = fmaf(wt[u], static_cast<float>(x[u][0]), acc.x);
+          acc.y = fmaf(wt[u], static_cast<float>(x[u][1]), acc.y);
+          acc.z = fmaf(wt[u], static_cast<float>(x[u][2]), acc.z);
+          acc.w = fmaf(wt[u], static_cast<float>(x[u][3]), acc.w);
         }
       }
     }
@@ -399,7 +399,7 @@ hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, c
 }
 
 hipError_t launch_merge_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const SeqInfo *seqs,
-                             const float *opart, const float *lse, uint16_t *ohat) {
+                             const uint16_t *opart, const float *lse, uint16_t *ohat) {
   return launch_kernel(merge_fast_kernel, dim3(c.batch, d.n_heads / 32, fast::DC / 32), 256, 0, s, c.batch,
                        d.n_heads, seqs, c.seq_len, opart, lse, ohat);
 }

@@ -637,7 +637,7 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
                                                         const WorkItem *__restrict__ items,
                                                         const SeqInfo *__restrict__ seqs,
                                                         const uint16_t *__restrict__ Q,
-                                                        float *__restrict__ opart,
+                                                        uint16_t *__restrict__ opart,
                                                         float *__restrict__ lse,
                                                         int32_t *__restrict__ status) {
   using namespace sk;
@@ -648,16 +648,16 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
   const int hl = lane & 31, half = lane >> 5;
   const int head = blockIdx.y * 128 + 32 * w + hl;
   const WorkItem wi = items[k];
-  // this workgroup's 128 heads of item k: 4 head blocks of 64 KB in the
-  // fragment order of the partials
-  float *ob = opart + (static_cast<size_t>(k) * (H / 32) + blockIdx.y * 4) * (16 * 1024);
+  // this workgroup's 128 heads of item k: 4 head blocks of 32 KB in the
+  // fragment order of the (fp16) partials
+  uint16_t *ob = opart + (static_cast<size_t>(k) * (H / 32) + blockIdx.y * 4) * (16 * 1024);
 
   const bool ok = c.seq_len[wi.b] == seqs[wi.b].len && wi.t0 >= 0 && wi.t0 < wi.t1 &&
                   wi.t1 <= c.seq_cap[wi.b] && static_cast<int64_t>(c.seq_start[wi.b]) >= 0 &&
                   static_cast<int64_t>(c.seq_start[wi.b]) + wi.t1 <= c.n_rows;
   if (!ok) {
     if (tid == 0 && blockIdx.y == 0) set_status(status, MLA_ERR_PLAN);
-    for (int x = tid; x < 4 * 16 * 256; x += 256) reinterpret_cast<float4 *>(ob)[x] = make_float4(0, 0, 0, 0);
+    for (int x = tid; x < 4 * 16 * 256 / 2; x += 256) reinterpret_cast<u32x4 *>(ob)[x] = u32x4{0, 0, 0, 0};
     if (half == 0) lse[static_cast<size_t>(k) * H + head] = -INFINITY;
     return;
   }
@@ -752,8 +752,8 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
   }
   wait_lds();
   __builtin_amdgcn_s_barrier();
-  // register group g4 of accumulator (j, hb) is one 1 KB run: head block
-  // hb, latent block 4 w + j
+  // register group g4 of accumulator (j, hb) is one 512-byte run: head
+  // block hb, latent block 4 w + j
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
     const float inv = 1.0f / gstat[32 * hb + hl];
@@ -762,8 +762,10 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const f32x16 &x = st.O[4 * j + hb];
-        *reinterpret_cast<float4 *>(ob + ((hb * 16 + 4 * w + j) * 4 + g4) * 256 + 4 * lane) =
-            make_float4(x[4 * g4] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv);
+        f16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(x[4 * g4 + e] * inv);
+        *reinterpret_cast<f16x4 *>(ob + ((hb * 16 + 4 * w + j) * 4 + g4) * 256 + 4 * lane) = v;
       }
     }
   }
@@ -772,7 +774,7 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
 }  // namespace
 
 hipError_t launch_decode_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,
-                              const WorkItem *items, const SeqInfo *seqs, const uint16_t *q, float *opart,
+                              const WorkItem *items, const SeqInfo *seqs, const uint16_t *q, uint16_t *opart,
                               float *lse, int32_t *status) {
   if (n_items == 0) return hipSuccess;
   const dim3 grid(n_items, d.n_heads / 128);

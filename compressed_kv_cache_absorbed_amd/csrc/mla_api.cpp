@@ -327,6 +327,8 @@ size_t mla_decode_workspace_bytes(const mla_dims *dims, const mla_plan *plan) {
   return decode_ws_layout(*dims, plan->batch, plan->n_items).total;
 }
 
+}  // extern "C"
+
 // The device copy of a plan's work list lives in the workspace. A decode
 // whose workspace already holds the copy of the same plan (made by an
 // earlier call on it, and not overwritten since) skips the upload: one fewer
@@ -359,6 +361,8 @@ static void plan_copy_forget(const void *ws) {
   std::lock_guard<std::mutex> g(c.mu);
   c.last.erase(ws);
 }
+
+extern "C" {
 
 mla_status mla_workspace_init(void *ws, size_t ws_bytes, void *stream) {
   if (!ws || ws_bytes < kStatusBytes || !aligned16(ws)) return MLA_ERR_INVALID_ARG;
@@ -467,15 +471,16 @@ static mla_status do_decode(const mla_dims *dims, const mla_cache *cache, const 
     plan_copy_record(ws, plan->id);
   }
   float *opart = reinterpret_cast<float *>(base + w.opart);
+  uint16_t *opart16 = reinterpret_cast<uint16_t *>(base + w.opart);
   float *lse = reinterpret_cast<float *>(base + w.lse);
   if (decode_fast_path(*dims, *cache, qw)) {
     uint16_t *q = reinterpret_cast<uint16_t *>(base + w.q);
     MLA_LAUNCH(s, K_ABSORB_FAST,
                launch_absorb_fast(s, *dims, plan->batch, q_nope, q_rope, q_pos, w_uk, seqs, q));
     MLA_LAUNCH(s, cache->latent_dtype == MLA_FP8_E4M3 ? K_DECODE_FP8 : K_DECODE_BF16,
-               launch_decode_fast(s, *dims, *cache, plan->n_items, items, seqs, q, opart, lse, status));
+               launch_decode_fast(s, *dims, *cache, plan->n_items, items, seqs, q, opart16, lse, status));
     uint16_t *ohat = reinterpret_cast<uint16_t *>(base + w.ohat);
-    MLA_LAUNCH(s, K_MERGE_FAST, launch_merge_fast(s, *dims, *cache, seqs, opart, lse, ohat));
+    MLA_LAUNCH(s, K_MERGE_FAST, launch_merge_fast(s, *dims, *cache, seqs, opart16, lse, ohat));
     MLA_LAUNCH(s, K_PROJECT_FAST, launch_project_fast(s, *dims, plan->batch, ohat, w_uv, o, od));
   } else {
     float *q = reinterpret_cast<float *>(base + w.q);
