@@ -44,6 +44,7 @@ namespace mla {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -64,6 +65,7 @@ constexpr int RAW_TILE = T * RAW_ROWB;                 // 20480
 constexpr int RAW_DMA_PER_WAVE = RAW_TILE / 1024 / 4;  // 5
 constexpr int SLACK = 8;             // running max is kept unless exceeded by 2^8
 constexpr int SPF = 3;               // score fragments read ahead of their product
+constexpr int VBLK = 15;             // bf16 path: the output block kept in VGPRs (its AGPRs hold the scores)
 
 // LDS map. bf16 latents: four fp16 tiles. fp8 latents: two fp16 tiles, three
 // raw tiles and their per-token scales. Both: the P exchange (8 KB), the
@@ -90,6 +92,17 @@ namespace {
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// Value products with the accumulator's register file fixed (bf16 path:
+// every output block in AGPRs but one, whose AGPRs hold the scores), so the
+// compiler never moves a block between files. Operands come from LDS reads
+// (waited for by lgkmcnt) or from the rescale, which runs long before; the
+// leading s_nop covers a vector-ALU write of the VGPR-form accumulator.
+__device__ __forceinline__ void mfma_acc_a(f32x16 &c, f16x8 a, f16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc_v(f32x16 &c, f16x8 a, f16x8 b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 
 // Score products (fp16 x fp16 -> fp32) in VGPR form, issued as inline asm: the compiler would
@@ -120,6 +133,7 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x16 &x, f32x16 &y) {
 __device__ __forceinline__ void mfma_vgpr_drain(f32x16 &x) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
 }
+
 
 // 2 bf16 (one dword) -> 2 fp16, exact for |x| < 65504 (a bf16 significand
 // fits in fp16's); round-toward-zero saturates larger magnitudes to +-65504.
@@ -356,11 +370,49 @@ struct WaveState {
   f16x8 qf[sk::D / 16];   // absorbed query (fp16), B operand of the scores
   f32x16 O[sk::DC / 32];
   float m, l;
-  int sl, sl2;   // latent score-fragment base (tiles 0, 1) and its copy for tiles 2, 3
-  int sr[4];     // k_rope score-fragment bases, by k-step
-  int vl, vl2;   // value-fragment base (tiles 0, 1) and its copy for tiles 2, 3
-  int half, hl, w, lane;
+  int w, lane;
 };
+
+// Fragment base addresses, recomputed from the lane index at the start of
+// each phase (from an opaque copy, so they are not hoisted into registers
+// kept live across the whole loop). Buffers 2 and 3 lie beyond the 16-bit
+// offset range of LDS reads and get their own base.
+struct ScoreBase {
+  int sl;  // latent A fragment, k-step 0: token hl, chunk half of the row
+  int sr;  // k_rope A fragment of k-step 32; k-step 32 + j is at sr ^ 32 j
+};
+template <bool FP8, int B>
+__device__ __forceinline__ ScoreBase score_base(int lane_) {
+  using M = sk::Map<FP8>;
+  const int ln = opaque(lane_), hl = ln & 31, half = ln >> 5;
+  ScoreBase b;
+  b.sl = sk::LROW * hl + 16 * half + (B < 2 ? 0 : M::lat(2));
+  // chunk (2 j + half) ^ rsw(hl) of the k_rope row: the XOR with 2 j only
+  // touches bits 5 and 6 of the byte offset, which the region base (a
+  // multiple of 128) and the row offset leave clear
+  static_assert(M::rope(0) % 128 == 0, "k_rope region alignment");
+  b.sr = M::rope(0) + 128 * hl + 16 * (half ^ rsw(hl));
+  return b;
+}
+// Value A fragment (transposed read): 16-lane group g, lane j in it points
+// at token 16 kb + 8 h + tt (tt = 4 (g/2) + j/4), latent column
+// 128 w + 32 jb + dd (dd = 16 (g%2) + 4 (j%4)). The P fragments follow the
+// lane index directly.
+struct ValueBase {
+  int vl, pl;
+};
+template <bool FP8, int B>
+__device__ __forceinline__ ValueBase value_base(int lane_, int w) {
+  using M = sk::Map<FP8>;
+  const int ln = opaque(lane_);
+  const int g = (ln >> 4) & 3, j = ln & 15;
+  const int tt = 4 * (g >> 1) + (j >> 2);
+  const int dd = 16 * (g & 1) + 4 * (j & 3);
+  ValueBase b;
+  b.vl = sk::LROW * tt + 2 * (128 * w + dd) + (B < 2 ? 0 : M::lat(2));
+  b.pl = M::px() + 16 * ln;
+  return b;
+}
 
 // Fragment reads. Score A fragment kk: token hl, dims 16 kk + 8 half .. +7
 // (one 16-byte read; latent for kk < 32, k_rope after). Value A fragment
@@ -368,21 +420,19 @@ struct WaveState {
 // + 8 (two transposed 8-byte reads). Value B fragment (hb, kb): P of head
 // block hb, k-step kb, as the scoring wave held it.
 template <bool FP8, int B>
-__device__ __forceinline__ f16x8 score_frag(const WaveState &st, int kk) {
+__device__ __forceinline__ f16x8 score_frag(const ScoreBase &sb, int kk) {
   using M = sk::Map<FP8>;
-  const char *p = kk < 32 ? (B < 2 ? g_lds + st.sl + M::lat(B) : g_lds + st.sl2 + (M::lat(B) - M::lat(2))) + 32 * kk
-                          : g_lds + st.sr[kk - 32] + (M::rope(B) - M::rope(0));
+  const char *p = kk < 32 ? g_lds + sb.sl + (B < 2 ? M::lat(B) : M::lat(B) - M::lat(2)) + 32 * kk
+                          : g_lds + (sb.sr ^ (32 * (kk - 32))) + (M::rope(B) - M::rope(0));
   return *reinterpret_cast<const f16x8 *>(p);
 }
-template <bool FP8>
-__device__ __forceinline__ f16x8 p_frag(const WaveState &st, int hb, int kb) {
-  return *reinterpret_cast<const f16x8 *>(g_lds + sk::Map<FP8>::px() + 16 * st.lane + 1024 * (2 * hb + kb));
+__device__ __forceinline__ f16x8 p_frag(const ValueBase &vb, int hb, int kb) {
+  return *reinterpret_cast<const f16x8 *>(g_lds + vb.pl + 1024 * (2 * hb + kb));
 }
 template <bool FP8, int B>
-__device__ __forceinline__ f16x8 value_frag(const WaveState &st, int j, int kb) {
+__device__ __forceinline__ f16x8 value_frag(const ValueBase &vb, int j, int kb) {
   using M = sk::Map<FP8>;
-  const char *p0 = (B < 2 ? g_lds + st.vl + M::lat(B) : g_lds + st.vl2 + (M::lat(B) - M::lat(2))) +
-                   sk::LROW * 16 * kb + 64 * j;
+  const char *p0 = g_lds + vb.vl + (B < 2 ? M::lat(B) : M::lat(B) - M::lat(2)) + sk::LROW * 16 * kb + 64 * j;
   const char *p1 = p0 + sk::LROW * 8;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(p0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(p1));
@@ -392,16 +442,16 @@ __device__ __forceinline__ f16x8 value_frag(const WaveState &st, int j, int kb) 
   return a;
 }
 
-// Work a step hides under the matrix-core loops of the tile it computes:
-// score_step(kk) runs after score product kk, value_step(n) after value
-// product n; each issues at most one load or one convert-and-store.
+// Work a step hides under its matrix-core loops: score_step(kk) runs after
+// score product kk, value_step(n) after value product n; each issues at most
+// one load or one convert-and-store.
 //
-// bf16 latents: the 9 direct loads of tile i+3 (one every fourth score
-// product) and the widening of tile i+1, 9 chunks per thread: chunks 0..4
-// under the score products (load at 7 x + 2, convert and store four
-// products later), chunks 5..8 under the value products (load at
-// 8 (x - 5), store four products later). Spreading it keeps the vector-ALU
-// work next to each matrix-core op small enough to run in its shadow.
+// bf16 latents: the 9 direct loads of tile i+3 go out under the score
+// products (one every fourth product, the k_rope part at product 32), and the
+// widening of tile i+2, 9 chunks of 16 bytes per thread, runs under the value
+// products, where the LDS has bandwidth to spare (chunk x is loaded after
+// product 3 x, and converted and stored three products later, just before
+// the next chunk's load).
 //
 // Both run unconditionally, also in an item's last steps: a copy of a tile
 // past the item's end re-reads its last row (in bounds, cached) into a
@@ -427,19 +477,16 @@ struct HideBf16 {
       row += x + 1 <= lim ? stride : 0;
     }
     if (kk == 32) lds_dma16(rope_base, rope_voff, LDS_OFF(g_lds) + M::rope(DMA_BUF) + 1024 * w);
-    if (kk >= 2 && (kk - 2) / 7 < 5) {
-      const int x = (kk - 2) / 7, ph = (kk - 2) % 7;
-      if (ph == 0) v = widen_bf16_load<WIDEN_BUF>(tid, x);
-      if (ph == 4) widen_bf16_store<WIDEN_BUF>(tid, x, v);
-    }
   }
   __device__ __forceinline__ void value_step(int n) {
-    const int x = 5 + n / 8, ph = n % 8;
-    if (x < 9) {
-      if (ph == 0) v = widen_bf16_load<WIDEN_BUF>(tid, x);
-      if (ph == 4) widen_bf16_store<WIDEN_BUF>(tid, x, v);
-    }
+    if (n >= 3 && n % 3 == 0 && n / 3 <= 9) widen_bf16_store<WIDEN_BUF>(tid, n / 3 - 1, v);
+    if (n % 3 == 0 && n / 3 < 9) v = widen_bf16_load<WIDEN_BUF>(tid, n / 3);
   }
+};
+
+struct NoHide {
+  __device__ __forceinline__ void score_step(int) {}
+  __device__ __forceinline__ void value_step(int) {}
 };
 
 // fp8 latents: the 6 direct loads of raw tile i+3 (one every sixth score
@@ -469,6 +516,64 @@ struct HideFp8 {
   }
 };
 
+// Value products of one tile (fp16 buffer B), after the P exchange:
+// O^T += C^T P^T over this wave's 128 latent columns, all heads, with the
+// rescale of the accumulators first when any head's running max moved.
+template <bool FP8, int B, class Hide>
+__device__ __forceinline__ void pv_phase(WaveState &st, Hide &hide, bool fresh, const f16x8 *fa0 = nullptr) {
+  using namespace sk;
+  using M = Map<FP8>;
+  // k-step kb, column block j, head block hb. The P fragments of the
+  // second k-step are read during the second half of the first, its value
+  // fragments two to six products ahead of their first use. The value
+  // fragments of the first k-step may come preloaded (fa0: they depend on
+  // the tile only, not on the P exchange).
+  const ValueBase vb = value_base<FP8, B>(st.lane, st.w);
+  f16x8 fa[2][4], fb[2][4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) fb[0][hb] = p_frag(vb, hb, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fa[0][j] = fa0 ? fa0[j] : value_frag<FP8, B>(vb, j, 0);
+  float al[4];
+  const int hl = opaque(st.lane) & 31;
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) al[hb] = reinterpret_cast<const float *>(g_lds + M::alpha())[32 * hb + hl];
+  // (an item's first tile needs none: the accumulators are still zero)
+  if (!fresh && __any(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
+    // one 16-register block at a time through VGPRs, back into AGPRs (the
+    // bf16 path's VGPR block stays there)
+#pragma unroll
+    for (int x = 0; x < DC / 32; ++x) {
+      f32x16 t = st.O[x];
+      asm volatile("" : "+v"(t));
+      t *= al[x & 3];
+      st.O[x] = t;
+      if (!FP8 && x == VBLK) asm volatile("" : "+v"(st.O[x]));
+      else asm volatile("" : "+a"(st.O[x]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      const int j = idx >> 2, hb = idx & 3;
+      if (kb == 0 && idx >= 8 && idx < 12) fb[1][idx - 8] = p_frag(vb, idx - 8, 1);
+      if ((kb == 0 && (idx == 12 || idx == 14)) || (kb == 1 && (idx == 2 || idx == 6))) {
+        const int jn = kb == 0 ? (idx - 12) / 2 : 2 + (idx - 2) / 4;
+        fa[1][jn] = value_frag<FP8, B>(vb, jn, 1);
+      }
+      if (FP8) st.O[4 * j + hb] = mfma32(fa[kb][j], fb[kb][hb], st.O[4 * j + hb]);
+      else if (4 * j + hb == VBLK) mfma_acc_v(st.O[4 * j + hb], fa[kb][j], fb[kb][hb]);
+      else mfma_acc_a(st.O[4 * j + hb], fa[kb][j], fb[kb][hb]);
+      hide.value_step(16 * kb + idx);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+
 // One tile (fp16 buffer B): both contractions are software-pipelined by hand
 // (fragment reads run ahead of the matrix-core op that consumes them) and
 // each step is fenced with a scheduling barrier, so the compiler keeps the
@@ -476,10 +581,11 @@ struct HideFp8 {
 // hidden work of the step sits after each product, where it runs while the
 // matrix core is busy.
 template <bool FP8, int B, class Hide>
-__device__ __forceinline__ void compute_tile(WaveState &st, int valid, Hide &hide) {
+__device__ __forceinline__ void compute_tile(WaveState &st, int valid, bool fresh, Hide &hide) {
   using namespace sk;
   using M = Map<FP8>;
-  const int half = st.half;
+  const int half = opaque(st.lane) >> 5;
+  const ScoreBase sb = score_base<FP8, B>(st.lane);
   const float *tscl = reinterpret_cast<const float *>(g_lds + M::sclbf(B));
   // ---- S^T = K Q^T. bf16: one chain over all 36 k-steps (back-to-back
   // accumulation into the same registers runs at the full matrix-core rate).
@@ -489,10 +595,10 @@ __device__ __forceinline__ void compute_tile(WaveState &st, int valid, Hide &hid
   {
     f16x8 af[SPF + 1];
 #pragma unroll
-    for (int j = 0; j < SPF; ++j) af[j] = score_frag<FP8, B>(st, j);
+    for (int j = 0; j < SPF; ++j) af[j] = score_frag<FP8, B>(sb, j);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      if (kk + SPF < D / 16) af[(kk + SPF) % (SPF + 1)] = score_frag<FP8, B>(st, kk + SPF);
+      if (kk + SPF < D / 16) af[(kk + SPF) % (SPF + 1)] = score_frag<FP8, B>(sb, kk + SPF);
       const f16x8 a = af[kk % (SPF + 1)];
       if (FP8) {
         if (kk < DC / 16) {
@@ -542,62 +648,131 @@ __device__ __forceinline__ void compute_tile(WaveState &st, int valid, Hide &hid
   st.l = fmaf(st.l, alpha, pair_sum(psum));
   st.m = m_new;
   // ---- hand P and alpha of this wave's heads to every wave
-  char *px = g_lds + M::px() + 16 * st.lane + 2048 * st.w;
+  const int ln = opaque(st.lane);
+  char *px = g_lds + M::px() + 16 * ln + 2048 * st.w;
   *reinterpret_cast<f16x8 *>(px) = P[0];
   *reinterpret_cast<f16x8 *>(px + 1024) = P[1];
-  if (half == 0) reinterpret_cast<float *>(g_lds + M::alpha())[32 * st.w + st.hl] = alpha;
+  if (half == 0) reinterpret_cast<float *>(g_lds + M::alpha())[32 * st.w + (ln & 31)] = alpha;
   wait_lds();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  // ---- O^T += C^T P^T over this wave's 128 latent columns, all heads:
-  // k-step kb, column block j, head block hb. The fragments of the next
-  // k-step are read during the second half of the current one.
-  f16x8 fa[2][4], fb[2][4];
-#pragma unroll
-  for (int hb = 0; hb < 4; ++hb) fb[0][hb] = p_frag<FP8>(st, hb, 0);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) fa[0][j] = value_frag<FP8, B>(st, j, 0);
-  float al[4];
-#pragma unroll
-  for (int hb = 0; hb < 4; ++hb) al[hb] = reinterpret_cast<const float *>(g_lds + M::alpha())[32 * hb + st.hl];
-  if (__any(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
-    // one 16-register block at a time through VGPRs, back into AGPRs
-#pragma unroll
-    for (int x = 0; x < DC / 32; ++x) {
-      f32x16 t = st.O[x];
-      asm volatile("" : "+v"(t));
-      t *= al[x & 3];
-      st.O[x] = t;
-      asm volatile("" : "+a"(st.O[x]));
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  pv_phase<FP8, B>(st, hide, fresh);
+}
+
+// Online softmax of one tile's scores (this lane's head: 16 tokens here, 16
+// in lane ^ 32), cut into pieces that run between the score products of the
+// next tile: piece kk runs after product kk. The wave issues in order, so a
+// piece never waits on a result produced in the same piece (a stalled vector
+// op would hold back the next matrix-core op): the cross-lane exchanges and
+// each exp2 are consumed one piece later. Scores are in log2 units; exp2 of
+// a value below -126 may flush to zero, below the fp16 resolution of P.
+//   0..3   partial maxima of 4 rows each
+//   4      max of this lane's 16 rows, exchange with lane ^ 32
+//   5      row max mx
+//   6      new running max (kept unless exceeded by SLACK), alpha
+//   7..22  p_r = exp2(s_r - m) for r = kk - 7; p_{r-1} summed and packed;
+//          P rows 0..7 go to LDS at 15, rows 8..15 at 23
+//   23     last p summed and packed, P rows 8..15 out, sum exchange
+//   24     l = alpha l + sum, m updated, alpha out
+struct Softmax {
+  float m4[4], mx, m_new, alpha, psum, pe, prev;
+  uint32_t xs[2];
+  uint32_t P[4];  // fp16 pairs of P, 8 rows at a time
+};
+__device__ __forceinline__ void softmax_consume(WaveState &st, Softmax &sm, int r) {
+  // p_r (in sm.prev) into the sum and the packed rows
+  sm.psum += sm.prev;
+  if (r % 2 == 0) {
+    sm.pe = sm.prev;
+  } else {
+    f16x2 h;
+    h[0] = static_cast<_Float16>(sm.pe);
+    h[1] = static_cast<_Float16>(sm.prev);
+    sm.P[(r >> 1) & 3] = __builtin_bit_cast(uint32_t, h);
   }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      const int j = idx >> 2, hb = idx & 3;
-      if (kb == 0 && idx >= 8) {
-        if (idx < 12) fb[1][idx - 8] = p_frag<FP8>(st, idx - 8, 1);
-        else fa[1][idx - 12] = value_frag<FP8, B>(st, idx - 12, 1);
-      }
-      st.O[4 * j + hb] = mfma32(fa[kb][j], fb[kb][hb], st.O[4 * j + hb]);
-      hide.value_step(16 * kb + idx);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  if (r % 8 == 7) {
+    // hand these 8 rows of P (rows 8 (r / 8) ..) to every wave
+    char *px = g_lds + sk::Map<false>::px() + 16 * opaque(st.lane) + 2048 * st.w + 1024 * (r >> 3);
+    *reinterpret_cast<u32x4 *>(px) = u32x4{sm.P[0], sm.P[1], sm.P[2], sm.P[3]};
+  }
+}
+__device__ __forceinline__ void softmax_piece(WaveState &st, Softmax &sm, const f32x16 &S, int kk) {
+  using namespace sk;
+  if (kk < 4) {
+    sm.m4[kk] = fmaxf(fmaxf(S[4 * kk], S[4 * kk + 1]), fmaxf(S[4 * kk + 2], S[4 * kk + 3]));
+  } else if (kk == 4) {
+    const float t = fmaxf(fmaxf(sm.m4[0], sm.m4[1]), fmaxf(sm.m4[2], sm.m4[3]));
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    sm.xs[0] = r[0];
+    sm.xs[1] = r[1];
+  } else if (kk == 5) {
+    sm.mx = fmaxf(__uint_as_float(sm.xs[0]), __uint_as_float(sm.xs[1]));
+  } else if (kk == 6) {
+    sm.m_new = sm.mx > st.m + SLACK ? sm.mx : st.m;
+    sm.alpha = __builtin_amdgcn_exp2f(st.m - sm.m_new);
+    sm.psum = 0.0f;
+  } else if (kk < 23) {
+    const int r = kk - 7;
+    const float p = __builtin_amdgcn_exp2f(S[r] - sm.m_new);
+    if (r > 0) softmax_consume(st, sm, r - 1);
+    sm.prev = p;
+  } else if (kk == 23) {
+    softmax_consume(st, sm, 15);
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm.psum), __float_as_uint(sm.psum), false, false);
+    sm.xs[0] = r[0];
+    sm.xs[1] = r[1];
+  } else if (kk == 24) {
+    st.l = fmaf(st.l, sm.alpha, __uint_as_float(sm.xs[0]) + __uint_as_float(sm.xs[1]));
+    st.m = sm.m_new;
+    const int ln = opaque(st.lane);
+    if (ln < 32) reinterpret_cast<float *>(g_lds + Map<false>::alpha())[32 * st.w + ln] = sm.alpha;
   }
 }
 
-// One pipeline step for bf16 latents (B = i % 4). After the barrier every
-// wave's copies of tile i+1 have landed and tile i is widened; the step
-// computes tile i while widening tile i+1 in place and fetching tile i+3
-// into the buffer tile i-1 used.
+// Score products of one bf16-path tile (fp16 buffer B): one chain over the
+// 36 k-steps, accumulating in AGPRs (S), with the softmax of the previous
+// tile's scores (Sv, a VGPR copy) woven in when SOFTMAX is set. An AGPR-form
+// chain leaves the VGPR file's ports to the vector ALU, and the compiler's
+// own hazard handling needs no blanket wait before each product, so the
+// softmax's vector work runs in the products' shadow (with a VGPR-form
+// chain, or an s_nop before each product, it mostly serialises).
+template <int B, bool SOFTMAX, class Hide>
+__device__ __forceinline__ void score_chain_bf16(WaveState &st, f32x16 &S, const f32x16 &Sv, Hide &hide) {
+  using namespace sk;
+  Softmax sm;
+  const ScoreBase sb = score_base<false, B>(st.lane);
+  f16x8 af[SPF + 1];
+#pragma unroll
+  for (int j = 0; j < SPF; ++j) af[j] = score_frag<false, B>(sb, j);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    if (kk + SPF < D / 16) af[(kk + SPF) % (SPF + 1)] = score_frag<false, B>(sb, kk + SPF);
+    const f16x8 a = af[kk % (SPF + 1)];
+    S = mfma32(a, st.qf[kk], kk == 0 ? f32x16{} : S);
+    asm volatile("" : "+a"(S));
+    hide.score_step(kk);
+    if (SOFTMAX) softmax_piece(st, sm, Sv, kk);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One pipeline step for bf16 latents (B = i % 4), software-pipelined by one
+// tile. On entry tile i+1 is widened and visible and S (AGPRs) holds tile
+// i's scores; they are copied to VGPRs first. The step
+//   1. runs the score products of tile i+1 (buffer B+1) into S, with the
+//      softmax of tile i woven in and the copies of tile i+3 (into buffer
+//      B+3, which tile i-1 used) issued under them;
+//   2. waits for its own copies of tile i+2 and the P exchange, barrier;
+//   3. runs the value products of tile i (buffer B) with the widening of
+//      tile i+2 (buffer B+2) woven in;
+//   4. barrier: tile i+2 is ready for the next step's scores and buffer B is
+//      free for the next step's copies.
+// In an item's last step the scores of the tile past its end are computed
+// on the finite rows that buffer holds and dropped.
 template <int B>
-__device__ __forceinline__ void step_bf16(WaveState &st, const Item &it, int i, int w, int lane, int tid) {
-  wait_vm_lds<9>();  // every step issues 9 copies; the previous step's may still fly
-  __builtin_amdgcn_s_barrier();
-  HideBf16<(B + 3) % 4, (B + 1) % 4> h;
+__device__ __forceinline__ void step_bf16(WaveState &st, f32x16 &S, const Item &it, int i, int w, int lane,
+                                          int tid) {
+  HideBf16<(B + 3) % 4, (B + 2) % 4> h;
   const TileSrc src = tile_src(it, i + 3);
   h.stride = src.stride;
   h.lim = src.tmax - 8 * w;
@@ -610,7 +785,34 @@ __device__ __forceinline__ void step_bf16(WaveState &st, const Item &it, int i, 
   h.w = w;
   h.lane = lane;
   h.tid = opaque(tid);
-  compute_tile<false, B>(st, min(sk::T, it.t1 - (it.t0 + i * sk::T)), h);
+  f32x16 Sv = S;
+  asm volatile("" : "+v"(Sv));
+  const int valid = min(sk::T, it.t1 - (it.t0 + i * sk::T));
+  if (valid < sk::T) {  // the item's last tile only (a real branch: the asm cannot be speculated)
+    asm volatile("; tail mask");
+    const int lim = valid - 4 * (opaque(st.lane) >> 5);  // one register, not 16 hoisted row indices
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + (r & 3) >= lim) Sv[r] = -INFINITY;
+  }
+  score_chain_bf16<(B + 1) % 4, true>(st, S, Sv, h);
+  // the first value fragments of tile i need no P: read them before the
+  // barrier; wait for everything but those 8 reads (P is written) and for
+  // tile i+2's copies (this step's 9 may still fly)
+  f16x8 fa0[4];
+  {
+    const ValueBase vb = value_base<false, B>(st.lane, st.w);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fa0[j] = value_frag<false, B>(vb, j, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the 8 reads stay ahead of the count below
+  __builtin_amdgcn_s_waitcnt((9 & 15) | (7 << 4) | (8 << 8) | ((9 >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  pv_phase<false, B>(st, h, i == 0, fa0);
+  wait_lds();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // One pipeline step for fp8 latents (B3 = i % 3, B2 = i % 2): computes tile
@@ -629,7 +831,7 @@ __device__ __forceinline__ void step_fp8(WaveState &st, const Item &it, int i, i
   h.tid = opaque(tid);
   h.dma_on = i + 3 < it.ntiles;
   h.widen_on = i + 1 < it.ntiles;
-  compute_tile<true, B2>(st, min(sk::T, it.t1 - (it.t0 + i * sk::T)), h);
+  compute_tile<true, B2>(st, min(sk::T, it.t1 - (it.t0 + i * sk::T)), i == 0, h);
 }
 
 template <bool FP8>
@@ -682,8 +884,6 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
   }
 
   WaveState st;
-  st.half = half;
-  st.hl = hl;
   st.w = w;
   st.lane = lane;
   {
@@ -694,29 +894,14 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
 #pragma unroll
   for (int db = 0; db < DC / 32; ++db) {
     st.O[db] = f32x16{};
-    asm volatile("" : "+a"(st.O[db]));
+    if (!FP8 && db == VBLK) asm volatile("" : "+v"(st.O[db]));
+    else asm volatile("" : "+a"(st.O[db]));
   }
   st.m = -INFINITY;
   st.l = 0.0f;
-  // score A fragment kk: token hl, 16-byte chunk 2 kk + half of the latent
-  // row, or chunk 2 (kk - 32) + half of the k_rope row (swizzled)
-  st.sl = LROW * hl + 16 * half;
-  st.sl2 = st.sl + M::lat(2);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) st.sr[j] = M::rope(0) + 128 * hl + 16 * ((2 * j + half) ^ rsw(hl));
-  // value A fragment (transposed read): 16-lane group g, lane j in it points at
-  // token 16 kb + 8 h + tt (tt = 4 (g/2) + j/4), latent column 128 w + 32 jb + dd
-  // (dd = 16 (g%2) + 4 (j%4))
-  {
-    const int g = (lane >> 4) & 3, j = lane & 15;
-    const int tt = 4 * (g >> 1) + (j >> 2);
-    const int dd = 16 * (g & 1) + 4 * (j & 3);
-    st.vl = LROW * tt + 2 * (128 * w + dd);
-    st.vl2 = st.vl + M::lat(2);
-  }
 
-  // widen tile 0 before the loop; each step then widens one tile ahead
   if (FP8) {
+    // widen tile 0 before the loop; each step then widens one tile ahead
     constexpr int PER = RAW_DMA_PER_WAVE + 1;
     if (it.ntiles > 2) wait_vm<2 * PER>(); else if (it.ntiles > 1) wait_vm<PER>(); else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
@@ -730,18 +915,37 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
       if (i + 5 < it.ntiles) step_fp8<2, 1>(st, it, i + 5, w, lane, tid);
     }
   } else {
-    wait_vm<18>();
+    // tiles 0 and 1 landed (only Q's loads, issued last, may still fly) and
+    // widened; then the scores of tile 0 alone
+    wait_vm<9>();
     __builtin_amdgcn_s_barrier();
     widen_bf16_inplace<0>(tid);
+    widen_bf16_inplace<1>(tid);
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    f32x16 S;
+    {
+      NoHide nh;
+      score_chain_bf16<0, false>(st, S, S, nh);
+    }
     for (int i = 0; i < it.ntiles; i += 4) {
-      step_bf16<0>(st, it, i, w, lane, tid);
-      if (i + 1 < it.ntiles) step_bf16<1>(st, it, i + 1, w, lane, tid);
-      if (i + 2 < it.ntiles) step_bf16<2>(st, it, i + 2, w, lane, tid);
-      if (i + 3 < it.ntiles) step_bf16<3>(st, it, i + 3, w, lane, tid);
+      step_bf16<0>(st, S, it, i, w, lane, tid);
+      if (i + 1 < it.ntiles) step_bf16<1>(st, S, it, i + 1, w, lane, tid);
+      if (i + 2 < it.ntiles) step_bf16<2>(st, S, it, i + 2, w, lane, tid);
+      if (i + 3 < it.ntiles) step_bf16<3>(st, S, it, i + 3, w, lane, tid);
     }
   }
 
   wait_vm<0>();  // no copy may still be landing in LDS when the workgroup ends
+  if (!FP8) {
+    // the value products are asm on the bf16 path: cover their result
+    // latency before the vector ALU reads the accumulators
+#pragma unroll
+    for (int x = 0; x < DC / 32; ++x) {
+      if (x == VBLK) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(st.O[x]));
+      else asm volatile("" : "+a"(st.O[x]));
+    }
+  }
   // ---- normalised partials and log-sum-exp (base 2): each wave writes its
   // 128 latent columns of all 128 heads, dividing by the denominators the
   // scoring waves hand over
