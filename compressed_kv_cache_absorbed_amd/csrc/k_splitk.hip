@@ -294,14 +294,16 @@ __device__ __forceinline__ void dma_raw(const Item &it, int tile, int w, int lan
   for (int x = 0; x <= sk::RAW_DMA_PER_WAVE; ++x) dma_raw_piece<R>(src, w, lane, x);
 }
 
-// Widening a bf16 tile to fp16 in place, 9 chunks of 16 bytes per thread:
-// x < 8: latent token (tid / 64) + 4 x, bytes 16 (tid % 64) ..; x = 8: k_rope
-// chunk tid. Split into load and convert-store so the two can be spread over
-// a matrix-core loop.
+// Widening a bf16 tile to fp16 in place, 9 chunks of 16 bytes per thread,
+// exactly the bytes the thread's wave copied (dma_bf16_piece), so a wave
+// needs to wait for its own copies only: x < 8: latent token 8 w + x, bytes
+// 16 lane ..; x = 8: chunk tid of the k_rope region (wave w's 1 KB). Split
+// into load and convert-store so the two can be spread over a matrix-core
+// loop.
 template <int B>
 __device__ __forceinline__ char *widen_bf16_addr(int tid, int x) {
   using M = sk::Map<false>;
-  return x < 8 ? g_lds + M::lat(B) + sk::LROW * ((tid >> 6) + 4 * x) + 16 * (tid & 63)
+  return x < 8 ? g_lds + M::lat(B) + sk::LROW * (8 * (tid >> 6) + x) + 16 * (tid & 63)
                : g_lds + M::rope(B) + 16 * tid;
 }
 template <int B>
@@ -520,36 +522,32 @@ struct HideFp8 {
 // O^T += C^T P^T over this wave's 128 latent columns, all heads, with the
 // rescale of the accumulators first when any head's running max moved.
 template <bool FP8, int B, class Hide>
-__device__ __forceinline__ void pv_phase(WaveState &st, Hide &hide, bool fresh, const f16x8 *fa0 = nullptr) {
+__device__ __forceinline__ void pv_phase(WaveState &st, Hide &hide, bool fresh) {
   using namespace sk;
   using M = Map<FP8>;
   // k-step kb, column block j, head block hb. The P fragments of the
   // second k-step are read during the second half of the first, its value
-  // fragments two to six products ahead of their first use. The value
-  // fragments of the first k-step may come preloaded (fa0: they depend on
-  // the tile only, not on the P exchange).
+  // fragments two to six products ahead of their first use.
   const ValueBase vb = value_base<FP8, B>(st.lane, st.w);
   f16x8 fa[2][4], fb[2][4];
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) fb[0][hb] = p_frag(vb, hb, 0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fa[0][j] = fa0 ? fa0[j] : value_frag<FP8, B>(vb, j, 0);
+  for (int j = 0; j < 4; ++j) fa[0][j] = value_frag<FP8, B>(vb, j, 0);
   float al[4];
   const int hl = opaque(st.lane) & 31;
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) al[hb] = reinterpret_cast<const float *>(g_lds + M::alpha())[32 * hb + hl];
   // (an item's first tile needs none: the accumulators are still zero)
   if (!fresh && __any(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
-    // one 16-register block at a time through VGPRs, back into AGPRs (the
-    // bf16 path's VGPR block stays there)
+    // one 16-register block at a time through VGPRs, back into AGPRs
 #pragma unroll
     for (int x = 0; x < DC / 32; ++x) {
       f32x16 t = st.O[x];
       asm volatile("" : "+v"(t));
       t *= al[x & 3];
       st.O[x] = t;
-      if (!FP8 && x == VBLK) asm volatile("" : "+v"(st.O[x]));
-      else asm volatile("" : "+a"(st.O[x]));
+      asm volatile("" : "+a"(st.O[x]));
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -564,9 +562,7 @@ __device__ __forceinline__ void pv_phase(WaveState &st, Hide &hide, bool fresh, 
         const int jn = kb == 0 ? (idx - 12) / 2 : 2 + (idx - 2) / 4;
         fa[1][jn] = value_frag<FP8, B>(vb, jn, 1);
       }
-      if (FP8) st.O[4 * j + hb] = mfma32(fa[kb][j], fb[kb][hb], st.O[4 * j + hb]);
-      else if (4 * j + hb == VBLK) mfma_acc_v(st.O[4 * j + hb], fa[kb][j], fb[kb][hb]);
-      else mfma_acc_a(st.O[4 * j + hb], fa[kb][j], fb[kb][hb]);
+      st.O[4 * j + hb] = mfma32(fa[kb][j], fb[kb][hb], st.O[4 * j + hb]);
       hide.value_step(16 * kb + idx);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -670,16 +666,17 @@ __device__ __forceinline__ void compute_tile(WaveState &st, int valid, bool fres
 //   4      max of this lane's 16 rows, exchange with lane ^ 32
 //   5      row max mx
 //   6      new running max (kept unless exceeded by SLACK), alpha
-//   7..22  p_r = exp2(s_r - m) for r = kk - 7; p_{r-1} summed and packed;
-//          P rows 0..7 go to LDS at 15, rows 8..15 at 23
-//   23     last p summed and packed, P rows 8..15 out, sum exchange
-//   24     l = alpha l + sum, m updated, alpha out
+//   7..22  p_r = exp2(s_r - m) for r = kk - 7; p_{r-1} summed and packed
+//   23     last p summed and packed, sum exchange
+//   24     l = alpha l + sum, m updated
+// P stays in registers (fp16 pairs, rows 2 j and 2 j + 1 in P[j]) for the
+// value products of the same wave.
 struct Softmax {
   float m4[4], mx, m_new, alpha, psum, pe, prev;
   uint32_t xs[2];
-  uint32_t P[4];  // fp16 pairs of P, 8 rows at a time
+  uint32_t P[8];
 };
-__device__ __forceinline__ void softmax_consume(WaveState &st, Softmax &sm, int r) {
+__device__ __forceinline__ void softmax_consume(Softmax &sm, int r) {
   // p_r (in sm.prev) into the sum and the packed rows
   sm.psum += sm.prev;
   if (r % 2 == 0) {
@@ -688,12 +685,7 @@ __device__ __forceinline__ void softmax_consume(WaveState &st, Softmax &sm, int 
     f16x2 h;
     h[0] = static_cast<_Float16>(sm.pe);
     h[1] = static_cast<_Float16>(sm.prev);
-    sm.P[(r >> 1) & 3] = __builtin_bit_cast(uint32_t, h);
-  }
-  if (r % 8 == 7) {
-    // hand these 8 rows of P (rows 8 (r / 8) ..) to every wave
-    char *px = g_lds + sk::Map<false>::px() + 16 * opaque(st.lane) + 2048 * st.w + 1024 * (r >> 3);
-    *reinterpret_cast<u32x4 *>(px) = u32x4{sm.P[0], sm.P[1], sm.P[2], sm.P[3]};
+    sm.P[r >> 1] = __builtin_bit_cast(uint32_t, h);
   }
 }
 __device__ __forceinline__ void softmax_piece(WaveState &st, Softmax &sm, const f32x16 &S, int kk) {
@@ -714,18 +706,16 @@ __device__ __forceinline__ void softmax_piece(WaveState &st, Softmax &sm, const 
   } else if (kk < 23) {
     const int r = kk - 7;
     const float p = __builtin_amdgcn_exp2f(S[r] - sm.m_new);
-    if (r > 0) softmax_consume(st, sm, r - 1);
+    if (r > 0) softmax_consume(sm, r - 1);
     sm.prev = p;
   } else if (kk == 23) {
-    softmax_consume(st, sm, 15);
+    softmax_consume(sm, 15);
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm.psum), __float_as_uint(sm.psum), false, false);
     sm.xs[0] = r[0];
     sm.xs[1] = r[1];
   } else if (kk == 24) {
     st.l = fmaf(st.l, sm.alpha, __uint_as_float(sm.xs[0]) + __uint_as_float(sm.xs[1]));
     st.m = sm.m_new;
-    const int ln = opaque(st.lane);
-    if (ln < 32) reinterpret_cast<float *>(g_lds + Map<false>::alpha())[32 * st.w + ln] = sm.alpha;
   }
 }
 
@@ -737,9 +727,9 @@ __device__ __forceinline__ void softmax_piece(WaveState &st, Softmax &sm, const 
 // softmax's vector work runs in the products' shadow (with a VGPR-form
 // chain, or an s_nop before each product, it mostly serialises).
 template <int B, bool SOFTMAX, class Hide>
-__device__ __forceinline__ void score_chain_bf16(WaveState &st, f32x16 &S, const f32x16 &Sv, Hide &hide) {
+__device__ __forceinline__ void score_chain_bf16(WaveState &st, f32x16 &S, const f32x16 &Sv, Softmax &sm,
+                                                 Hide &hide) {
   using namespace sk;
-  Softmax sm;
   const ScoreBase sb = score_base<false, B>(st.lane);
   f16x8 af[SPF + 1];
 #pragma unroll
@@ -756,15 +746,93 @@ __device__ __forceinline__ void score_chain_bf16(WaveState &st, f32x16 &S, const
   }
 }
 
+// Value A fragment of the bf16 path (transposed read): 16-lane group g,
+// lane j in it points at token 16 kb + 8 h + tt (tt = 4 (g/2) + j/4), latent
+// column 32 cb + dd (dd = 16 (g%2) + 4 (j%4)); the base includes the offset
+// of buffers 2 and 3, beyond the 16-bit range of LDS read offsets.
+template <int B>
+__device__ __forceinline__ int row_value_base(int lane_) {
+  using M = sk::Map<false>;
+  const int ln = opaque(lane_);
+  const int g = (ln >> 4) & 3, j = ln & 15;
+  const int tt = 4 * (g >> 1) + (j >> 2);
+  const int dd = 16 * (g & 1) + 4 * (j & 3);
+  return sk::LROW * tt + 2 * dd + (B < 2 ? 0 : M::lat(2));
+}
+template <int B>
+__device__ __forceinline__ f16x8 row_value_frag(int vl, int cb, int kb) {
+  using M = sk::Map<false>;
+  const char *p0 = g_lds + vl + (B < 2 ? M::lat(B) : M::lat(B) - M::lat(2)) + sk::LROW * 16 * kb + 64 * cb;
+  const char *p1 = p0 + sk::LROW * 8;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(p1));
+  f16x8 a;
+  a.lo = __builtin_bit_cast(f16x4, lo);
+  a.hi = __builtin_bit_cast(f16x4, hi);
+  return a;
+}
+
+// Value products of one bf16-path tile (buffer B) for this wave's heads:
+// O^T [512 x 32 heads] += C^T [512 x 32 tok] P^T [32 tok x 32 heads], 16
+// column blocks x 2 k-steps, value fragments read VPF products ahead. P is
+// the wave's own, used in place: in k-step kb, element e of lane l stands
+// for token 16 kb + 8 (e / 4) + 4 (l / 32) + e % 4 in both operands (the
+// rows the softmax left in the lane, and the tokens the transposed value
+// reads fetch), an order of the 16 tokens the contraction does not see.
+// Every accumulator value of a lane belongs to the lane's head, so the
+// rescale is a per-lane factor.
+constexpr int VPF = 4;
+template <int B, class Hide>
+__device__ __forceinline__ void pv_rows(WaveState &st, const Softmax &sm, Hide &hide, bool fresh) {
+  using namespace sk;
+  const int vl = row_value_base<B>(st.lane);
+  f16x8 va[VPF + 1];
+#pragma unroll
+  for (int n = 0; n < VPF; ++n) va[n] = row_value_frag<B>(vl, n & 15, n >> 4);
+  f16x8 pb[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+    pb[kb] = __builtin_bit_cast(f16x8, u32x4{sm.P[4 * kb], sm.P[4 * kb + 1], sm.P[4 * kb + 2], sm.P[4 * kb + 3]});
+  // wait states between the vector-ALU writes of P and the asm products
+  // reading it
+  asm volatile("s_nop 4" : "+v"(pb[0]), "+v"(pb[1]));
+  // (an item's first tile needs none: the accumulators are still zero)
+  if (!fresh && __any(sm.alpha != 1.0f)) {
+    // one 16-register block at a time through VGPRs, back into AGPRs (the
+    // VGPR block stays there)
+#pragma unroll
+    for (int x = 0; x < DC / 32; ++x) {
+      f32x16 t = st.O[x];
+      asm volatile("" : "+v"(t));
+      t *= sm.alpha;
+      st.O[x] = t;
+      if (x == VBLK) asm volatile("" : "+v"(st.O[x]));
+      else asm volatile("" : "+a"(st.O[x]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int n = 0; n < 2 * (DC / 32); ++n) {
+    const int kb = n >> 4, cb = n & 15;
+    if (n + VPF < 2 * (DC / 32)) va[(n + VPF) % (VPF + 1)] = row_value_frag<B>(vl, (n + VPF) & 15, (n + VPF) >> 4);
+    if (cb == VBLK) mfma_acc_v(st.O[cb], va[n % (VPF + 1)], pb[kb]);
+    else mfma_acc_a(st.O[cb], va[n % (VPF + 1)], pb[kb]);
+    hide.value_step(n);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // One pipeline step for bf16 latents (B = i % 4), software-pipelined by one
 // tile. On entry tile i+1 is widened and visible and S (AGPRs) holds tile
 // i's scores; they are copied to VGPRs first. The step
 //   1. runs the score products of tile i+1 (buffer B+1) into S, with the
 //      softmax of tile i woven in and the copies of tile i+3 (into buffer
 //      B+3, which tile i-1 used) issued under them;
-//   2. waits for its own copies of tile i+2 and the P exchange, barrier;
-//   3. runs the value products of tile i (buffer B) with the widening of
-//      tile i+2 (buffer B+2) woven in;
+//   2. waits for its own copies of tile i+2 (no other wave's: each wave
+//      widens the rows it copied);
+//   3. runs the value products of tile i (buffer B) with the widening of its
+//      rows of tile i+2 (buffer B+2) woven in;
 //   4. barrier: tile i+2 is ready for the next step's scores and buffer B is
 //      free for the next step's copies.
 // In an item's last step the scores of the tile past its end are computed
@@ -795,21 +863,11 @@ __device__ __forceinline__ void step_bf16(WaveState &st, f32x16 &S, const Item &
     for (int r = 0; r < 16; ++r)
       if (8 * (r >> 2) + (r & 3) >= lim) Sv[r] = -INFINITY;
   }
-  score_chain_bf16<(B + 1) % 4, true>(st, S, Sv, h);
-  // the first value fragments of tile i need no P: read them before the
-  // barrier; wait for everything but those 8 reads (P is written) and for
-  // tile i+2's copies (this step's 9 may still fly)
-  f16x8 fa0[4];
-  {
-    const ValueBase vb = value_base<false, B>(st.lane, st.w);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fa0[j] = value_frag<false, B>(vb, j, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);  // the 8 reads stay ahead of the count below
-  __builtin_amdgcn_s_waitcnt((9 & 15) | (7 << 4) | (8 << 8) | ((9 >> 4) << 14));
-  __builtin_amdgcn_s_barrier();
+  Softmax sm;
+  score_chain_bf16<(B + 1) % 4, true>(st, S, Sv, sm, h);
+  wait_vm<9>();  // this wave's copies of tile i+2 landed (this step's 9 may still fly)
   __builtin_amdgcn_sched_barrier(0);
-  pv_phase<false, B>(st, h, i == 0, fa0);
+  pv_rows<B>(st, sm, h, i == 0);
   wait_lds();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -915,10 +973,10 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
       if (i + 5 < it.ntiles) step_fp8<2, 1>(st, it, i + 5, w, lane, tid);
     }
   } else {
-    // tiles 0 and 1 landed (only Q's loads, issued last, may still fly) and
-    // widened; then the scores of tile 0 alone
+    // this wave's rows of tiles 0 and 1 landed (only Q's loads, issued
+    // last, may still fly) and widened; then the scores of tile 0 alone
     wait_vm<9>();
-    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     widen_bf16_inplace<0>(tid);
     widen_bf16_inplace<1>(tid);
     wait_lds();
@@ -926,7 +984,8 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
     f32x16 S;
     {
       NoHide nh;
-      score_chain_bf16<0, false>(st, S, S, nh);
+      Softmax sm;
+      score_chain_bf16<0, false>(st, S, S, sm, nh);
     }
     for (int i = 0; i < it.ntiles; i += 4) {
       step_bf16<0>(st, S, it, i, w, lane, tid);
@@ -945,10 +1004,26 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
       if (x == VBLK) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(st.O[x]));
       else asm volatile("" : "+a"(st.O[x]));
     }
+    // ---- normalised partials and log-sum-exp (base 2) of this wave's
+    // heads: register group g4 of column block cb is one 512-byte run of
+    // head block w
+    const float inv = 1.0f / st.l;
+    if (half == 0) lse[static_cast<size_t>(k) * H + head] = st.m + log2f(st.l);
+#pragma unroll
+    for (int cb = 0; cb < DC / 32; ++cb) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(st.O[cb][4 * g4 + e] * inv);
+        *reinterpret_cast<f16x4 *>(ob + ((w * 16 + cb) * 4 + g4) * 256 + 4 * lane) = v;
+      }
+    }
+    return;
   }
-  // ---- normalised partials and log-sum-exp (base 2): each wave writes its
-  // 128 latent columns of all 128 heads, dividing by the denominators the
-  // scoring waves hand over
+  // ---- normalised partials and log-sum-exp (base 2), fp8 path: each wave
+  // writes its 128 latent columns of all 128 heads, dividing by the
+  // denominators the scoring waves hand over
   float *gstat = reinterpret_cast<float *>(g_lds + M::stat());
   if (half == 0) {
     gstat[32 * w + hl] = st.l;
