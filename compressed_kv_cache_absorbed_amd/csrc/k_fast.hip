@@ -172,53 +172,91 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qs
 // Grid (batch, H/32, d_c/32), 256 threads: sequence b, head block hb,
 // latent block db (32 columns). Log-sum-exp merge of the sequence's split
 // partials (base 2): o^ = sum_s 2^(lse_s - M) o^_s / sum_s 2^(lse_s - M).
-// In the fragment order of the (fp16) partials the (hb, db) block is 2 KB
-// contiguous per split; thread (g = tid / 64, lane) owns the four values at
-// 256 g + 4 lane of it (head hl = lane % 32, columns 8 g + 4 (lane / 32) ..),
-// and keeps 8 splits' loads in flight. The result goes out as bf16 hi and
-// lo planes (lo = bf16(o^ - hi), about 16 significant bits), laid out
+// First the 32 heads' M and denominator, in one pass: thread (head h,
+// part p = tid / 32) runs an online max-and-sum over splits p, p + 8, ..
+// (loads issued four at a time), and the 8 parts are combined through LDS.
+// Then the weighted sum: in the fragment order of the (fp16) partials the
+// (hb, db) block is 2 KB contiguous per split; thread (g = tid / 64, lane)
+// owns the four values at 256 g + 4 lane of it (head hl = lane % 32,
+// columns 8 g + 4 (lane / 32) ..) and keeps 16 splits' loads (and their
+// lse) in flight (4 for a sequence of at most 4 splits). The result goes out as bf16 hi and lo planes
+// (lo = bf16(o^ - hi), about 16 significant bits), laid out
 // [head][sequence][column] for the W_UV product, through an LDS transpose.
+__device__ __forceinline__ void lse_combine(float &m, float &d, float m2, float d2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  d = d * exp2f(m - mn) + d2 * exp2f(m2 - mn);
+  m = mn;
+}
+// Weighted sum over a sequence's S splits, SB loads (and their lse) in
+// flight per batch; the last batch re-reads split S - 1 for its tail (in
+// bounds, weight 0), so short sequences take the small batch.
+template <int SB>
+__device__ __forceinline__ void merge_accumulate(float4 &acc, int S, const uint16_t *src, size_t stride,
+                                                 const float *lrow, int H, float M, float inv) {
+  for (int s0 = 0; s0 < S; s0 += SB) {
+    f16x4 x[SB];
+    float l[SB];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int s = min(s0 + u, S - 1);
+      l[u] = lrow[static_cast<size_t>(s) * H];
+      x[u] = *reinterpret_cast<const f16x4 *>(src + s * stride);
+    }
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const float wt = s0 + u < S ? exp2f(l[u] - M) * inv : 0.0f;
+      acc.x = fmaf(wt, static_cast<float>(x[u][0]), acc.x);
+      acc.y = fmaf(wt, static_cast<float>(x[u][1]), acc.y);
+      acc.z = fmaf(wt, static_cast<float>(x[u][2]), acc.z);
+      acc.w = fmaf(wt, static_cast<float>(x[u][3]), acc.w);
+    }
+  }
+}
 __global__ __launch_bounds__(256) void merge_fast_kernel(int B, int H, const SeqInfo *__restrict__ seqs,
                                                          const int32_t *__restrict__ dev_len,
                                                          const uint16_t *__restrict__ opart,
                                                          const float *__restrict__ lse, uint16_t *__restrict__ ohat) {
   using namespace fast;
-  constexpr int SB = 8;  // splits loaded per batch
   __shared__ float tile[32 * 33];
+  __shared__ float part_m[8][32], part_d[8][32];
   const int b = blockIdx.x, hb = blockIdx.y, db = blockIdx.z;
   const int tid = threadIdx.x, g = tid >> 6, lane = tid & 63, hl = lane & 31, half = lane >> 5;
   const int head = 32 * hb + hl;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const SeqInfo si = seqs[b];
-  if (si.item_count > 0 && dev_len[b] == si.len) {
+  const bool live = si.item_count > 0 && dev_len[b] == si.len;  // uniform over the workgroup
+  if (live) {
     const int S = si.item_count;
-    const float *lrow = lse + static_cast<size_t>(si.item_begin) * H + head;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, lrow[static_cast<size_t>(s) * H]);
+    const float *lcol = lse + static_cast<size_t>(si.item_begin) * H + 32 * hb;
+    {
+      const int h = tid & 31, p = tid >> 5;
+      float m = -INFINITY, d = 0.0f;
+      for (int s0 = p; s0 < S; s0 += 32) {
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int s = s0 + 8 * u;
+          x[u] = s < S ? lcol[static_cast<size_t>(s) * H + h] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lse_combine(m, d, x[u], 1.0f);  // -inf past S adds nothing
+      }
+      part_m[p][h] = m;
+      part_d[p][h] = d;
+    }
+    __syncthreads();
+    float M = part_m[0][hl], den = part_d[0][hl];
+#pragma unroll
+    for (int p = 1; p < 8; ++p) lse_combine(M, den, part_m[p][hl], part_d[p][hl]);
     if (M != -INFINITY) {
-      float den = 0.0f;
-      for (int s = 0; s < S; ++s) den += exp2f(lrow[static_cast<size_t>(s) * H] - M);
       const float inv = 1.0f / den;
+      const float *lrow = lcol + hl;
       const size_t stride = static_cast<size_t>(H / 32) * 16 * 1024;  // elements per item
       const uint16_t *src = opart + (static_cast<size_t>(si.item_begin) * (H / 32) + hb) * (16 * 1024) + 1024 * db +
                             256 * g + 4 * lane;
-      for (int s0 = 0; s0 < S; s0 += SB) {
-        f16x4 x[SB];
-        float wt[SB];
-#pragma unroll
-        for (int u = 0; u < SB; ++u) {
-          const int s = min(s0 + u, S - 1);
-          wt[u] = s0 + u < S ? exp2f(lrow[static_cast<size_t>(s) * H] - M) * inv : 0.0f;
-          x[u] = *reinterpret_cast<const f16x4 *>(src + s * stride);
-        }
-#pragma unroll
-        for (int u = 0; u < SB; ++u) {
-          acc.x = fmaf(wt[u], static_cast<float>(x[u][0]), acc.x);
-          acc.y = fmaf(wt[u], static_cast<float>(x[u][1]), acc.y);
-          acc.z = fmaf(wt[u], static_cast<float>(x[u][2]), acc.z);
-          acc.w = fmaf(wt[u], static_cast<float>(x[u][3]), acc.w);
-        }
-      }
+      if (S <= 4) merge_accumulate<4>(acc, S, src, stride, lrow, H, M, inv);
+      else merge_accumulate<16>(acc, S, src, stride, lrow, H, M, inv);
     }
   }
   float *trow = tile + hl * 33 + 8 * g + 4 * half;
@@ -257,14 +295,25 @@ __global__ __launch_bounds__(64) void project_fast_kernel(int B, int H, const ui
   const uint16_t *wrow = w_uv + (static_cast<size_t>(i) * DV + 32 * vb + hl) * DC + 8 * half;
   const uint16_t *hrow = ohat + (static_cast<size_t>(i) * B + min(b, B - 1)) * DC + 8 * half;
   const uint16_t *lrow = hrow + static_cast<size_t>(H) * B * DC;
+  // two batches of 16 k-steps, every load of a batch issued before its
+  // products (a lone wave per output tile: the loads' latency, not the
+  // matrix core, bounds the kernel)
   f32x16 acc = {};
-#pragma unroll 8
-  for (int kk = 0; kk < DC / 16; ++kk) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(wrow + 16 * kk);
-    const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(hrow + 16 * kk);
-    const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(lrow + 16 * kk);
-    acc = mfma32(a, bh, acc);
-    acc = mfma32(a, bl, acc);
+#pragma unroll
+  for (int k0 = 0; k0 < DC / 16; k0 += 16) {
+    bf16x8 a[16], bh[16], bl[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      a[u] = *reinterpret_cast<const bf16x8 *>(wrow + 16 * (k0 + u));
+      bh[u] = *reinterpret_cast<const bf16x8 *>(hrow + 16 * (k0 + u));
+      bl[u] = *reinterpret_cast<const bf16x8 *>(lrow + 16 * (k0 + u));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep all 48 loads ahead of the products
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      acc = mfma32(a[u], bh[u], acc);
+      acc = mfma32(a[u], bl[u], acc);
+    }
   }
   // D: lane holds sequence b0 + l%32, v = 32 vb + 8(r/4) + 4(l/32) + r%4
   if (b < B) {

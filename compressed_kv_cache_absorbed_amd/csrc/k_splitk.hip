@@ -449,11 +449,13 @@ __device__ __forceinline__ f16x8 value_frag(const ValueBase &vb, int j, int kb) 
 // one load or one convert-and-store.
 //
 // bf16 latents: the 9 direct loads of tile i+3 go out under the score
-// products (one every fourth product, the k_rope part at product 32), and the
-// widening of tile i+2, 9 chunks of 16 bytes per thread, runs under the value
-// products, where the LDS has bandwidth to spare (chunk x is loaded after
-// product 3 x, and converted and stored three products later, just before
-// the next chunk's load).
+// products (one every fourth product, the k_rope part at product 32), and so
+// does the widening of this wave's rows of tile i+2, 9 chunks of 16 bytes per
+// thread: the score products leave LDS bandwidth to spare, the value
+// products (transposed reads of the whole tile by every wave) do not. Chunk
+// x is loaded after product 16 + 2 x, once this wave's copies of tile i+2
+// have landed (waited for at product 16: only this step's first 5 copies
+// may still fly), and converted and stored two products later.
 //
 // Both run unconditionally, also in an item's last steps: a copy of a tile
 // past the item's end re-reads its last row (in bounds, cached) into a
@@ -470,7 +472,7 @@ struct HideBf16 {
   int lim;                // rows 8 w + x with x <= lim exist; later ones repeat the last
   uint32_t rope_voff;     // this lane's k_rope source offset from rope_base
   int w, lane, tid;
-  u32x4 v;
+  u32x4 v[2];
   __device__ __forceinline__ void score_step(int kk) {
     using M = sk::Map<false>;
     if (kk % 4 == 0 && kk / 4 < 8) {
@@ -479,11 +481,20 @@ struct HideBf16 {
       row += x + 1 <= lim ? stride : 0;
     }
     if (kk == 32) lds_dma16(rope_base, rope_voff, LDS_OFF(g_lds) + M::rope(DMA_BUF) + 1024 * w);
+    if (kk == 16) {
+      wait_vm<5>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kk >= 18 && kk % 2 == 0 && (kk - 18) / 2 < 9) {
+      const int x = (kk - 18) / 2;
+      widen_bf16_store<WIDEN_BUF>(tid, x, v[x & 1]);
+    }
+    if (kk >= 16 && kk % 2 == 0 && (kk - 16) / 2 < 9) {
+      const int x = (kk - 16) / 2;
+      v[x & 1] = widen_bf16_load<WIDEN_BUF>(tid, x);
+    }
   }
-  __device__ __forceinline__ void value_step(int n) {
-    if (n >= 3 && n % 3 == 0 && n / 3 <= 9) widen_bf16_store<WIDEN_BUF>(tid, n / 3 - 1, v);
-    if (n % 3 == 0 && n / 3 < 9) v = widen_bf16_load<WIDEN_BUF>(tid, n / 3);
-  }
+  __device__ __forceinline__ void value_step(int) {}
 };
 
 struct NoHide {
@@ -827,13 +838,13 @@ __device__ __forceinline__ void pv_rows(WaveState &st, const Softmax &sm, Hide &
 // tile. On entry tile i+1 is widened and visible and S (AGPRs) holds tile
 // i's scores; they are copied to VGPRs first. The step
 //   1. runs the score products of tile i+1 (buffer B+1) into S, with the
-//      softmax of tile i woven in and the copies of tile i+3 (into buffer
-//      B+3, which tile i-1 used) issued under them;
-//   2. waits for its own copies of tile i+2 (no other wave's: each wave
-//      widens the rows it copied);
-//   3. runs the value products of tile i (buffer B) with the widening of its
-//      rows of tile i+2 (buffer B+2) woven in;
-//   4. barrier: tile i+2 is ready for the next step's scores and buffer B is
+//      softmax of tile i woven in, the copies of tile i+3 (into buffer
+//      B+3, which tile i-1 used) issued under them
+//      and the widening of its rows of tile i+2 (buffer B+2) after them
+//      (no other wave's copies are needed: each wave widens the rows it
+//      copied);
+//   2. runs the value products of tile i (buffer B);
+//   3. barrier: tile i+2 is ready for the next step's scores and buffer B is
 //      free for the next step's copies.
 // In an item's last step the scores of the tile past its end are computed
 // on the finite rows that buffer holds and dropped.
@@ -865,8 +876,6 @@ __device__ __forceinline__ void step_bf16(WaveState &st, f32x16 &S, const Item &
   }
   Softmax sm;
   score_chain_bf16<(B + 1) % 4, true>(st, S, Sv, sm, h);
-  wait_vm<9>();  // this wave's copies of tile i+2 landed (this step's 9 may still fly)
-  __builtin_amdgcn_sched_barrier(0);
   pv_rows<B>(st, sm, h, i == 0);
   wait_lds();
   __builtin_amdgcn_s_barrier();
