@@ -9,8 +9,8 @@
 //   (the split-K kernel between them lives in k_splitk.hip)
 //   append_gemm_kernel   [c ; k_r] = [W_DKV ; W_KR] h for the new tokens (K-split)
 //   append_finish_kernel sum of the splits, RoPE, rounding / fp8 scale, row store
-//   merge_fast_kernel    log-sum-exp merge of the split partials into o^
-//   project_fast_kernel  o = W_UV o^ (the output-side absorption)
+//   combine_fast_kernel  log-sum-exp merge of the split partials and
+//                        o = W_UV o^ (the output-side absorption)
 //
 // Weight absorption ("02 — Multi-Latent Attention (MLA)", "Coste de cómputo";
 // "Atención latente de múltiples cabezas", "Información técnica"): W_UK is
@@ -37,10 +37,12 @@ namespace mla {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -168,167 +170,238 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qs
   }
 }
 
-// ------------------------------------------------------------------ merge
-// Grid (batch, H/32, d_c/32), 256 threads: sequence b, head block hb,
-// latent block db (32 columns). Log-sum-exp merge of the sequence's split
-// partials (base 2): o^ = sum_s 2^(lse_s - M) o^_s / sum_s 2^(lse_s - M).
-// First the 32 heads' M and denominator, in one pass: thread (head h,
-// part p = tid / 32) runs an online max-and-sum over splits p, p + 8, ..
-// (loads issued four at a time), and the 8 parts are combined through LDS.
-// Then the weighted sum: in the fragment order of the (fp16) partials the
-// (hb, db) block is 2 KB contiguous per split; thread (g = tid / 64, lane)
-// owns the four values at 256 g + 4 lane of it (head hl = lane % 32,
-// columns 8 g + 4 (lane / 32) ..) and keeps 16 splits' loads (and their
-// lse) in flight (4 for a sequence of at most 4 splits). The result goes out as bf16 hi and lo planes
-// (lo = bf16(o^ - hi), about 16 significant bits), laid out
-// [head][sequence][column] for the W_UV product, through an LDS transpose.
+// ---------------------------------------------------------------- combine
+// The log-sum-exp merge of the split partials (base 2) and the W_UV product
+// ("02 — Multi-Latent Attention (MLA)", "Coste de cómputo": W_UV is applied
+// to the latent-space output) in one kernel. 1-D grid of H G workgroups
+// (G = ceil(B / NB) groups of NB sequences), 512 threads (8 waves).
+// Workgroup L runs on XCD L % 8 and all groups of one head get the same
+// L % 8, so W_UV,i is fetched from HBM once and from that XCD's L2 by the
+// other groups. Every byte a workgroup reads arrives in whole rows: 1 KB
+// per load instruction.
+//   1. For each sequence b of the group: M_b = max_s lse_s and
+//      den_b = sum_s 2^(lse_s - M_b), by an online max-and-sum of its
+//      TPB = 512 / NB threads over splits p, p + TPB, .., combined by
+//      shuffles (and across waves in LDS, in a fixed order).
+//   2. o^[b] = sum_s 2^(lse_s - M_b) / den_b o^_s[b]: the partial rows are
+//      512 fp16 per (item, head); each of the TPB threads of a sequence owns
+//      512 / TPB columns (TPB >= 64: 8 columns, and R = TPB / 64 interleaved
+//      subsets of the splits whose sums meet in LDS in a fixed order), with
+//      12 or 16 splits' rows in flight, the first of them issued before
+//      step 1. o^ goes to LDS as bf16 hi and lo planes
+//      (lo = bf16(o^ - hi): about 16 significant bits).
+//   3. o[b, i, :] = W_UV,i o^[b] as D [16 v x 16 b] = W_UV rows (A) x o^^T
+//      (B, from LDS; hi and lo, two products per k-step) on
+//      v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16, k = 8(l/16) ..
+//      +7; B: column l%16, same k; D: lane l, register r holds row
+//      4(l/16) + r, column l%16). Wave w owns values 16 w .. 16 w + 15; it
+//      loads their rows whole at the start and turns them into the A
+//      layout through LDS (half of k at a time) once the merge is done.
+// A sequence with no splits, or whose length no longer matches the plan,
+// gets o = 0.
 __device__ __forceinline__ void lse_combine(float &m, float &d, float m2, float d2) {
   const float mn = fmaxf(m, m2);
   if (mn == -INFINITY) return;
   d = d * exp2f(m - mn) + d2 * exp2f(m2 - mn);
   m = mn;
 }
-// Weighted sum over a sequence's S splits, SB loads (and their lse) in
-// flight per batch; the last batch re-reads split S - 1 for its tail (in
-// bounds, weight 0), so short sequences take the small batch.
-template <int SB>
-__device__ __forceinline__ void merge_accumulate(float4 &acc, int S, const uint16_t *src, size_t stride,
-                                                 const float *lrow, int H, float M, float inv) {
-  for (int s0 = 0; s0 < S; s0 += SB) {
-    f16x4 x[SB];
-    float l[SB];
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// One batch of the weighted sum over a sequence's splits: the rows of
+// splits s0, s0 + R, .. (SBX of them, NL 16-byte loads each) and their lse.
+// Past the last split the batch re-reads split S - 1 (in bounds, weight 0).
+template <int NL, int SBX, int R>
+struct RowBatch {
+  u32x4 x[SBX][NL];
+  float l[SBX];
+  __device__ __forceinline__ void issue(int s0, int S, const uint16_t *src, size_t stride, const float *lcol, int H) {
 #pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      const int s = min(s0 + u, S - 1);
-      l[u] = lrow[static_cast<size_t>(s) * H];
-      x[u] = *reinterpret_cast<const f16x4 *>(src + s * stride);
-    }
+    for (int u = 0; u < SBX; ++u) {
+      const int s = min(s0 + R * u, S - 1);
+      l[u] = lcol[static_cast<size_t>(s) * H];
 #pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      const float wt = s0 + u < S ? exp2f(l[u] - M) * inv : 0.0f;
-      acc.x = fmaf(wt, static_cast<float>(x[u][0]), acc.x);
-      acc.y = fmaf(wt, static_cast<float>(x[u][1]), acc.y);
-      acc.z = fmaf(wt, static_cast<float>(x[u][2]), acc.z);
-      acc.w = fmaf(wt, static_cast<float>(x[u][3]), acc.w);
+      for (int n = 0; n < NL; ++n) x[u][n] = *reinterpret_cast<const u32x4 *>(src + s * stride + 8 * n);
     }
   }
-}
-__global__ __launch_bounds__(256) void merge_fast_kernel(int B, int H, const SeqInfo *__restrict__ seqs,
-                                                         const int32_t *__restrict__ dev_len,
-                                                         const uint16_t *__restrict__ opart,
-                                                         const float *__restrict__ lse, uint16_t *__restrict__ ohat) {
-  using namespace fast;
-  __shared__ float tile[32 * 33];
-  __shared__ float part_m[8][32], part_d[8][32];
-  const int b = blockIdx.x, hb = blockIdx.y, db = blockIdx.z;
-  const int tid = threadIdx.x, g = tid >> 6, lane = tid & 63, hl = lane & 31, half = lane >> 5;
-  const int head = 32 * hb + hl;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const SeqInfo si = seqs[b];
-  const bool live = si.item_count > 0 && dev_len[b] == si.len;  // uniform over the workgroup
-  if (live) {
-    const int S = si.item_count;
-    const float *lcol = lse + static_cast<size_t>(si.item_begin) * H + 32 * hb;
-    {
-      const int h = tid & 31, p = tid >> 5;
-      float m = -INFINITY, d = 0.0f;
-      for (int s0 = p; s0 < S; s0 += 32) {
-        float x[4];
+  __device__ __forceinline__ void consume(float (&acc)[8 * NL], int s0, int S, float M, float inv) const {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int s = s0 + 8 * u;
-          x[u] = s < S ? lcol[static_cast<size_t>(s) * H + h] : -INFINITY;
-        }
+    for (int u = 0; u < SBX; ++u) {
+      const float wt = s0 + R * u < S ? exp2f(l[u] - M) * inv : 0.0f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) lse_combine(m, d, x[u], 1.0f);  // -inf past S adds nothing
+      for (int n = 0; n < NL; ++n) {
+        const f16x8 v = __builtin_bit_cast(f16x8, x[u][n]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[8 * n + e] = fmaf(wt, static_cast<float>(v[e]), acc[8 * n + e]);
       }
-      part_m[p][h] = m;
-      part_d[p][h] = d;
+    }
+  }
+};
+template <int NB>
+__global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int G, const SeqInfo *__restrict__ seqs,
+                                                           const int32_t *__restrict__ dev_len,
+                                                           const uint16_t *__restrict__ opart,
+                                                           const float *__restrict__ lse,
+                                                           const uint16_t *__restrict__ w_uv, void *o, int o_bf16) {
+  using namespace fast;
+  constexpr int NW = 8;                            // waves
+  constexpr int TPB = 64 * NW / NB;                // threads per sequence
+  constexpr int R = TPB >= 64 ? TPB / 64 : 1;      // split subsets per sequence
+  constexpr int CPT = TPB >= 64 ? 8 : DC / TPB;    // columns per thread: 8 or 16
+  constexpr int NL = CPT / 8;                      // 16-byte loads per split
+  constexpr int SB = NL == 1 ? 16 : 12;            // splits per batch (rows in flight per thread)
+  constexpr int OROW = 1040;                       // LDS bytes per o^ row (conflict-free B reads)
+  constexpr int WROW = 528;                        // LDS bytes per staged W half-row
+  __shared__ __attribute__((aligned(16))) char so[2 * 16 * OROW];
+  __shared__ __attribute__((aligned(16))) char sw[NW * 16 * WROW];
+  __shared__ float red_m[NW], red_d[NW];
+  __shared__ __attribute__((aligned(16))) float red_acc[R > 1 ? NW : 1][DC];
+  const int L = blockIdx.x, slot = L >> 3;
+  const int i = (L & 7) + 8 * (slot / G), b0 = (slot % G) * NB;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+  const int bl = tid / TPB, q = tid % TPB;
+  const int b = b0 + bl;
+  int S = 0, ib = 0;
+  if (b < B) {
+    const SeqInfo si = seqs[b];
+    if (si.item_count > 0 && dev_len[b] == si.len) {
+      S = si.item_count;
+      ib = si.item_begin;
+    }
+  }
+  const float *lcol = lse + static_cast<size_t>(ib) * H + i;
+  // loads in the order they are needed: this thread's first lse for step 1,
+  // the first batch of partial rows for step 2 (they need no weight yet),
+  // then the weight rows for step 3
+  const float l0 = q < S ? lcol[static_cast<size_t>(q) * H] : -INFINITY;
+  const int r = TPB >= 64 ? q / 64 : 0;
+  const int c0 = TPB >= 64 ? 8 * (q % 64) : CPT * q;
+  const uint16_t *src = opart + (static_cast<size_t>(ib) * H + i) * DC + c0;
+  const size_t stride = static_cast<size_t>(H) * DC;
+  RowBatch<NL, SB, R> rb;
+  if (r < S) rb.issue(r, S, src, stride, lcol, H);
+
+  // rows 16 w .. 16 w + 15 of W_UV,i, whole: lane l holds columns 8 l .. 8 l + 7
+  u32x4 wr[16];
+  {
+    const uint16_t *wrow = w_uv + (static_cast<size_t>(i) * DV + 16 * w) * DC + 8 * lane;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) wr[x] = *reinterpret_cast<const u32x4 *>(wrow + x * DC);
+  }
+
+  // 1. M_b and den_b
+  float M = -INFINITY, den = 0.0f;
+  lse_combine(M, den, l0, 1.0f);
+  for (int s = q + TPB; s < S; s += TPB) lse_combine(M, den, lcol[static_cast<size_t>(s) * H], 1.0f);
+#pragma unroll
+  for (int off = 1; off < (TPB < 64 ? TPB : 64); off <<= 1) {
+    const float m2 = __shfl_xor(M, off), d2 = __shfl_xor(den, off);
+    lse_combine(M, den, m2, d2);  // symmetric: every lane ends with the same value
+  }
+  if (TPB > 64) {
+    if (lane == 0) {
+      red_m[w] = M;
+      red_d[w] = den;
     }
     __syncthreads();
-    float M = part_m[0][hl], den = part_d[0][hl];
+    M = red_m[bl * R];
+    den = red_d[bl * R];
 #pragma unroll
-    for (int p = 1; p < 8; ++p) lse_combine(M, den, part_m[p][hl], part_d[p][hl]);
-    if (M != -INFINITY) {
-      const float inv = 1.0f / den;
-      const float *lrow = lcol + hl;
-      const size_t stride = static_cast<size_t>(H / 32) * 16 * 1024;  // elements per item
-      const uint16_t *src = opart + (static_cast<size_t>(si.item_begin) * (H / 32) + hb) * (16 * 1024) + 1024 * db +
-                            256 * g + 4 * lane;
-      if (S <= 4) merge_accumulate<4>(acc, S, src, stride, lrow, H, M, inv);
-      else merge_accumulate<16>(acc, S, src, stride, lrow, H, M, inv);
-    }
+    for (int x = 1; x < R; ++x) lse_combine(M, den, red_m[bl * R + x], red_d[bl * R + x]);
   }
-  float *trow = tile + hl * 33 + 8 * g + 4 * half;
-  trow[0] = acc.x;
-  trow[1] = acc.y;
-  trow[2] = acc.z;
-  trow[3] = acc.w;
-  __syncthreads();
-  if (tid < 128) {  // head hh, 8 columns from c0
-    const int hh = tid >> 2, c0 = 8 * (tid & 3);
-    bf16x8 hi, lo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = tile[hh * 33 + c0 + e];
-      const __bf16 h = static_cast<__bf16>(v);
-      hi[e] = h;
-      lo[e] = static_cast<__bf16>(v - static_cast<float>(h));
-    }
-    uint16_t *dh = ohat + (static_cast<size_t>(32 * hb + hh) * B + b) * DC + 32 * db + c0;
-    *reinterpret_cast<bf16x8 *>(dh) = hi;
-    *reinterpret_cast<bf16x8 *>(dh + static_cast<size_t>(H) * B * DC) = lo;
-  }
-}
 
-// ---------------------------------------------------------------- project
-// Grid (H, d_v/32, ceil(B/32)), one wave: o[b, i, v] = W_UV,i[v, :] o^[b, i, :]
-// for 32 values v and 32 sequences, as D^T [32 v x 32 b] = W_UV rows (A,
-// straight from global memory) times o^^T (B: the hi and lo planes, two
-// products per k-step).
-__global__ __launch_bounds__(64) void project_fast_kernel(int B, int H, const uint16_t *__restrict__ ohat,
-                                                          const uint16_t *__restrict__ w_uv, void *o, int o_bf16) {
-  using namespace fast;
-  const int i = blockIdx.x, vb = blockIdx.y, b0 = blockIdx.z * 32;
-  const int lane = threadIdx.x, hl = lane & 31, half = lane >> 5;
-  const int b = b0 + hl;
-  const uint16_t *wrow = w_uv + (static_cast<size_t>(i) * DV + 32 * vb + hl) * DC + 8 * half;
-  const uint16_t *hrow = ohat + (static_cast<size_t>(i) * B + min(b, B - 1)) * DC + 8 * half;
-  const uint16_t *lrow = hrow + static_cast<size_t>(H) * B * DC;
-  // two batches of 16 k-steps, every load of a batch issued before its
-  // products (a lone wave per output tile: the loads' latency, not the
-  // matrix core, bounds the kernel)
-  f32x16 acc = {};
-#pragma unroll
-  for (int k0 = 0; k0 < DC / 16; k0 += 16) {
-    bf16x8 a[16], bh[16], bl[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      a[u] = *reinterpret_cast<const bf16x8 *>(wrow + 16 * (k0 + u));
-      bh[u] = *reinterpret_cast<const bf16x8 *>(hrow + 16 * (k0 + u));
-      bl[u] = *reinterpret_cast<const bf16x8 *>(lrow + 16 * (k0 + u));
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep all 48 loads ahead of the products
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      acc = mfma32(a[u], bh[u], acc);
-      acc = mfma32(a[u], bl[u], acc);
+  // 2. o^[b]; rows NB .. 15 of the B operand are zero
+  if (NB < 16) {
+    constexpr int ZR = NB < 16 ? 16 - NB : 1;
+    for (int x = tid; x < 2 * ZR * 64; x += 64 * NW) {
+      const int pl = x / (ZR * 64), row = NB + (x / 64) % ZR;
+      *reinterpret_cast<u32x4 *>(so + (pl * 16 + row) * OROW + 16 * (x % 64)) = u32x4{0, 0, 0, 0};
     }
   }
-  // D: lane holds sequence b0 + l%32, v = 32 vb + 8(r/4) + 4(l/32) + r%4
-  if (b < B) {
-    const size_t base = (static_cast<size_t>(b) * H + i) * DV + 32 * vb + 4 * half;
+  float acc[CPT];
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      if (o_bf16) {
-        bf16x4 v;
+  for (int e = 0; e < CPT; ++e) acc[e] = 0.0f;
+  if (M != -INFINITY && r < S) {
+    const float inv = 1.0f / den;
+    rb.consume(acc, r, S, M, inv);
+    for (int s0 = r + R * SB; s0 < S; s0 += R * SB) {
+      rb.issue(s0, S, src, stride, lcol, H);
+      rb.consume(acc, s0, S, M, inv);
+    }
+  }
+
+  // W_UV rows into the A layout: k-half h, k-step kk = 8 h + t: lane l
+  // takes row l%16, columns 256 h + 32 t + 8(l/16) .. +7
+  bf16x8 wa[DC / 32];
+  {
+    char *sww = sw + w * 16 * WROW;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = static_cast<__bf16>(acc[4 * g4 + r]);
-        *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(o) + base + 8 * g4) = v;
-      } else {
-        *reinterpret_cast<float4 *>(static_cast<float *>(o) + base + 8 * g4) =
-            make_float4(acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]);
+    for (int h = 0; h < 2; ++h) {
+      // lanes exchange data through LDS: wave-scope fences keep the compiler
+      // from reusing the first pass's loads or moving the stores across them
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      if ((lane >> 5) == h) {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) *reinterpret_cast<u32x4 *>(sww + x * WROW + 16 * (lane & 31)) = wr[x];
       }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        wa[8 * h + t] = *reinterpret_cast<const bf16x8 *>(sww + (lane & 15) * WROW + 64 * t + 16 * (lane >> 4));
+    }
+  }
+
+  if (R > 1) {
+    if (r > 0) {
+#pragma unroll
+      for (int e = 0; e < CPT; e += 4)
+        *reinterpret_cast<float4 *>(&red_acc[w][c0 + e]) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    }
+    __syncthreads();
+    if (r == 0) {
+#pragma unroll
+      for (int x = 1; x < R; ++x) {
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) acc[e] += red_acc[w + x][c0 + e];
+      }
+    }
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int e0 = 0; e0 < CPT; e0 += 8) {
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 hv = static_cast<__bf16>(acc[e0 + e]);
+        hi[e] = hv;
+        lo[e] = static_cast<__bf16>(acc[e0 + e] - static_cast<float>(hv));
+      }
+      char *row = so + bl * OROW + 2 * (c0 + e0);
+      *reinterpret_cast<bf16x8 *>(row) = hi;
+      *reinterpret_cast<bf16x8 *>(row + 16 * OROW) = lo;
+    }
+  }
+  __syncthreads();
+
+  // 3. o = W_UV,i o^
+  f32x4 d = {};
+  const char *bp = so + (lane & 15) * OROW + 16 * (lane >> 4);
+#pragma unroll
+  for (int kk = 0; kk < DC / 32; ++kk) {
+    d = mfma16(wa[kk], *reinterpret_cast<const bf16x8 *>(bp + 64 * kk), d);
+    d = mfma16(wa[kk], *reinterpret_cast<const bf16x8 *>(bp + 64 * kk + 16 * OROW), d);
+  }
+  const int bo = b0 + (lane & 15);
+  if ((lane & 15) < NB && bo < B) {
+    const size_t base = (static_cast<size_t>(bo) * H + i) * DV + 16 * w + 4 * (lane >> 4);
+    if (o_bf16) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(d[e]);
+      *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(o) + base) = v;
+    } else {
+      *reinterpret_cast<float4 *>(static_cast<float *>(o) + base) = make_float4(d[0], d[1], d[2], d[3]);
     }
   }
 }
@@ -447,16 +520,29 @@ hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, c
                        static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seqs, q_out);
 }
 
-hipError_t launch_merge_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const SeqInfo *seqs,
-                             const uint16_t *opart, const float *lse, uint16_t *ohat) {
-  return launch_kernel(merge_fast_kernel, dim3(c.batch, d.n_heads / 32, fast::DC / 32), 256, 0, s, c.batch,
-                       d.n_heads, seqs, c.seq_len, opart, lse, ohat);
-}
-
-hipError_t launch_project_fast(hipStream_t s, const mla_dims &d, int32_t batch, const uint16_t *ohat,
-                               const void *w_uv, void *o, mla_dtype od) {
-  return launch_kernel(project_fast_kernel, dim3(d.n_heads, fast::DV / 32, (batch + 31) / 32), 64, 0, s, batch,
-                       d.n_heads, ohat, static_cast<const uint16_t *>(w_uv), o, od == MLA_BF16 ? 1 : 0);
+hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const SeqInfo *seqs,
+                               const uint16_t *opart, const float *lse, const uint16_t *w_uv, void *o, int o_bf16) {
+  const int B = c.batch, H = d.n_heads;
+  if (B == 0) return hipSuccess;
+  // the largest group (up to the 16 columns of one product) that still
+  // gives a workgroup to every compute unit
+  int nb = 1;
+  while (nb < 16 && static_cast<int64_t>(H) * ((B + 2 * nb - 1) / (2 * nb)) >= 256) nb *= 2;
+  const int G = (B + nb - 1) / nb;
+  const dim3 grid(H * G);
+#define MLA_COMBINE(NBV)                                                                                      \
+  case NBV:                                                                                                  \
+    return launch_kernel(combine_fast_kernel<NBV>, grid, 512, 0, s, B, H, G, seqs, c.seq_len, opart, lse, w_uv, \
+                         o, o_bf16)
+  switch (nb) {
+    MLA_COMBINE(1);
+    MLA_COMBINE(2);
+    MLA_COMBINE(4);
+    MLA_COMBINE(8);
+    default:
+      MLA_COMBINE(16);
+  }
+#undef MLA_COMBINE
 }
 
 }  // namespace mla

@@ -69,6 +69,7 @@ constexpr int SLACK = 8;             // running max is kept unless exceeded by 2
 constexpr int SPF = 3;               // score fragments read ahead of their product
 constexpr int VPF = 4;               // value fragments read ahead of their product
 constexpr int VBLK = 15;             // the output block kept in VGPRs (its AGPRs hold the scores)
+constexpr int OROW = 1040;           // partial row stride of the closing transpose in LDS (bytes)
 
 // LDS map. bf16 latents: four fp16 tiles (copied and widened in place).
 // fp8 latents: three fp16 tiles, two raw tiles and their per-token scales,
@@ -85,6 +86,7 @@ template <bool FP8> struct Map {
 };
 constexpr int LDS_BYTES = Map<false>::end() > Map<true>::end() ? Map<false>::end() : Map<true>::end();
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(4 * 32 * OROW <= Map<false>::end() && 4 * 32 * OROW <= Map<true>::end(), "transpose area");
 }  // namespace sk
 
 __shared__ __attribute__((aligned(1024))) char g_lds[sk::LDS_BYTES];
@@ -712,16 +714,15 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
   const int half = lane >> 5;
   const int head = blockIdx.y * 128 + 32 * w + (lane & 31);
   const WorkItem wi = items[k];
-  // this workgroup's 128 heads of item k: 4 head blocks of 32 KB in the
-  // fragment order of the (fp16) partials
-  uint16_t *ob = opart + (static_cast<size_t>(k) * (H / 32) + blockIdx.y * 4) * (16 * 1024);
+  // this workgroup's 128 heads of item k: 128 rows of 512 fp16 partials
+  uint16_t *ob = opart + (static_cast<size_t>(k) * H + blockIdx.y * 128) * DC;
 
   const bool ok = c.seq_len[wi.b] == seqs[wi.b].len && wi.t0 >= 0 && wi.t0 < wi.t1 &&
                   wi.t1 <= c.seq_cap[wi.b] && static_cast<int64_t>(c.seq_start[wi.b]) >= 0 &&
                   static_cast<int64_t>(c.seq_start[wi.b]) + wi.t1 <= c.n_rows;
   if (!ok) {
     if (tid == 0 && blockIdx.y == 0) set_status(status, MLA_ERR_PLAN);
-    for (int x = tid; x < 4 * 16 * 256 / 2; x += 256) reinterpret_cast<u32x4 *>(ob)[x] = u32x4{0, 0, 0, 0};
+    for (int x = tid; x < 128 * DC / 8; x += 256) reinterpret_cast<u32x4 *>(ob)[x] = u32x4{0, 0, 0, 0};
     if (half == 0) lse[static_cast<size_t>(k) * H + head] = -INFINITY;
     return;
   }
@@ -812,10 +813,15 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
     if (x == VBLK) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(st.O[x]));
     else asm volatile("" : "+a"(st.O[x]));
   }
-  // ---- normalised partials and log-sum-exp (base 2) of this wave's heads:
-  // register group g4 of column block cb is one 512-byte run of head block w
+  // ---- normalised partials and log-sum-exp (base 2) of this wave's heads,
+  // written head by head (one 1 KB row of 512 fp16 per head). The
+  // accumulator holds a head per lane, so the wave turns it around in LDS:
+  // every wave's copies have landed and every wave is past its last tile
+  // read once all have reached the barrier, so the tile buffers are free.
+  __builtin_amdgcn_s_barrier();
   const float inv = 1.0f / st.l;
   if (half == 0) lse[static_cast<size_t>(k) * H + head] = st.m + log2f(st.l);
+  char *tb = g_lds + w * 32 * OROW;
 #pragma unroll
   for (int cb = 0; cb < DC / 32; ++cb) {
 #pragma unroll
@@ -823,9 +829,15 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
       f16x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(st.O[cb][4 * g4 + e] * inv);
-      *reinterpret_cast<f16x4 *>(ob + ((w * 16 + cb) * 4 + g4) * 256 + 4 * lane) = v;
+      // head lane%32, columns 32 cb + 8 g4 + 4 half .. +3
+      *reinterpret_cast<f16x4 *>(tb + (lane & 31) * OROW + 64 * cb + 16 * g4 + 8 * half) = v;
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the rows come from other lanes
+  uint16_t *orow = ob + static_cast<size_t>(32 * w) * DC + 8 * lane;
+#pragma unroll
+  for (int h = 0; h < 32; ++h)
+    *reinterpret_cast<u32x4 *>(orow + h * DC) = *reinterpret_cast<const u32x4 *>(tb + h * OROW + 16 * lane);
 }
 
 }  // namespace

@@ -84,7 +84,7 @@ Profiler &prof() {
 const char *kKernelNames[K_COUNT] = {
     "init",           "append_generic", "append_gemm",    "append_finish",
     "absorb_generic", "absorb_fast",    "decode_generic", "decode_bf16",
-    "decode_fp8",     "combine_generic", "merge_fast",    "project_fast", "copy"};
+    "decode_fp8",     "combine_generic", "combine_fast",  "copy"};
 
 #define MLA_LAUNCH(stream, kid, call)          \
   do {                                         \
@@ -154,8 +154,6 @@ DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items) {
   off = align_up(off + sizeof(float) * static_cast<size_t>(std::max(n_items, 1)) * d.n_heads * d.d_c, 256);
   w.lse = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(std::max(n_items, 1)) * d.n_heads, 256);
-  w.ohat = off;
-  off = align_up(off + 2 * sizeof(uint16_t) * static_cast<size_t>(batch) * d.n_heads * d.d_c, 256);
   w.total = off;
   return w;
 }
@@ -479,9 +477,8 @@ static mla_status do_decode(const mla_dims *dims, const mla_cache *cache, const 
                launch_absorb_fast(s, *dims, plan->batch, q_nope, q_rope, q_pos, w_uk, seqs, q));
     MLA_LAUNCH(s, cache->latent_dtype == MLA_FP8_E4M3 ? K_DECODE_FP8 : K_DECODE_BF16,
                launch_decode_fast(s, *dims, *cache, plan->n_items, items, seqs, q, opart16, lse, status));
-    uint16_t *ohat = reinterpret_cast<uint16_t *>(base + w.ohat);
-    MLA_LAUNCH(s, K_MERGE_FAST, launch_merge_fast(s, *dims, *cache, seqs, opart16, lse, ohat));
-    MLA_LAUNCH(s, K_PROJECT_FAST, launch_project_fast(s, *dims, plan->batch, ohat, w_uv, o, od));
+    MLA_LAUNCH(s, K_COMBINE_FAST,
+               launch_combine_fast(s, *dims, *cache, seqs, opart16, lse, static_cast<const uint16_t *>(w_uv), o, od));
   } else {
     float *q = reinterpret_cast<float *>(base + w.q);
     MLA_LAUNCH(s, K_ABSORB_GENERIC,

@@ -29,8 +29,7 @@ enum KernelId : int {
   K_DECODE_BF16,
   K_DECODE_FP8,
   K_COMBINE_GENERIC,
-  K_MERGE_FAST,
-  K_PROJECT_FAST,
+  K_COMBINE_FAST,
   K_COPY,
   K_COUNT
 };
@@ -76,26 +75,11 @@ struct DecodeWs {
   size_t items = 0;   // WorkItem[n_items]
   size_t seqs = 0;    // SeqInfo[batch]
   size_t q = 0;       // absorbed query [batch, H, d_c + d_rope]: bf16 (fast) or f32
-  size_t opart = 0;   // f32 [n_items, H, d_c]; matrix-core path: fp16 in fragment order (below)
+  size_t opart = 0;   // normalised split partials [n_items, H, d_c]: f32, or fp16 on the matrix-core path
   size_t lse = 0;     // f32 [n_items, H]
-  size_t ohat = 0;    // matrix-core path: merged o^ as bf16 hi and lo planes [2][H][batch][d_c]
   size_t total = 0;
 };
 DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items);
-
-// Fragment order of the matrix-core split partials (d_c = 512, fp16): the
-// normalised partial o^ of item k, head 32 hb + hl, latent column
-// 32 db + 8 g + 4 h + e is element
-//   (((k * H/32 + hb) * 16 + db) * 4 + g) * 256 + 4 (hl + 32 h) + e,
-// i.e. one matrix-core output register group per 512 bytes, so the split-K
-// kernel stores whole runs and the merge reads 2 KB runs. fp16 halves the
-// partials' traffic; a normalised partial is an average of cached values,
-// which the fp16 products already require below 65504 in magnitude.
-inline size_t opart_frag_offset(size_t k, int n_heads, int head, int col) {
-  const int hb = head >> 5, hl = head & 31, db = col >> 5, r = col & 31;
-  const int g = r >> 3, h = (r >> 2) & 1, e = r & 3;
-  return (((k * (n_heads / 32) + hb) * 16 + db) * 4 + g) * 256 + 4 * (hl + 32 * h) + e;
-}
 
 struct AppendWs {
   size_t status = 0;
@@ -144,10 +128,8 @@ hipError_t launch_decode_fast(hipStream_t s, const mla_dims &d, const mla_cache 
 hipError_t launch_combine_generic(hipStream_t s, const mla_dims &d, const mla_cache &c,
                                   const SeqInfo *seqs, const float *opart, const float *lse,
                                   const void *w_uv, mla_dtype qw, void *o, mla_dtype od);
-hipError_t launch_merge_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const SeqInfo *seqs,
-                             const uint16_t *opart, const float *lse, uint16_t *ohat);
-hipError_t launch_project_fast(hipStream_t s, const mla_dims &d, int32_t batch, const uint16_t *ohat,
-                               const void *w_uv, void *o, mla_dtype od);
+hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const SeqInfo *seqs,
+                               const uint16_t *opart, const float *lse, const uint16_t *w_uv, void *o, int o_bf16);
 
 hipError_t launch_copy(hipStream_t s, void *dst, const void *src, size_t n16);
 
