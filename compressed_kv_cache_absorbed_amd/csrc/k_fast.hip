@@ -99,32 +99,16 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qs
   __shared__ __attribute__((aligned(16))) char smem[DNOPE * WROW];
   const int i = blockIdx.x, cq = blockIdx.y, b0 = blockIdx.z * 32;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const uint16_t *W = w_uk + static_cast<size_t>(i) * DNOPE * DC + 128 * cq;
-  // 32 KB of weights: 128 rows x 16 chunks of 16 bytes, 8 per thread
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const int q = tid + 256 * x, n = q >> 4, ch = q & 15;
-    *reinterpret_cast<u32x4 *>(smem + n * WROW + 16 * ch) = *reinterpret_cast<const u32x4 *>(W + n * DC + 8 * ch);
+  // every global load first, in the order of use: the RoPE inputs, the
+  // q_nope fragments, the weight quarter (32 KB: 128 rows x 16 chunks of
+  // 16 bytes, 8 per thread)
+  const int rb = b0 + (tid >> 3), rp = 8 * cq + (tid & 7);  // RoPE: sequence, pair
+  int64_t P = 0;
+  uint32_t xr = 0;
+  if (rb < B) {
+    P = q_pos ? q_pos[rb] : static_cast<int64_t>(seqs[rb].len) - 1;
+    xr = *reinterpret_cast<const uint32_t *>(q_rope + (static_cast<size_t>(rb) * H + i) * DR + 2 * rp);
   }
-
-  // RoPE: thread (sequence b0 + tid / 8, pair 8 cq + tid % 8)
-  {
-    const int bb = b0 + (tid >> 3), p = 8 * cq + (tid & 7);
-    if (bb < B) {
-      const size_t bi = static_cast<size_t>(bb) * H + i;
-      const int64_t P = q_pos ? q_pos[bb] : static_cast<int64_t>(seqs[bb].len) - 1;
-      float cs, sn;
-      rope_cos_sin(P, p, DR, rope_base, &cs, &sn);
-      const uint32_t xr = *reinterpret_cast<const uint32_t *>(q_rope + bi * DR + 2 * p);
-      const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(xr & 0xffffu));
-      const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(xr >> 16));
-      f16x2 r;
-      r[0] = static_cast<_Float16>((x0 * cs - x1 * sn) * qscale);
-      r[1] = static_cast<_Float16>((x0 * sn + x1 * cs) * qscale);
-      *reinterpret_cast<f16x2 *>(Q + bi * D + DC + 2 * p) = r;
-    }
-  }
-
   // B operand: q_nope^T [16 n x 32 b]: lane holds sequence b0 + l%32, n = 16 kk + 8(l/32) .. +7
   const int bb = b0 + (lane & 31);
   bf16x8 qb[DNOPE / 16];
@@ -136,6 +120,30 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qs
     } else {
       qb[kk] = bf16x8{};
     }
+  }
+  const uint16_t *W = w_uk + static_cast<size_t>(i) * DNOPE * DC + 128 * cq;
+  u32x4 wv[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const int q = tid + 256 * x, n = q >> 4, ch = q & 15;
+    wv[x] = *reinterpret_cast<const u32x4 *>(W + n * DC + 8 * ch);
+  }
+
+  // RoPE of pair rp of sequence rb, while the weights land
+  if (rb < B) {
+    float cs, sn;
+    rope_cos_sin(P, rp, DR, rope_base, &cs, &sn);
+    const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(xr & 0xffffu));
+    const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(xr >> 16));
+    f16x2 r;
+    r[0] = static_cast<_Float16>((x0 * cs - x1 * sn) * qscale);
+    r[1] = static_cast<_Float16>((x0 * sn + x1 * cs) * qscale);
+    *reinterpret_cast<f16x2 *>(Q + (static_cast<size_t>(rb) * H + i) * D + DC + 2 * rp) = r;
+  }
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const int q = tid + 256 * x, n = q >> 4, ch = q & 15;
+    *reinterpret_cast<u32x4 *>(smem + n * WROW + 16 * ch) = wv[x];
   }
   __syncthreads();
   // A operand: W^T [32 c x 16 n] via transposed LDS reads of W [n][c], with
