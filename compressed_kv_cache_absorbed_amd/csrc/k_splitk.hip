@@ -708,7 +708,11 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
                                                         float *__restrict__ lse,
                                                         int32_t *__restrict__ status) {
   using namespace sk;
-  const int k = blockIdx.x;
+  // item k: workgroup L runs on XCD L % 8; the items of one sequence are
+  // consecutive, so giving each XCD a contiguous block of items lets the
+  // splits of a sequence share its absorbed query in that XCD's L2
+  const int n = gridDim.x, nfull = n & ~7, L = blockIdx.x;
+  const int k = L < nfull ? (L & 7) * (nfull >> 3) + (L >> 3) : L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;

@@ -58,13 +58,27 @@ def test_fast_matches_generic_path(gpu, latent, monkeypatch):
     gen = to_np(run.decode(n_workers=8))
     monkeypatch.delenv("MLA_FORCE_GENERIC")
     # the generic path keeps q~ and P in fp32 (it agrees with the oracle to
-    # ~1e-5); the fast one rounds q~ to fp16 and P to bf16, so the two differ
-    # by the fast path's own rounding error
+    # ~1e-5); the fast one rounds q~, P and the cached values to fp16, so the
+    # two differ by the fast path's own rounding error
     tol = TOL_FP8_REL if latent == "fp8" else TOL_BF16_REL
     ref = oracle_decode(case, absorbed=True)
     assert rel_rms_err(gen, ref) <= 1e-4
     assert rel_rms_err(fast, ref) <= tol
     assert rel_rms_err(fast, gen) <= tol
+
+
+@pytest.mark.parametrize("B", [1, 3, 8, 12, 20])
+def test_fast_combine_group_sizes(gpu, B):
+    """The combine kernel groups 1, 2, 4, 8 or 16 sequences per workgroup
+    (by batch size); every grouping, with a partial last group, and many
+    splits per sequence."""
+    rng = np.random.default_rng(1000 + B)
+    lens = [int(x) for x in rng.integers(1, 400, size=B)]
+    case = v3_case(lens, seed=60 + B)
+    run = GpuRun(gpu, case)
+    o = to_np(run.decode(n_workers=4 * B + 3))
+    assert run.status() == 0
+    check(case, o, TOL_BF16_REL)
 
 
 def test_fast_split_invariance_and_determinism(gpu):
