@@ -67,16 +67,18 @@ def test_fast_matches_generic_path(gpu, latent, monkeypatch):
     assert rel_rms_err(fast, gen) <= tol
 
 
-@pytest.mark.parametrize("B", [1, 3, 8, 12, 20])
-def test_fast_combine_group_sizes(gpu, B):
+@pytest.mark.parametrize("B,max_len,splits", [(1, 400, 4), (1, 6000, 300), (3, 400, 4), (8, 400, 4),
+                                               (12, 400, 4), (20, 400, 4), (20, 1200, 24)])
+def test_fast_combine_group_sizes(gpu, B, max_len, splits):
     """The combine kernel groups 1, 2, 4, 8 or 16 sequences per workgroup
-    (by batch size); every grouping, with a partial last group, and many
-    splits per sequence."""
-    rng = np.random.default_rng(1000 + B)
-    lens = [int(x) for x in rng.integers(1, 400, size=B)]
+    (by batch size); every grouping, with a partial last group, and more
+    splits per sequence than one batch of row loads holds (B = 1 with 188
+    splits, B = 20 with up to 38)."""
+    rng = np.random.default_rng(1000 + B + max_len)
+    lens = [int(x) for x in rng.integers(max_len // 2 if max_len > 1000 else 1, max_len, size=B)]
     case = v3_case(lens, seed=60 + B)
     run = GpuRun(gpu, case)
-    o = to_np(run.decode(n_workers=4 * B + 3))
+    o = to_np(run.decode(n_workers=splits * B + 3))
     assert run.status() == 0
     check(case, o, TOL_BF16_REL)
 
