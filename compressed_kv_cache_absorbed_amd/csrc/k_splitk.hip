@@ -674,8 +674,7 @@ template <int I> struct StepHide<true, I> {
 // this wave's rows of tile i+2 woven in, then the value products of tile i,
 // then one barrier: tile i+2 is ready for the next step's scores, and tile
 // i's buffer (and, fp8, the raw buffer tile i+2 came from) is free for the
-// next step's copies. In an item's last step the scores of the tile past its
-// end are computed on the finite rows its buffer holds and dropped.
+// next step's copies. An item's last step runs the softmax alone.
 template <bool FP8, int I>
 __device__ __forceinline__ void step(WaveState &st, f32x16 &S, const Item &it, int i, int w, int lane, int tid) {
   constexpr int NB = sk::Map<FP8>::NBUF;
@@ -692,7 +691,14 @@ __device__ __forceinline__ void step(WaveState &st, f32x16 &S, const Item &it, i
       if (8 * (r >> 2) + (r & 3) >= lim) Sv[r] = -INFINITY;
   }
   Softmax sm;
-  score_chain<FP8, (I + 1) % NB, true>(st, S, Sv, sm, h);
+  if (i + 1 < it.ntiles) {
+    score_chain<FP8, (I + 1) % NB, true>(st, S, Sv, sm, h);
+  } else {
+    // the item's last tile: no next tile to score and nothing left to copy
+    // or widen, only this tile's softmax
+#pragma unroll
+    for (int kk = 0; kk <= 24; ++kk) softmax_piece(st, sm, Sv, kk);
+  }
   pv_rows<FP8, I % NB>(st, sm, i == 0);
   wait_lds();
   __builtin_amdgcn_s_barrier();

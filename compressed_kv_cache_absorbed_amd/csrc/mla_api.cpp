@@ -207,7 +207,7 @@ mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32
   }
   int64_t min_tiles = 1;
   if (n_workers == 0) {
-    min_tiles = 8;
+    min_tiles = 2;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)

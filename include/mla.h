@@ -136,8 +136,9 @@ mla_status mla_append(const mla_dims *dims, const mla_cache *cache, const void *
  * log-sum-exp identity (the combine step). n_workers is the number of
  * concurrent work items to aim for; 0 means "derive from the current HIP
  * device" (one per compute unit), and then no item is made shorter than
- * 256 tokens unless its sequence is (a few long items beat many one-tile
- * ones whose partial results cost more to write and merge than they save).
+ * 64 tokens unless its sequence is (an item's fixed cost, its first copies
+ * and its partial result, outweighs a one-tile item's work; a 4K-token
+ * sequence alone runs fastest in 64 items of two tiles).
  * With an explicit n_workers the chunks are as short as that count needs
  * (one 32-token tile at the least). The plan is deterministic in its inputs
  * and reusable across layers and calls with the same lengths. Returns
