@@ -67,6 +67,21 @@ def test_fast_matches_generic_path(gpu, latent, monkeypatch):
     assert rel_rms_err(fast, gen) <= tol
 
 
+@pytest.mark.parametrize("latent", ["bf16", "fp8"])
+def test_fast_256_heads(gpu, latent):
+    """Two 128-head blocks per work item (split-K grid of two rows of
+    workgroups), and a head count the combine kernel maps across XCDs in
+    two rounds."""
+    lens = [45, 300, 0, 97, 1024]
+    case = make(B=len(lens), lens=("list", lens), latent_dtype=latent, rope_dtype="bf16", act_dtype="bf16",
+                seed=70, H=256, d_c=512, d_rope=64, d_nope=128, d_v=128)
+    run = GpuRun(gpu, case)
+    o = to_np(run.decode(n_workers=12))
+    assert run.status() == 0
+    check(case, o, TOL_FP8_REL if latent == "fp8" else TOL_BF16_REL)
+    assert np.all(o[2] == 0)
+
+
 @pytest.mark.parametrize("B,max_len,splits", [(1, 400, 4), (1, 6000, 300), (3, 400, 4), (8, 400, 4),
                                                (12, 400, 4), (20, 400, 4), (20, 1200, 24)])
 def test_fast_combine_group_sizes(gpu, B, max_len, splits):
