@@ -244,6 +244,49 @@ def decode_absorbed(C, R, seq_start, seq_len, q_nope, q_rope, w_uk, w_uv,
     return out
 
 
+# ------------------------------------------------------ several query tokens
+
+
+def decode_multi(C, R, seq_start, seq_len, q_nope, q_rope, w_uk, w_uv, softmax_scale,
+                 rope_base, q_pos=None, triples=None, absorbed=False):
+    """Decode of Q new query tokens per sequence (the use the pages name next
+    to MLA: multi-token prediction and speculative decoding, "Multi-head Latent
+    Attention (MLA) și arhitectura DeepSeekMoE", "Concepte cheie și
+    caracteristici"; "02 — Multi-Latent Attention (MLA)", "Lo que esta fase NO
+    cubre"). The pages give no formula for it; the plainest reading, causal
+    attention among the new tokens, is taken:
+
+    * the Q new tokens are the last Q cached rows of the sequence (appended
+      before the decode, as for one token);
+    * query j (j = 0 .. Q-1) sits at position P_b - (Q - 1 - j), with P_b =
+      q_pos[b] or seq_len[b] - 1, and sees rows 0 .. seq_len[b] - 1 - (Q - 1 - j):
+      itself and what precedes it, never a later new token;
+    * so query j is exactly one single-token decode over the cache truncated
+      to the rows it sees, which is how it is computed here.
+
+    q_nope [B, Q, H, d_nope], q_rope [B, Q, H, d_hR]. A query that sees no row
+    (seq_len[b] < Q - j) gives 0. Returns o [B, Q, H, d_v], or [len(triples),
+    d_v] for a list of (b, j, i) triples."""
+    B, Q, H, _ = q_nope.shape
+    d_v = w_uv.shape[1]
+    fn = decode_absorbed if absorbed else decode
+    L = np.asarray(seq_len, dtype=np.int64)
+    P = _positions(seq_len, q_pos)
+    if triples is None:
+        out = np.zeros((B, Q, H, d_v), dtype=np.float64)
+        for j in range(Q):
+            back = Q - 1 - j
+            out[:, j] = fn(C, R, seq_start, np.maximum(L - back, 0), q_nope[:, j], q_rope[:, j], w_uk, w_uv,
+                           softmax_scale, rope_base, q_pos=P - back)
+        return out
+    out = np.zeros((len(triples), d_v), dtype=np.float64)
+    for n, (b, j, i) in enumerate(triples):
+        back = Q - 1 - int(j)
+        out[n] = fn(C, R, seq_start, np.maximum(L - back, 0), q_nope[:, j], q_rope[:, j], w_uk, w_uv,
+                    softmax_scale, rope_base, q_pos=P - back, pairs=[(int(b), int(i))])[0]
+    return out
+
+
 # ------------------------------------------------------------------ split merge
 
 

@@ -120,3 +120,37 @@ def test_lse_merge_without_max_shift_weights_is_caught(monkeypatch):
         return sum(np.asarray(o) for o, _ in parts) / len(parts)
     monkeypatch.setattr(omla, "lse_merge", bad)
     assert _fails(ta.test_lse_merge_of_any_partition_equals_unsplit, 1)
+
+
+def _multi_window_off_by_one(C, R, seq_start, seq_len, q_nope, q_rope, w_uk, w_uv, softmax_scale, rope_base,
+                             q_pos=None, triples=None, absorbed=False):
+    """Query j sees one row too many (the next new token)."""
+    B, Q = q_nope.shape[:2]
+    L = np.asarray(seq_len, dtype=np.int64)
+    P = L - 1 if q_pos is None else np.asarray(q_pos, dtype=np.int64)
+    out = np.zeros((B, Q, q_nope.shape[2], w_uv.shape[1]))
+    for j in range(Q):
+        back = max(Q - 2 - j, 0)
+        out[:, j] = omla.decode(C, R, seq_start, np.maximum(L - back, 0), q_nope[:, j], q_rope[:, j], w_uk, w_uv,
+                                softmax_scale, rope_base, q_pos=P - (Q - 1 - j))
+    return out
+
+
+def _multi_position_not_shifted(C, R, seq_start, seq_len, q_nope, q_rope, w_uk, w_uv, softmax_scale, rope_base,
+                                q_pos=None, triples=None, absorbed=False):
+    """Every query rotated at the last position instead of its own."""
+    B, Q = q_nope.shape[:2]
+    L = np.asarray(seq_len, dtype=np.int64)
+    out = np.zeros((B, Q, q_nope.shape[2], w_uv.shape[1]))
+    for j in range(Q):
+        back = Q - 1 - j
+        out[:, j] = omla.decode(C, R, seq_start, np.maximum(L - back, 0), q_nope[:, j], q_rope[:, j], w_uk, w_uv,
+                                softmax_scale, rope_base, q_pos=L - 1)
+    return out
+
+
+@pytest.mark.parametrize("bad", [_multi_window_off_by_one, _multi_position_not_shifted])
+def test_multi_query_mistakes_are_caught(monkeypatch, bad):
+    from tests import test_oracle_multi as tm
+    monkeypatch.setattr(omla, "decode_multi", bad)
+    assert _fails(tm.test_matches_masked_matrix_form)
