@@ -72,12 +72,13 @@ def measured_traffic(bytes_alg):
 DT = {"f32": 0, "bf16": 1, "fp8": 2}
 
 
-def run_workload(m, torch, name, steps, warmup):
+def run_workload(m, torch, name, steps, warmup, q_len=1):
     """Times `steps` decode steps of one workload (after `warmup` untimed ones).
     A step is one mla_decode call, or one mla_append_decode call for the
     workload that appends a token per sequence; that step also restores
     seq_len first (a 4-byte-per-sequence device copy) so every step appends
-    at the same place."""
+    at the same place. With q_len > 1 a step is one mla_decode_multi call:
+    q_len new query tokens per sequence (the last q_len cached rows)."""
     import mla_synth
     from mla_synth.device import upload
 
@@ -101,11 +102,18 @@ def run_workload(m, torch, name, steps, warmup):
                       None if scale is None else scale[j]) for j in range(ncopy)]
     plan = m.mla_plan_create(d, lens.tolist(), 0)
     nbytes = m.mla_decode_workspace_bytes(d, plan)
+    if q_len > 1:
+        import numpy as np
+        qn, qr = mla_synth.multi_queries(case, q_len, seed=17)
+        qn = torch.from_numpy(qn.view(np.int16)).to(dev)
+        qr = torch.from_numpy(qr.view(np.int16)).to(dev)
+        nbytes = m.mla_decode_multi_workspace_bytes(d, plan, q_len)
     if case.n_new:
         nbytes = max(nbytes, m.mla_append_workspace_bytes(d, case.B, case.n_new))
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     m.mla_workspace_init(ws)
-    o = torch.empty((case.B, case.H, case.d_v), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((case.B, q_len, case.H, case.d_v) if q_len > 1 else (case.B, case.H, case.d_v),
+                    dtype=torch.bfloat16, device=dev)
     len0 = t["seq_len"].clone()
     act = DT[case.act_dtype]
 
@@ -115,6 +123,8 @@ def run_workload(m, torch, name, steps, warmup):
             t["seq_len"].copy_(len0)
             m.mla_append_decode(d, caches[j], plan, t["h"], case.n_new, t["w_dkv"], t["w_kr"], t["q_nope"],
                                 t["q_rope"], None, wuk[j], wuv[j], act, o, 1, ws)
+        elif q_len > 1:
+            m.mla_decode_multi(d, caches[j], plan, q_len, qn, qr, None, wuk[j], wuv[j], act, o, 1, ws)
         else:
             m.mla_decode(d, caches[j], plan, t["q_nope"], t["q_rope"], None, wuk[j], wuv[j], act, o, 1, ws)
 
@@ -148,17 +158,17 @@ def run_workload(m, torch, name, steps, warmup):
     splitk_ms = kms / kn
     return dict(case=case, t=t, o=o, d=d, plan=plan, cache_bytes=cache_bytes, ms_step=ms_step,
                 ms_step_profiled=ms_step_profiled, splitk_ms=splitk_ms, splitk_name=kname,
-                prof={k: v[0] / v[1] for k, v in prof.items()}, n_items=plan.n_items, ncopy=ncopy)
+                prof={k: v[0] / v[1] for k, v in prof.items()}, n_items=plan.n_items, ncopy=ncopy, q_len=q_len)
 
 
 def workload_summary(res):
     """One line per extra workload: step and split-K rates, per-kernel times."""
-    case = res["case"]
-    flops = 2.0 * case.H * (2 * case.d_c + case.d_rope) * float((case.lens + case.n_new).sum())
-    return {"batch": case.B, "cache_tokens": int((case.lens + case.n_new).sum()),
+    case, ql = res["case"], res["q_len"]
+    flops = 2.0 * case.H * ql * (2 * case.d_c + case.d_rope) * float((case.lens + case.n_new).sum())
+    return {"batch": case.B, "query_tokens_per_seq": ql, "cache_tokens": int((case.lens + case.n_new).sum()),
             "latent_dtype": case.latent_dtype, "appends": int(case.n_new),
             "ms_per_step": round(res["ms_step"], 5),
-            "tokens_per_s": round(case.B / (res["ms_step"] * 1e-3), 1),
+            "tokens_per_s": round(case.B * ql / (res["ms_step"] * 1e-3), 1),
             "cache_GBs_step": round(res["cache_bytes"] / (res["ms_step"] * 1e-3) / 1e9, 2),
             "splitk_GBs": round(res["cache_bytes"] / (res["splitk_ms"] * 1e-3) / 1e9, 2),
             "splitk_hbm_frac": round(res["cache_bytes"] / (res["splitk_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -273,9 +283,10 @@ def main():
     }
     if a.extra:
         out["other_workloads"] = {}
-        for name in ("v3_b32_8k", "v3_b1_4k", "v3_b4_128k", "v3_b128_fp8"):
-            r = run_workload(m, torch, name, a.steps, a.warmup)
-            out["other_workloads"][name] = workload_summary(r)
+        for name, ql in (("v3_b32_8k", 1), ("v3_b1_4k", 1), ("v3_b4_128k", 1), ("v3_b128_fp8", 1),
+                         ("v3_b32_ragged", 4)):
+            r = run_workload(m, torch, name, a.steps, a.warmup, q_len=ql)
+            out["other_workloads"][name if ql == 1 else f"{name}_{ql}_query_tokens"] = workload_summary(r)
             del r
             torch.cuda.empty_cache()
     if not a.no_cpu_baseline:

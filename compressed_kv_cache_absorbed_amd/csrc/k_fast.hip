@@ -87,7 +87,7 @@ namespace {
 // so the transposed reads below are conflict-free) and read transposed as the
 // A operand of q~^T = W_UK,i^T q_nope^T; wave w owns columns 32 w of the
 // quarter. The quarter also rotates RoPE pairs 8 cq .. 8 cq + 7 of q_rope.
-__global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qscale, float rope_base,
+__global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, int q_len, float qscale, float rope_base,
                                                           const uint16_t *__restrict__ q_nope,
                                                           const uint16_t *__restrict__ q_rope,
                                                           const int32_t *__restrict__ q_pos,
@@ -97,7 +97,9 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qs
   using namespace fast;
   constexpr int WROW = 288;  // LDS bytes per W row (128 columns = 256 bytes + 32)
   __shared__ __attribute__((aligned(16))) char smem[DNOPE * WROW];
+  // head i of H = q_len * Hr: (new token j, head i % Hr), token-major
   const int i = blockIdx.x, cq = blockIdx.y, b0 = blockIdx.z * 32;
+  const int iw = i % Hr, back = q_len - 1 - i / Hr;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   // every global load first, in the order of use: the RoPE inputs, the
   // q_nope fragments, the weight quarter (32 KB: 128 rows x 16 chunks of
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qs
   int64_t P = 0;
   uint32_t xr = 0;
   if (rb < B) {
-    P = q_pos ? q_pos[rb] : static_cast<int64_t>(seqs[rb].len) - 1;
+    P = (q_pos ? q_pos[rb] : static_cast<int64_t>(seqs[rb].len) - 1) - back;
     xr = *reinterpret_cast<const uint32_t *>(q_rope + (static_cast<size_t>(rb) * H + i) * DR + 2 * rp);
   }
   // B operand: q_nope^T [16 n x 32 b]: lane holds sequence b0 + l%32, n = 16 kk + 8(l/32) .. +7
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, float qs
       qb[kk] = bf16x8{};
     }
   }
-  const uint16_t *W = w_uk + static_cast<size_t>(i) * DNOPE * DC + 128 * cq;
+  const uint16_t *W = w_uk + static_cast<size_t>(iw) * DNOPE * DC + 128 * cq;
   u32x4 wv[8];
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
@@ -246,7 +248,7 @@ struct RowBatch {
   }
 };
 template <int NB>
-__global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int G, const SeqInfo *__restrict__ seqs,
+__global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr, int G, const SeqInfo *__restrict__ seqs,
                                                            const int32_t *__restrict__ dev_len,
                                                            const uint16_t *__restrict__ opart,
                                                            const float *__restrict__ lse,
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int G, 
   // rows 16 w .. 16 w + 15 of W_UV,i, whole: lane l holds columns 8 l .. 8 l + 7
   u32x4 wr[16];
   {
-    const uint16_t *wrow = w_uv + (static_cast<size_t>(i) * DV + 16 * w) * DC + 8 * lane;
+    const uint16_t *wrow = w_uv + (static_cast<size_t>(i % Hr) * DV + 16 * w) * DC + 8 * lane;
 #pragma unroll
     for (int x = 0; x < 16; ++x) wr[x] = *reinterpret_cast<const u32x4 *>(wrow + x * DC);
   }
@@ -520,17 +522,18 @@ hipError_t launch_append_finish(hipStream_t s, const mla_dims &d, const mla_cach
   return launch_advance_len(s, c, n_new);
 }
 
-hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, const void *q_nope,
+hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, int32_t q_len, const void *q_nope,
                               const void *q_rope, const int32_t *q_pos, const void *w_uk,
                               const SeqInfo *seqs, uint16_t *q_out) {
-  return launch_kernel(absorb_fast_kernel, dim3(d.n_heads, fast::DC / 128, (batch + 31) / 32), 256, 0, s, batch,
-                       d.n_heads, d.softmax_scale * kLog2e, d.rope_base, static_cast<const uint16_t *>(q_nope),
+  const int H = d.n_heads * q_len;
+  return launch_kernel(absorb_fast_kernel, dim3(H, fast::DC / 128, (batch + 31) / 32), 256, 0, s, batch, H,
+                       d.n_heads, q_len, d.softmax_scale * kLog2e, d.rope_base, static_cast<const uint16_t *>(q_nope),
                        static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seqs, q_out);
 }
 
-hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const SeqInfo *seqs,
+hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, const SeqInfo *seqs,
                                const uint16_t *opart, const float *lse, const uint16_t *w_uv, void *o, int o_bf16) {
-  const int B = c.batch, H = d.n_heads;
+  const int B = c.batch, H = d.n_heads * q_len;
   if (B == 0) return hipSuccess;
   // the largest group (up to the 16 columns of one product) that still
   // gives a workgroup to every compute unit
@@ -540,7 +543,7 @@ hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache
   const dim3 grid(H * G);
 #define MLA_COMBINE(NBV)                                                                                      \
   case NBV:                                                                                                  \
-    return launch_kernel(combine_fast_kernel<NBV>, grid, 512, 0, s, B, H, G, seqs, c.seq_len, opart, lse, w_uv, \
+    return launch_kernel(combine_fast_kernel<NBV>, grid, 512, 0, s, B, H, d.n_heads, G, seqs, c.seq_len, opart, lse, w_uv, \
                          o, o_bf16)
   switch (nb) {
     MLA_COMBINE(1);

@@ -160,6 +160,7 @@ struct Item {
   const float *scale;
   int64_t stride, row0;
   int t0, t1, ntiles;
+  int tvis;  // this wave's queries see tokens < tvis (t1, or less for an earlier one of several new tokens)
 };
 
 // Where tile `tile` of an item starts in global memory, and its last valid
@@ -421,7 +422,7 @@ __device__ __forceinline__ f16x8 score_frag(const ScoreBase &sb, int kk) {
 // P stays in registers (fp16 pairs, rows 2 j and 2 j + 1 in P[j]) for the
 // value products of the same wave.
 struct Softmax {
-  float m4[4], mx, m_new, alpha, psum, pe, prev;
+  float m4[4], mx, m_new, m_sub, alpha, psum, pe, prev;
   uint32_t xs[2];
   uint32_t P[8];
 };
@@ -449,12 +450,15 @@ __device__ __forceinline__ void softmax_piece(WaveState &st, Softmax &sm, const 
   } else if (kk == 5) {
     sm.mx = fmaxf(__uint_as_float(sm.xs[0]), __uint_as_float(sm.xs[1]));
   } else if (kk == 6) {
+    // (a row whose tokens are all masked so far keeps m = -inf: alpha 1 and
+    // exponents taken against 0, so every p is exactly 0)
     sm.m_new = sm.mx > st.m + SLACK ? sm.mx : st.m;
-    sm.alpha = __builtin_amdgcn_exp2f(st.m - sm.m_new);
+    sm.alpha = sm.m_new == st.m ? 1.0f : __builtin_amdgcn_exp2f(st.m - sm.m_new);
+    sm.m_sub = sm.m_new == -INFINITY ? 0.0f : sm.m_new;
     sm.psum = 0.0f;
   } else if (kk < 23) {
     const int r = kk - 7;
-    const float p = __builtin_amdgcn_exp2f(S[r] - sm.m_new);
+    const float p = __builtin_amdgcn_exp2f(S[r] - sm.m_sub);
     if (r > 0) softmax_consume(sm, r - 1);
     sm.prev = p;
   } else if (kk == 23) {
@@ -682,8 +686,8 @@ __device__ __forceinline__ void step(WaveState &st, f32x16 &S, const Item &it, i
   StepHide<FP8, I>::init(h, tile_src(it, i + 3), w, lane, tid);
   f32x16 Sv = S;
   asm volatile("" : "+v"(Sv));
-  const int valid = min(sk::T, it.t1 - (it.t0 + i * sk::T));
-  if (valid < sk::T) {  // the item's last tile only (a real branch: the asm cannot be speculated)
+  const int valid = min(sk::T, it.tvis - (it.t0 + i * sk::T));
+  if (valid < sk::T) {  // the last tile(s) only (a real branch: the asm cannot be speculated)
     asm volatile("; tail mask");
     const int lim = valid - 4 * (opaque(st.lane) >> 5);  // one register, not 16 hoisted row indices
 #pragma unroll
@@ -706,7 +710,7 @@ __device__ __forceinline__ void step(WaveState &st, f32x16 &S, const Item &it, i
 }
 
 template <bool FP8>
-__global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
+__global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H, int Hr, int q_len, int n_items,
                                                         const WorkItem *__restrict__ items,
                                                         const SeqInfo *__restrict__ seqs,
                                                         const uint16_t *__restrict__ Q,
@@ -714,24 +718,39 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
                                                         float *__restrict__ lse,
                                                         int32_t *__restrict__ status) {
   using namespace sk;
-  // item k: workgroup L runs on XCD L % 8; the items of one sequence are
-  // consecutive, so giving each XCD a contiguous block of items lets the
-  // splits of a sequence share its absorbed query in that XCD's L2
-  const int n = gridDim.x, nfull = n & ~7, L = blockIdx.x;
-  const int k = L < nfull ? (L & 7) * (nfull >> 3) + (L >> 3) : L;
+  // item k, head block y (of Y = H / 128): workgroup L runs on XCD L % 8;
+  // the items of one sequence are consecutive, so giving each XCD a
+  // contiguous block of items lets the splits of a sequence share its
+  // absorbed query in that XCD's L2, and the head blocks of one item, next
+  // to each other there, share its cache tiles
+  const int Y = H >> 7, nfull = n_items & ~7, lfull = nfull * Y, L = blockIdx.x;
+  int k, y;
+  if (L < lfull) {
+    const int sl = L >> 3;
+    k = (L & 7) * (nfull >> 3) + sl / Y;
+    y = sl - (sl / Y) * Y;
+  } else {
+    const int r = L - lfull;
+    k = nfull + r / Y;
+    y = r - (r / Y) * Y;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
-  const int head = blockIdx.y * 128 + 32 * w + (lane & 31);
+  const int head = y * 128 + 32 * w + (lane & 31);
+  // with several new query tokens per sequence the heads are (token j,
+  // head) pairs, token-major: this wave's 32 all belong to token
+  // jq = (y * 128 + 32 w) / Hr, which sees the rows before len - (q_len - 1 - jq)
+  const int jq = (y * 128 + 32 * w) / Hr;
   const WorkItem wi = items[k];
   // this workgroup's 128 heads of item k: 128 rows of 512 fp16 partials
-  uint16_t *ob = opart + (static_cast<size_t>(k) * H + blockIdx.y * 128) * DC;
+  uint16_t *ob = opart + (static_cast<size_t>(k) * H + y * 128) * DC;
 
   const bool ok = c.seq_len[wi.b] == seqs[wi.b].len && wi.t0 >= 0 && wi.t0 < wi.t1 &&
                   wi.t1 <= c.seq_cap[wi.b] && static_cast<int64_t>(c.seq_start[wi.b]) >= 0 &&
                   static_cast<int64_t>(c.seq_start[wi.b]) + wi.t1 <= c.n_rows;
   if (!ok) {
-    if (tid == 0 && blockIdx.y == 0) set_status(status, MLA_ERR_PLAN);
+    if (tid == 0 && y == 0) set_status(status, MLA_ERR_PLAN);
     for (int x = tid; x < 128 * DC / 8; x += 256) reinterpret_cast<u32x4 *>(ob)[x] = u32x4{0, 0, 0, 0};
     if (half == 0) lse[static_cast<size_t>(k) * H + head] = -INFINITY;
     return;
@@ -744,6 +763,7 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
   it.t0 = wi.t0;
   it.t1 = wi.t1;
   it.ntiles = (wi.t1 - wi.t0 + T - 1) / T;
+  it.tvis = min(wi.t1, seqs[wi.b].len - (q_len - 1 - jq));
 
   // prologue copies first, so they overlap the Q fetch (tiles past the end
   // re-read the last row, like the steps)
@@ -829,8 +849,10 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
   // every wave's copies have landed and every wave is past its last tile
   // read once all have reached the barrier, so the tile buffers are free.
   __builtin_amdgcn_s_barrier();
-  const float inv = 1.0f / st.l;
-  if (half == 0) lse[static_cast<size_t>(k) * H + head] = st.m + log2f(st.l);
+  // (a row that saw no token, possible with several new tokens, has l = 0:
+  // partial 0, log-sum-exp -inf)
+  const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+  if (half == 0) lse[static_cast<size_t>(k) * H + head] = st.l > 0.0f ? st.m + log2f(st.l) : -INFINITY;
   char *tb = g_lds + w * 32 * OROW;
 #pragma unroll
   for (int cb = 0; cb < DC / 32; ++cb) {
@@ -852,14 +874,17 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H,
 
 }  // namespace
 
-hipError_t launch_decode_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,
+hipError_t launch_decode_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, int32_t n_items,
                               const WorkItem *items, const SeqInfo *seqs, const uint16_t *q, uint16_t *opart,
                               float *lse, int32_t *status) {
   if (n_items == 0) return hipSuccess;
-  const dim3 grid(n_items, d.n_heads / 128);
+  const int H = d.n_heads * q_len;
+  const dim3 grid(n_items * (H / 128));
   if (c.latent_dtype == MLA_FP8_E4M3)
-    return launch_kernel(splitk_kernel<true>, grid, 256, 0, s, c, d.n_heads, items, seqs, q, opart, lse, status);
-  return launch_kernel(splitk_kernel<false>, grid, 256, 0, s, c, d.n_heads, items, seqs, q, opart, lse, status);
+    return launch_kernel(splitk_kernel<true>, grid, 256, 0, s, c, H, d.n_heads, q_len, n_items, items, seqs, q, opart,
+                         lse, status);
+  return launch_kernel(splitk_kernel<false>, grid, 256, 0, s, c, H, d.n_heads, q_len, n_items, items, seqs, q, opart,
+                       lse, status);
 }
 
 }  // namespace mla

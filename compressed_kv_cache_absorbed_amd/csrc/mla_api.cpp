@@ -141,7 +141,7 @@ void prof_after(hipStream_t, int kernel_id) {
   p.taken = false;
 }
 
-DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items) {
+DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items, int32_t q_len) {
   DecodeWs w;
   size_t off = kStatusBytes;
   // items and seq info are contiguous: one copy of the plan's host block
@@ -149,11 +149,12 @@ DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items) {
   w.seqs = off + sizeof(WorkItem) * n_items;
   off = align_up(w.seqs + sizeof(SeqInfo) * batch, 256);
   w.q = off;
-  off = align_up(off + sizeof(float) * batch * d.n_heads * (d.d_c + d.d_rope), 256);
+  const size_t hq = static_cast<size_t>(d.n_heads) * std::max(q_len, 1);
+  off = align_up(off + sizeof(float) * batch * hq * (d.d_c + d.d_rope), 256);
   w.opart = off;
-  off = align_up(off + sizeof(float) * static_cast<size_t>(std::max(n_items, 1)) * d.n_heads * d.d_c, 256);
+  off = align_up(off + sizeof(float) * static_cast<size_t>(std::max(n_items, 1)) * hq * d.d_c, 256);
   w.lse = off;
-  off = align_up(off + sizeof(float) * static_cast<size_t>(std::max(n_items, 1)) * d.n_heads, 256);
+  off = align_up(off + sizeof(float) * static_cast<size_t>(std::max(n_items, 1)) * hq, 256);
   w.total = off;
   return w;
 }
@@ -325,6 +326,11 @@ size_t mla_decode_workspace_bytes(const mla_dims *dims, const mla_plan *plan) {
   return decode_ws_layout(*dims, plan->batch, plan->n_items).total;
 }
 
+size_t mla_decode_multi_workspace_bytes(const mla_dims *dims, const mla_plan *plan, int32_t q_len) {
+  if (check_dims(dims, false, true) != MLA_OK || !plan || q_len < 1 || q_len > kMaxQueryTokens) return 0;
+  return decode_ws_layout(*dims, plan->batch, plan->n_items, q_len).total;
+}
+
 }  // extern "C"
 
 // The device copy of a plan's work list lives in the workspace. A decode
@@ -432,7 +438,7 @@ mla_status mla_append(const mla_dims *dims, const mla_cache *cache, const void *
 static mla_status validate_decode(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
                                   const void *q_nope, const void *q_rope, const void *w_uk,
                                   const void *w_uv, mla_dtype qw, const void *o, mla_dtype od,
-                                  void *ws, size_t ws_bytes) {
+                                  void *ws, size_t ws_bytes, int32_t q_len = 1) {
   mla_status st = check_dims(dims, false, true);
   if (st != MLA_OK) return st;
   st = check_cache(*dims, cache);
@@ -444,8 +450,10 @@ static mla_status validate_decode(const mla_dims *dims, const mla_cache *cache, 
   if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(w_uv) ||
       !aligned16(o) || !aligned16(ws))
     return MLA_ERR_INVALID_ARG;
-  if (ws_bytes < decode_ws_layout(*dims, plan->batch, plan->n_items).total) return MLA_ERR_WORKSPACE;
+  if (q_len < 1 || q_len > kMaxQueryTokens) return MLA_ERR_INVALID_ARG;
+  if (ws_bytes < decode_ws_layout(*dims, plan->batch, plan->n_items, q_len).total) return MLA_ERR_WORKSPACE;
   if (!decode_fast_path(*dims, *cache, qw)) {
+    if (q_len > 1) return MLA_ERR_UNSUPPORTED;
     if (dims->d_c > 1024) return MLA_ERR_UNSUPPORTED;
     if (sizeof(float) * (static_cast<size_t>(dims->d_c) + dims->d_rope + 260) > 64 * 1024 ||
         sizeof(float) * static_cast<size_t>(dims->d_nope) > 64 * 1024)
@@ -457,8 +465,8 @@ static mla_status validate_decode(const mla_dims *dims, const mla_cache *cache, 
 static mla_status do_decode(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
                             const void *q_nope, const void *q_rope, const int32_t *q_pos,
                             const void *w_uk, const void *w_uv, mla_dtype qw, void *o, mla_dtype od,
-                            void *ws, hipStream_t s) {
-  const DecodeWs w = decode_ws_layout(*dims, plan->batch, plan->n_items);
+                            void *ws, hipStream_t s, int32_t q_len = 1) {
+  const DecodeWs w = decode_ws_layout(*dims, plan->batch, plan->n_items, q_len);
   char *base = static_cast<char *>(ws);
   int32_t *status = reinterpret_cast<int32_t *>(base + w.status);
   WorkItem *items = reinterpret_cast<WorkItem *>(base + w.items);
@@ -474,11 +482,12 @@ static mla_status do_decode(const mla_dims *dims, const mla_cache *cache, const 
   if (decode_fast_path(*dims, *cache, qw)) {
     uint16_t *q = reinterpret_cast<uint16_t *>(base + w.q);
     MLA_LAUNCH(s, K_ABSORB_FAST,
-               launch_absorb_fast(s, *dims, plan->batch, q_nope, q_rope, q_pos, w_uk, seqs, q));
+               launch_absorb_fast(s, *dims, plan->batch, q_len, q_nope, q_rope, q_pos, w_uk, seqs, q));
     MLA_LAUNCH(s, cache->latent_dtype == MLA_FP8_E4M3 ? K_DECODE_FP8 : K_DECODE_BF16,
-               launch_decode_fast(s, *dims, *cache, plan->n_items, items, seqs, q, opart16, lse, status));
+               launch_decode_fast(s, *dims, *cache, q_len, plan->n_items, items, seqs, q, opart16, lse, status));
     MLA_LAUNCH(s, K_COMBINE_FAST,
-               launch_combine_fast(s, *dims, *cache, seqs, opart16, lse, static_cast<const uint16_t *>(w_uv), o, od));
+               launch_combine_fast(s, *dims, *cache, q_len, seqs, opart16, lse, static_cast<const uint16_t *>(w_uv),
+                                   o, od));
   } else {
     float *q = reinterpret_cast<float *>(base + w.q);
     MLA_LAUNCH(s, K_ABSORB_GENERIC,
@@ -500,6 +509,17 @@ mla_status mla_decode(const mla_dims *dims, const mla_cache *cache, const mla_pl
   if (st != MLA_OK) return st;
   return do_decode(dims, cache, plan, q_nope, q_rope, q_pos, w_uk, w_uv, q_w_dtype, o, o_dtype, ws,
                    static_cast<hipStream_t>(stream));
+}
+
+mla_status mla_decode_multi(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan, int32_t q_len,
+                            const void *q_nope, const void *q_rope, const int32_t *q_pos, const void *w_uk,
+                            const void *w_uv, mla_dtype q_w_dtype, void *o, mla_dtype o_dtype, void *ws,
+                            size_t ws_bytes, void *stream) {
+  mla_status st = validate_decode(dims, cache, plan, q_nope, q_rope, w_uk, w_uv, q_w_dtype, o, o_dtype,
+                                  ws, ws_bytes, q_len);
+  if (st != MLA_OK) return st;
+  return do_decode(dims, cache, plan, q_nope, q_rope, q_pos, w_uk, w_uv, q_w_dtype, o, o_dtype, ws,
+                   static_cast<hipStream_t>(stream), q_len);
 }
 
 mla_status mla_append_decode(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,

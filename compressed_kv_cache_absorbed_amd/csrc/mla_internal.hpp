@@ -17,6 +17,9 @@ namespace mla {
 // are multiples of it so every tile except a sequence's last is full.
 constexpr int kTile = 32;
 
+// Most new query tokens per sequence one mla_decode_multi call takes.
+constexpr int kMaxQueryTokens = 16;
+
 // Kernel ids for the optional event-based profiler.
 enum KernelId : int {
   K_INIT = 0,
@@ -79,7 +82,8 @@ struct DecodeWs {
   size_t lse = 0;     // f32 [n_items, H]
   size_t total = 0;
 };
-DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items);
+// q_len new query tokens per sequence multiply every per-head array.
+DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items, int32_t q_len = 1);
 
 struct AppendWs {
   size_t status = 0;
@@ -114,21 +118,23 @@ hipError_t launch_advance_len(hipStream_t s, const mla_cache &c, int32_t n_new);
 hipError_t launch_absorb_generic(hipStream_t s, const mla_dims &d, int32_t batch,
                                  const void *q_nope, const void *q_rope, const int32_t *q_pos,
                                  const void *w_uk, mla_dtype qw, const SeqInfo *seqs, float *q_out);
-hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch,
+// The matrix-core launchers take q_len new query tokens per sequence (1 for
+// a plain decode): heads become (token, head) pairs, token-major.
+hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, int32_t q_len,
                               const void *q_nope, const void *q_rope, const int32_t *q_pos,
                               const void *w_uk, const SeqInfo *seqs, uint16_t *q_out);
 
 hipError_t launch_decode_generic(hipStream_t s, const mla_dims &d, const mla_cache &c,
                                  int32_t n_items, const WorkItem *items, const SeqInfo *seqs,
                                  const float *q, float *opart, float *lse, int32_t *status);
-hipError_t launch_decode_fast(hipStream_t s, const mla_dims &d, const mla_cache &c,
+hipError_t launch_decode_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len,
                               int32_t n_items, const WorkItem *items, const SeqInfo *seqs,
                               const uint16_t *q, uint16_t *opart, float *lse, int32_t *status);
 
 hipError_t launch_combine_generic(hipStream_t s, const mla_dims &d, const mla_cache &c,
                                   const SeqInfo *seqs, const float *opart, const float *lse,
                                   const void *w_uv, mla_dtype qw, void *o, mla_dtype od);
-hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, const SeqInfo *seqs,
+hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, const SeqInfo *seqs,
                                const uint16_t *opart, const float *lse, const uint16_t *w_uv, void *o, int o_bf16);
 
 hipError_t launch_copy(hipStream_t s, void *dst, const void *src, size_t n16);

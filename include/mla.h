@@ -183,6 +183,29 @@ mla_status mla_decode(const mla_dims *dims, const mla_cache *cache, const mla_pl
                       const void *w_uk, const void *w_uv, mla_dtype q_w_dtype, void *o,
                       mla_dtype o_dtype, void *ws, size_t ws_bytes, void *stream);
 
+/* mla_decode_multi — q_len new query tokens per sequence (multi-token
+ * prediction, speculative verification: "Multi-head Latent Attention (MLA)
+ * și arhitectura DeepSeekMoE", "Concepte cheie și caracteristici"), causal
+ * among themselves. The q_len new tokens are the last q_len cached rows of
+ * each sequence (appended first). Query j (0 .. q_len-1) of sequence b sits
+ * at position P - (q_len - 1 - j), P = q_pos[b] if q_pos is not NULL, else
+ * L - 1, and attends over rows 0 .. L - 1 - (q_len - 1 - j) exactly as
+ * mla_decode does over 0 .. L - 1; a query that sees no row gives o = 0.
+ *   q_nope  [batch, q_len, n_heads, d_nope], bf16, unrotated q_rope
+ *   q_rope  [batch, q_len, n_heads, d_rope], bf16
+ *   o       [batch, q_len, n_heads, d_v], o_dtype (F32 or BF16)
+ *   ws      at least mla_decode_multi_workspace_bytes(dims, plan, q_len)
+ * 1 <= q_len <= 16 (MLA_ERR_INVALID_ARG otherwise). Matrix-core path only:
+ * arguments the fast path does not take (see mla_decode) return
+ * MLA_ERR_UNSUPPORTED when q_len > 1. q_len = 1 is mla_decode, bit for bit.
+ * The cache is read once for all q_len queries: the work per cached byte
+ * grows q_len times. */
+mla_status mla_decode_multi(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan, int32_t q_len,
+                            const void *q_nope, const void *q_rope, const int32_t *q_pos, const void *w_uk,
+                            const void *w_uv, mla_dtype q_w_dtype, void *o, mla_dtype o_dtype, void *ws,
+                            size_t ws_bytes, void *stream);
+size_t mla_decode_multi_workspace_bytes(const mla_dims *dims, const mla_plan *plan, int32_t q_len);
+
 /* mla_append_decode — mla_append of n_new tokens followed, in stream order,
  * by mla_decode. The plan must have been made from the lengths after the
  * append (old lengths + n_new). ws must satisfy both workspace sizes. */

@@ -237,6 +237,23 @@ def make_case(name="custom", *, H, d_c, d_rope, d_nope, d_v, B, lens,
                 n_new=n_new, h=st(h), w_dkv=st(w_dkv), w_kr=st(w_kr), extra=extra)
 
 
+def multi_queries(case, q_len, seed):
+    """Queries of q_len new tokens per sequence for a several-token decode:
+    q_nope [B, q_len, H, d_nope] and q_rope [B, q_len, H, d_rope], N(0, 1), in
+    the case's activation dtype. The last token's queries are the case's own,
+    the earlier ones come from ``seed``."""
+    rng = np.random.default_rng(seed)
+    B, H = case.B, case.H
+    shape_n, shape_r = (B, q_len, H, case.d_nope), (B, q_len, H, case.d_rope)
+    q_nope = np.empty(shape_n, dtype=case.q_nope.dtype)
+    q_rope = np.empty(shape_r, dtype=case.q_rope.dtype)
+    q_nope[:, :q_len - 1] = to_storage(_normal(rng, (B, q_len - 1, H, case.d_nope)), case.act_dtype)
+    q_rope[:, :q_len - 1] = to_storage(_normal(rng, (B, q_len - 1, H, case.d_rope)), case.act_dtype)
+    q_nope[:, q_len - 1] = case.q_nope
+    q_rope[:, q_len - 1] = case.q_rope
+    return q_nope, q_rope
+
+
 def workload(name, seed=None, **overrides):
     """Build one of the named workloads (see the module docstring)."""
     kw = dict(WORKLOADS[name])

@@ -65,6 +65,23 @@ class GpuRun:
                           self.t["w_uk"], self.t["w_uv"], DT[c.act_dtype], o, DT[o_dtype], ws)
         return o
 
+    def decode_multi(self, q_len, q_nope, q_rope, plan=None, q_pos=None, o_dtype="f32", n_workers=0):
+        """mla_decode_multi with host query arrays [B, q_len, H, *] (storage dtype)."""
+        c = self.case
+        plan = plan or self.plan(n_workers=n_workers)
+        need = self.m.mla_decode_multi_workspace_bytes(self.d, plan, q_len)
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.t["rows"].device)
+            self.m.mla_workspace_init(self.ws)
+        dev = self.t["rows"].device
+        qn = torch.from_numpy(np.ascontiguousarray(q_nope).view(np.int16)).to(dev)
+        qr = torch.from_numpy(np.ascontiguousarray(q_rope).view(np.int16)).to(dev)
+        o = torch.empty((c.B, q_len, c.H, c.d_v), dtype=torch.float32 if o_dtype == "f32" else torch.bfloat16,
+                        device=dev)
+        self.m.mla_decode_multi(self.d, self.cache, plan, q_len, qn, qr, q_pos, self.t["w_uk"], self.t["w_uv"],
+                                DT[c.act_dtype], o, DT[o_dtype], self.ws)
+        return o
+
     def append_decode(self, plan=None, o_dtype="f32"):
         c = self.case
         plan = plan or self.plan()
@@ -125,6 +142,17 @@ def oracle_decode(case, pairs=None, absorbed=False, with_append=True, q_pos=None
               act_to_f64(case.q_rope, case.act_dtype), act_to_f64(case.w_uk, case.act_dtype),
               act_to_f64(case.w_uv, case.act_dtype), case.softmax_scale, case.rope_base,
               q_pos=q_pos, pairs=pairs)
+
+
+def oracle_decode_multi(case, q_nope, q_rope, triples=None, absorbed=True, q_pos=None, C=None, R=None):
+    """Oracle output of a several-token decode (queries [B, q_len, H, *] in
+    storage dtype)."""
+    if C is None:
+        C, R = oracle_cache(case)
+    return omla.decode_multi(C, R, case.seq_start, case.lens.astype(np.int64), act_to_f64(q_nope, case.act_dtype),
+                             act_to_f64(q_rope, case.act_dtype), act_to_f64(case.w_uk, case.act_dtype),
+                             act_to_f64(case.w_uv, case.act_dtype), case.softmax_scale, case.rope_base,
+                             q_pos=q_pos, triples=triples, absorbed=absorbed)
 
 
 def rel_rms_err(got, ref):

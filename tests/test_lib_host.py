@@ -141,6 +141,26 @@ def test_validation_rejects_before_launch():
     assert lib.mla_append(ctypes.byref(da), ctypes.byref(c), P, 1, P, P, 2, P, wsa, None) == 1
     assert lib.mla_append(ctypes.byref(da), ctypes.byref(c), None, 1, P, P, 1, P, wsa, None) == 1
     assert lib.mla_append(ctypes.byref(da), ctypes.byref(c), P, 1, P, P, 1, P, 16, None) == 5
+    # several query tokens: 1 <= q_len <= 16, the matrix-core path only, a
+    # workspace sized for q_len
+    ws4 = m.mla_decode_multi_workspace_bytes(d, plan, 4)
+    assert ws4 > ws_need and m.mla_decode_multi_workspace_bytes(d, plan, 1) == ws_need
+    assert m.mla_decode_multi_workspace_bytes(d, plan, 0) == 0
+    assert m.mla_decode_multi_workspace_bytes(d, plan, 17) == 0
+
+    def decm(c, q_len, ws_bytes, dd=d, qw=1):
+        return lib.mla_decode_multi(ctypes.byref(dd), ctypes.byref(c), plan.handle, q_len, P, P, None, P, P, qw, P,
+                                    0, P, ws_bytes, None)
+
+    assert decm(_cache_struct(), 0, ws4) == 1
+    assert decm(_cache_struct(), 17, 1 << 40) == 1
+    assert decm(_cache_struct(), 4, ws4 - 1) == 5
+    assert decm(_cache_struct(), 4, ws4, qw=0) == 2                # fp32 weights: generic path, one token only
+    small = m.dims(4, 32, 8, 16, 16)
+    plan_s = m.mla_plan_create(small, [10, 20], 4)
+    c_s = _cache_struct(row_stride=256)
+    assert lib.mla_decode_multi(ctypes.byref(small), ctypes.byref(c_s), plan_s.handle, 2, P, P, None, P, P, 0, P, 0,
+                                P, 1 << 30, None) == 2
     # calibration copy and workspace init validate too
     assert lib.mla_calib_copy(P, P, 17, None) == 1
     assert lib.mla_workspace_init(None, 256, None) == 1
