@@ -49,7 +49,8 @@ class MlaCache(ctypes.Structure):
                 ("rows", ctypes.c_void_p), ("row_stride", ctypes.c_int64),
                 ("scale", ctypes.c_void_p), ("n_rows", ctypes.c_int64), ("batch", ctypes.c_int32),
                 ("seq_start", ctypes.c_void_p), ("seq_cap", ctypes.c_void_p),
-                ("seq_len", ctypes.c_void_p)]
+                ("seq_len", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("block_tokens", ctypes.c_int32), ("max_blocks", ctypes.c_int32)]
 
 
 _LIB = None
@@ -133,13 +134,18 @@ def dims(n_heads, d_c, d_rope, d_nope, d_v, d_model=0, softmax_scale=None, rope_
     return MlaDims(n_heads, d_c, d_rope, d_nope, d_v, d_model, softmax_scale, rope_base)
 
 
-def cache(rows, row_stride, latent_dtype, rope_dtype, seq_start, seq_cap, seq_len, scale=None):
+def cache(rows, row_stride, latent_dtype, rope_dtype, seq_start, seq_cap, seq_len, scale=None,
+          block_table=None, block_tokens=0):
     """Describe a cache held in torch tensors: rows is uint8 [n_rows, row_stride];
-    seq_* are int32 [batch]; scale is float32 [n_rows] for fp8 latents."""
+    seq_* are int32 [batch]; scale is float32 [n_rows] for fp8 latents. A paged
+    cache passes block_table, int32 [batch, max_blocks], and block_tokens (then
+    seq_start may be None)."""
+    batch = seq_cap.numel()
     c = MlaCache(latent_dtype, rope_dtype, _ptr(rows), row_stride, _ptr(scale),
-                 rows.numel() // row_stride, seq_start.numel(), _ptr(seq_start), _ptr(seq_cap),
-                 _ptr(seq_len))
-    c._keep = (rows, scale, seq_start, seq_cap, seq_len)
+                 rows.numel() // row_stride, batch, _ptr(seq_start), _ptr(seq_cap),
+                 _ptr(seq_len), _ptr(block_table), block_tokens,
+                 0 if block_table is None else block_table.shape[-1])
+    c._keep = (rows, scale, seq_start, seq_cap, seq_len, block_table)
     return c
 
 

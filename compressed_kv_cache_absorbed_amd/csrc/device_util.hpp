@@ -128,4 +128,28 @@ __device__ __forceinline__ void set_status(int32_t *status, int32_t code) {
   atomicCAS(status, 0, code);
 }
 
+// Token range [0, t1) of sequence b lies in the cache: within its reserved
+// tokens, and (contiguous) within the rows or (paged) within its block
+// table row.
+__device__ __forceinline__ bool seq_range_ok(const mla_cache &c, int b, int64_t t1) {
+  if (t1 > c.seq_cap[b]) return false;
+  if (c.block_table == nullptr)
+    return static_cast<int64_t>(c.seq_start[b]) >= 0 && static_cast<int64_t>(c.seq_start[b]) + t1 <= c.n_rows;
+  return t1 <= static_cast<int64_t>(c.max_blocks) * c.block_tokens;
+}
+
+// Row of token t of sequence b (t inside a range seq_range_ok accepted):
+// seq_start[b] + t, or through the block table. A block id outside the cache
+// sets bad and reads block 0 instead.
+__device__ __forceinline__ int64_t cache_row(const mla_cache &c, int b, int64_t t, bool &bad) {
+  if (c.block_table == nullptr) return static_cast<int64_t>(c.seq_start[b]) + t;
+  const int64_t bt = c.block_tokens;
+  int64_t blk = c.block_table[static_cast<int64_t>(b) * c.max_blocks + t / bt];
+  if (blk < 0 || (blk + 1) * bt > c.n_rows) {
+    bad = true;
+    blk = 0;
+  }
+  return blk * bt + t % bt;
+}
+
 }  // namespace mla

@@ -472,9 +472,14 @@ __global__ __launch_bounds__(256) void append_finish_kernel(mla_dims d, mla_cach
   const int N = d.d_c + d.d_rope;
   const int32_t len = c.seq_len[b];
   const int64_t pos = static_cast<int64_t>(len) + j;
-  const int64_t row = static_cast<int64_t>(c.seq_start[b]) + pos;
-  if (len < 0 || static_cast<int64_t>(len) + n_new > c.seq_cap[b] || row < 0 || row >= c.n_rows) {
+  if (len < 0 || !seq_range_ok(c, b, static_cast<int64_t>(len) + n_new)) {
     if (tid == 0 && j == 0) set_status(status, MLA_ERR_CAPACITY);
+    return;
+  }
+  bool bad = false;
+  const int64_t row = cache_row(c, b, pos, bad);
+  if (bad) {
+    if (tid == 0) set_status(status, MLA_ERR_PLAN);
     return;
   }
   for (int n = tid; n < N; n += 256) {

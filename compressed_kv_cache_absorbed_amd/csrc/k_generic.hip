@@ -35,9 +35,14 @@ __global__ __launch_bounds__(256) void append_generic_kernel(mla_dims d, mla_cac
   const int32_t len = c.seq_len[b];
   const int32_t cap = c.seq_cap[b];
   const int64_t pos = static_cast<int64_t>(len) + j;
-  const int64_t row = static_cast<int64_t>(c.seq_start[b]) + pos;
-  if (len < 0 || static_cast<int64_t>(len) + n_new > cap || row < 0 || row >= c.n_rows) {
+  if (len < 0 || static_cast<int64_t>(len) + n_new > cap || !seq_range_ok(c, b, static_cast<int64_t>(len) + n_new)) {
     if (tid == 0 && j == 0) set_status(status, MLA_ERR_CAPACITY);
+    return;
+  }
+  bool bad = false;
+  const int64_t row = cache_row(c, b, pos, bad);
+  if (bad) {
+    if (tid == 0) set_status(status, MLA_ERR_PLAN);
     return;
   }
 
@@ -107,9 +112,7 @@ __global__ __launch_bounds__(256) void absorb_generic_kernel(mla_dims d, const v
 // True when the device length agrees with the plan and the item's rows lie in
 // the sequence's reserved range and in the cache.
 __device__ __forceinline__ bool item_ok(const mla_cache &c, const WorkItem &it, const SeqInfo &si) {
-  return c.seq_len[it.b] == si.len && it.t0 >= 0 && it.t0 < it.t1 && it.t1 <= c.seq_cap[it.b] &&
-         static_cast<int64_t>(c.seq_start[it.b]) >= 0 &&
-         static_cast<int64_t>(c.seq_start[it.b]) + it.t1 <= c.n_rows;
+  return c.seq_len[it.b] == si.len && it.t0 >= 0 && it.t0 < it.t1 && seq_range_ok(c, it.b, it.t1);
 }
 
 __global__ __launch_bounds__(256) void decode_generic_kernel(mla_dims d, mla_cache c,
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(mla_dims d, mla_cac
   for (int x = tid; x < D; x += 256) qs[x] = qrow[x];
   __syncthreads();
 
-  const int64_t row0 = c.seq_start[it.b];
+  bool bad = false;
   const int lat_b = elem_bytes(c.latent_dtype);
   const bool fp8 = c.latent_dtype == MLA_FP8_E4M3;
   float m = -INFINITY, l = 0.0f;
@@ -145,10 +148,11 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(mla_dims d, mla_cac
     const int t = t0 + tid;
     float s = -INFINITY;
     if (t < it.t1) {
-      const char *rowp = static_cast<const char *>(c.rows) + (row0 + t) * c.row_stride;
+      const int64_t row = cache_row(c, it.b, t, bad);
+      const char *rowp = static_cast<const char *>(c.rows) + row * c.row_stride;
       float dot = 0.0f;
       for (int x = 0; x < d.d_c; ++x) dot = fmaf(qs[x], load_elem(rowp, x, c.latent_dtype), dot);
-      if (fp8) dot *= c.scale[row0 + t];
+      if (fp8) dot *= c.scale[row];
       const char *rp = rowp + static_cast<int64_t>(d.d_c) * lat_b;
       for (int x = 0; x < d.d_rope; ++x) dot = fmaf(qs[d.d_c + x], load_elem(rp, x, c.rope_dtype), dot);
       s = dot;
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(mla_dims d, mla_cac
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] *= alpha;
     for (int tt = 0; tt < nt; ++tt) {
-      const int64_t row = row0 + t0 + tt;
+      const int64_t row = cache_row(c, it.b, t0 + tt, bad);
       const char *rowp = static_cast<const char *>(c.rows) + row * c.row_stride;
       const float pt = fp8 ? ps[tt] * c.scale[row] : ps[tt];
 #pragma unroll
@@ -182,6 +186,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(mla_dims d, mla_cac
     if (cc < d.d_c) op[cc] = acc[r] * inv;
   }
   if (tid == 0) lse[static_cast<int64_t>(k) * H + i] = m + log2f(l);
+  if (bad && tid == 0) set_status(status, MLA_ERR_PLAN);  // a block id outside the cache: block 0 was read
 }
 
 __global__ __launch_bounds__(256) void combine_generic_kernel(mla_dims d, mla_cache c,

@@ -158,14 +158,18 @@ __device__ __forceinline__ void lds_dma4(const char *base, uint32_t voff, uint32
 struct Item {
   const char *rows;
   const float *scale;
+  const int32_t *blocks;  // paged cache: this sequence's block table row, else nullptr
   int64_t stride, row0;
+  int block_tokens, n_blocks;  // paged: rows per block, blocks in the cache
   int t0, t1, ntiles;
   int tvis;  // this wave's queries see tokens < tvis (t1, or less for an earlier one of several new tokens)
 };
 
 // Where tile `tile` of an item starts in global memory, and its last valid
 // token (tokens past it repeat that row: finite data, masked out of the
-// softmax).
+// softmax). A tile past the item's end reads the item's last tile instead
+// (its data is never scored). Tiles start at multiples of 32 tokens, so a
+// tile never straddles two blocks of a paged cache: one lookup per tile.
 struct TileSrc {
   const char *base;   // row of the tile's first token
   const char *sbase;  // fp8 scales
@@ -173,10 +177,16 @@ struct TileSrc {
   int tmax;
 };
 __device__ __forceinline__ TileSrc tile_src(const Item &it, int tile) {
-  const int ts = it.t0 + tile * sk::T;
+  const int ts = it.t0 + min(tile, it.ntiles - 1) * sk::T;
+  int64_t row = it.row0 + ts;
+  if (it.blocks != nullptr) {
+    // (ids outside the cache were reported when the item started; clamped here)
+    const int blk = min(max(it.blocks[ts / it.block_tokens], 0), it.n_blocks - 1);
+    row = static_cast<int64_t>(blk) * it.block_tokens + ts % it.block_tokens;
+  }
   TileSrc r;
-  r.base = it.rows + (it.row0 + ts) * it.stride;
-  r.sbase = reinterpret_cast<const char *>(it.scale + it.row0 + ts);
+  r.base = it.rows + row * it.stride;
+  r.sbase = reinterpret_cast<const char *>(it.scale + row);
   r.stride = it.stride;
   r.tmax = it.t1 - 1 - ts;
   return r;
@@ -746,9 +756,7 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H, int 
   // this workgroup's 128 heads of item k: 128 rows of 512 fp16 partials
   uint16_t *ob = opart + (static_cast<size_t>(k) * H + y * 128) * DC;
 
-  const bool ok = c.seq_len[wi.b] == seqs[wi.b].len && wi.t0 >= 0 && wi.t0 < wi.t1 &&
-                  wi.t1 <= c.seq_cap[wi.b] && static_cast<int64_t>(c.seq_start[wi.b]) >= 0 &&
-                  static_cast<int64_t>(c.seq_start[wi.b]) + wi.t1 <= c.n_rows;
+  const bool ok = c.seq_len[wi.b] == seqs[wi.b].len && wi.t0 >= 0 && wi.t0 < wi.t1 && seq_range_ok(c, wi.b, wi.t1);
   if (!ok) {
     if (tid == 0 && y == 0) set_status(status, MLA_ERR_PLAN);
     for (int x = tid; x < 128 * DC / 8; x += 256) reinterpret_cast<u32x4 *>(ob)[x] = u32x4{0, 0, 0, 0};
@@ -759,7 +767,18 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H, int 
   it.rows = static_cast<const char *>(c.rows);
   it.scale = c.scale;
   it.stride = c.row_stride;
-  it.row0 = c.seq_start[wi.b];
+  it.row0 = c.block_table == nullptr ? c.seq_start[wi.b] : 0;
+  it.blocks = c.block_table == nullptr ? nullptr : c.block_table + static_cast<int64_t>(wi.b) * c.max_blocks;
+  it.block_tokens = c.block_tokens;
+  it.n_blocks = c.block_table == nullptr ? 0 : static_cast<int>(c.n_rows / c.block_tokens);
+  if (it.blocks != nullptr && w == 0) {
+    // the item's block ids, checked once (one per lane)
+    const int nb = (wi.t1 - 1) / c.block_tokens - wi.t0 / c.block_tokens + 1;
+    for (int x = lane; x < nb; x += 64) {
+      const int blk = it.blocks[wi.t0 / c.block_tokens + x];
+      if (blk < 0 || blk >= it.n_blocks) set_status(status, MLA_ERR_PLAN);
+    }
+  }
   it.t0 = wi.t0;
   it.t1 = wi.t1;
   it.ntiles = (wi.t1 - wi.t0 + T - 1) / T;

@@ -38,7 +38,14 @@ mla_status check_dims(const mla_dims *d, bool need_model, bool need_heads) {
 }
 
 mla_status check_cache(const mla_dims &d, const mla_cache *c) {
-  if (!c || !c->rows || !c->seq_start || !c->seq_cap || !c->seq_len) return MLA_ERR_INVALID_ARG;
+  if (!c || !c->rows || !c->seq_cap || !c->seq_len) return MLA_ERR_INVALID_ARG;
+  if (c->block_table) {
+    // paged: blocks of a multiple of 32 rows (one split-K tile never spans two)
+    if (c->block_tokens < kTile || c->block_tokens % kTile || c->max_blocks < 1 || c->n_rows < c->block_tokens)
+      return MLA_ERR_INVALID_ARG;
+  } else if (!c->seq_start) {
+    return MLA_ERR_INVALID_ARG;
+  }
   if (c->batch < 1 || c->n_rows < 1) return MLA_ERR_INVALID_ARG;
   if (!is_dtype(c->latent_dtype) || (c->rope_dtype != MLA_F32 && c->rope_dtype != MLA_BF16))
     return MLA_ERR_INVALID_ARG;

@@ -77,14 +77,24 @@ typedef struct {
   float softmax_scale, rope_base;
 } mla_dims;
 
-/* A ragged, contiguous-per-sequence latent cache.
+/* A ragged latent cache, contiguous per sequence or paged.
  * Row r is rows + r * row_stride: [c_kv: d_c elements of latent_dtype |
  * k_rope: d_rope elements of rope_dtype], packed from byte 0; the rest of
- * the stride is padding the library never reads or writes. Sequence b owns
- * rows seq_start[b] .. seq_start[b] + seq_cap[b] - 1, of which the first
- * seq_len[b] are valid. k_rope is stored already rotated at its own
- * position. For MLA_FP8_E4M3 latents, scale[r] (fp32) multiplies row r's
- * latent codes; scale is NULL otherwise. */
+ * the stride is padding the library never reads or writes. k_rope is stored
+ * already rotated at its own position. For MLA_FP8_E4M3 latents, scale[r]
+ * (fp32) multiplies row r's latent codes; scale is NULL otherwise.
+ * Contiguous (block_table NULL): sequence b's token t is row seq_start[b] + t,
+ * for t < seq_cap[b].
+ * Paged (block_table not NULL): the rows form blocks of block_tokens rows
+ * (a multiple of 32); sequence b's token t is row
+ *     block_table[b * max_blocks + t / block_tokens] * block_tokens
+ *         + t % block_tokens,
+ * for t < seq_cap[b] <= max_blocks * block_tokens; seq_start is not read and
+ * may be NULL. A block id outside [0, n_rows / block_tokens) is a device
+ * error (MLA_ERR_PLAN): the access is clamped to block 0 and the status word
+ * set. (Block tables are not on the pages: the layout serving engines use,
+ * orthogonal to what MLA stores per token.)
+ * Either way the first seq_len[b] tokens are valid. */
 typedef struct {
   mla_dtype latent_dtype; /* F32, BF16 or FP8_E4M3 */
   mla_dtype rope_dtype;   /* F32 or BF16 */
@@ -93,9 +103,12 @@ typedef struct {
   float *scale;           /* [n_rows] for FP8 latents, else NULL         */
   int64_t n_rows;
   int32_t batch;
-  const int32_t *seq_start; /* [batch] first row of each sequence */
-  const int32_t *seq_cap;   /* [batch] rows reserved per sequence  */
-  int32_t *seq_len;         /* [batch] valid rows; mla_append adds */
+  const int32_t *seq_start; /* [batch] first row of each sequence (contiguous) */
+  const int32_t *seq_cap;   /* [batch] tokens reserved per sequence             */
+  int32_t *seq_len;         /* [batch] valid tokens; mla_append adds            */
+  const int32_t *block_table; /* NULL, or [batch, max_blocks] block ids (paged) */
+  int32_t block_tokens;       /* rows per block, multiple of 32 (paged), else 0 */
+  int32_t max_blocks;         /* entries per sequence in block_table            */
 } mla_cache;
 
 /* Host-side split plan for decode (opaque). */

@@ -24,16 +24,57 @@ def case_dims(m, case):
                   case.softmax_scale, case.rope_base)
 
 
-class GpuRun:
-    """Holds the device tensors of one case and runs the C-ABI entry points."""
+def paged_layout(case, block_tokens, seed, spare_blocks=3):
+    """The case's cache rearranged into blocks of block_tokens rows in a
+    shuffled order: returns (rows, scale, block_table) with rows [n_blocks *
+    block_tokens, row_stride] (unused blocks filled with 0xAB bytes), scale
+    likewise (or None), block_table int32 [B, max_blocks] (-1 past a
+    sequence's blocks). Token t of sequence b moves from row seq_start[b] + t
+    to row block_table[b, t // bt] * bt + t % bt."""
+    rng = np.random.default_rng(seed)
+    bt = block_tokens
+    nblk = [(int(c) + bt - 1) // bt for c in case.seq_cap]
+    total = sum(nblk) + spare_blocks
+    max_blocks = max(max(nblk), 1)
+    ids = rng.permutation(total).astype(np.int32)
+    table = np.full((case.B, max_blocks), -1, dtype=np.int32)
+    rows = np.full((total * bt, case.row_stride), 0xAB, dtype=np.uint8)
+    scale = None if case.scale is None else np.full(total * bt, 7.0, dtype=np.float32)
+    k = 0
+    for b in range(case.B):
+        for j in range(nblk[b]):
+            blk = int(ids[k])
+            k += 1
+            table[b, j] = blk
+            n = min(bt, int(case.seq_cap[b]) - j * bt)
+            src = int(case.seq_start[b]) + j * bt
+            rows[blk * bt:blk * bt + n] = case.rows[src:src + n]
+            if scale is not None:
+                scale[blk * bt:blk * bt + n] = case.scale[src:src + n]
+    return rows, scale, table
 
-    def __init__(self, m, case, device="cuda"):
+
+class GpuRun:
+    """Holds the device tensors of one case and runs the C-ABI entry points.
+    ``paged`` = (rows, scale, block_table, block_tokens) from paged_layout()
+    runs the same case on a paged copy of its cache."""
+
+    def __init__(self, m, case, device="cuda", paged=None):
         self.m, self.case = m, case
         self.t = upload(case, device)
         self.d = case_dims(m, case)
-        self.cache = m.cache(self.t["rows"], case.row_stride, DT[case.latent_dtype],
-                             DT[case.rope_dtype], self.t["seq_start"], self.t["seq_cap"],
-                             self.t["seq_len"], self.t["scale"])
+        if paged is None:
+            self.cache = m.cache(self.t["rows"], case.row_stride, DT[case.latent_dtype],
+                                 DT[case.rope_dtype], self.t["seq_start"], self.t["seq_cap"],
+                                 self.t["seq_len"], self.t["scale"])
+        else:
+            rows, scale, table, bt = paged
+            self.t["rows"] = torch.from_numpy(rows).to(device)
+            self.t["scale"] = None if scale is None else torch.from_numpy(scale).to(device)
+            self.t["block_table"] = torch.from_numpy(table).to(device)
+            self.cache = m.cache(self.t["rows"], case.row_stride, DT[case.latent_dtype],
+                                 DT[case.rope_dtype], None, self.t["seq_cap"], self.t["seq_len"],
+                                 self.t["scale"], block_table=self.t["block_table"], block_tokens=bt)
         self.ws = None
 
     def plan(self, lens=None, n_workers=0):

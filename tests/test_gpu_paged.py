@@ -1,0 +1,93 @@
+"""GPU tests of the paged latent cache (block table, blocks of a multiple of
+32 rows): decode, several-token decode and append on a shuffled paged copy
+of a case give bit-for-bit the results of the contiguous cache (the kernels
+see the same rows, only their addresses move), on the matrix-core and the
+generic path; a block id outside the cache is reported, not followed."""
+import numpy as np
+import pytest
+import torch
+
+import mla_synth
+from tests.helpers import GpuRun, TOL_F32_ABS, make, max_abs_err, oracle_decode, paged_layout, to_np
+
+pytestmark = pytest.mark.gpu
+
+V3 = dict(H=128, d_c=512, d_rope=64, d_nope=128, d_v=128)
+LENS = [1, 31, 32, 33, 100, 700, 0, 64, 200]
+
+
+def v3_case(latent, seed, lens=LENS, **kw):
+    return make(B=len(lens), lens=("list", lens), latent_dtype=latent, rope_dtype="bf16", act_dtype="bf16",
+                seed=seed, **V3, **kw)
+
+
+@pytest.mark.parametrize("latent,bt", [("bf16", 64), ("fp8", 32), ("bf16", 128)])
+def test_paged_decode_matches_contiguous(gpu, latent, bt):
+    case = v3_case(latent, 100)
+    flat = GpuRun(gpu, case)
+    paged = GpuRun(gpu, case, paged=paged_layout(case, bt, seed=bt) + (bt,))
+    plan = flat.plan(n_workers=20)
+    a = flat.decode(plan=plan)
+    b = paged.decode(plan=plan)
+    assert flat.status() == 0 and paged.status() == 0
+    assert torch.equal(a, b)
+
+
+def test_paged_multi_token_decode_matches_contiguous(gpu):
+    case = v3_case("bf16", 101)
+    qn, qr = mla_synth.multi_queries(case, 3, seed=4)
+    flat = GpuRun(gpu, case)
+    paged = GpuRun(gpu, case, paged=paged_layout(case, 64, seed=5) + (64,))
+    plan = flat.plan(n_workers=16)
+    assert torch.equal(flat.decode_multi(3, qn, qr, plan=plan), paged.decode_multi(3, qn, qr, plan=plan))
+    assert flat.status() == 0 and paged.status() == 0
+
+
+def test_paged_generic_path_fp32(gpu):
+    case = make(B=3, lens=("list", [5, 64, 130]), latent_dtype="f32", rope_dtype="f32", act_dtype="f32", seed=102,
+                H=4, d_c=32, d_rope=8, d_nope=16, d_v=16)
+    flat = GpuRun(gpu, case)
+    paged = GpuRun(gpu, case, paged=paged_layout(case, 32, seed=6) + (32,))
+    plan = flat.plan(n_workers=5)
+    a, b = flat.decode(plan=plan), paged.decode(plan=plan)
+    assert flat.status() == 0 and paged.status() == 0
+    assert torch.equal(a, b)
+    assert max_abs_err(to_np(b), oracle_decode(case)) <= TOL_F32_ABS
+
+
+@pytest.mark.parametrize("latent", ["bf16", "fp8"])
+def test_paged_append_then_decode_matches_contiguous(gpu, latent):
+    lens = [3, 40, 63, 64, 500]
+    case = make(B=len(lens), lens=("list", lens), latent_dtype=latent, rope_dtype="bf16", act_dtype="bf16",
+                seed=103, n_new=1, d_model=1024, extra_cap=30, **V3)
+    flat = GpuRun(gpu, case)
+    bt = 32
+    layout = paged_layout(case, bt, seed=7)
+    paged = GpuRun(gpu, case, paged=layout + (bt,))
+    plan = flat.plan()
+    a = flat.append_decode(plan=plan)
+    b = paged.append_decode(plan=plan)
+    assert flat.status() == 0 and paged.status() == 0
+    assert torch.equal(a, b)
+    # the appended rows sit where the block table maps them, byte for byte
+    rows_f = flat.t["rows"].cpu().numpy()
+    rows_p = paged.t["rows"].cpu().numpy()
+    table = layout[2]
+    for bi, L in enumerate(lens):
+        t = L  # the new token's position
+        src = int(case.seq_start[bi]) + t
+        dst = int(table[bi, t // bt]) * bt + t % bt
+        np.testing.assert_array_equal(rows_p[dst], rows_f[src])
+        if latent == "fp8":
+            assert flat.t["scale"][src].item() == paged.t["scale"][dst].item()
+    assert np.all(flat.t["seq_len"].cpu().numpy() == np.array(lens) + 1)
+    assert np.all(paged.t["seq_len"].cpu().numpy() == np.array(lens) + 1)
+
+
+def test_paged_bad_block_id_is_reported(gpu):
+    case = v3_case("bf16", 104, lens=[100, 300])
+    rows, scale, table, = paged_layout(case, 64, seed=8)
+    table[1, 2] = 1 << 20  # outside the cache
+    paged = GpuRun(gpu, case, paged=(rows, scale, table, 64))
+    paged.decode(n_workers=4)
+    assert paged.status() == 6  # MLA_ERR_PLAN

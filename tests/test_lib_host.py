@@ -161,6 +161,12 @@ def test_validation_rejects_before_launch():
     c_s = _cache_struct(row_stride=256)
     assert lib.mla_decode_multi(ctypes.byref(small), ctypes.byref(c_s), plan_s.handle, 2, P, P, None, P, P, 0, P, 0,
                                 P, 1 << 30, None) == 2
+    # paged caches: blocks of a multiple of 32 rows, a table of at least one
+    # block per sequence; seq_start may then be NULL (and is required otherwise)
+    assert dec(_cache_struct(seq_start=None)) == 1
+    assert dec(_cache_struct(seq_start=None, block_table=P, block_tokens=48, max_blocks=4)) == 1
+    assert dec(_cache_struct(seq_start=None, block_table=P, block_tokens=64, max_blocks=0)) == 1
+    assert dec(_cache_struct(seq_start=None, block_table=P, block_tokens=0, max_blocks=4)) == 1
     # calibration copy and workspace init validate too
     assert lib.mla_calib_copy(P, P, 17, None) == 1
     assert lib.mla_workspace_init(None, 256, None) == 1
