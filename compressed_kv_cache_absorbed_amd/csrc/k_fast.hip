@@ -439,12 +439,21 @@ __global__ __launch_bounds__(64) void append_gemm_kernel(int T, int d_c, int d_m
   const uint16_t *arow = h + static_cast<size_t>(m) * d_model + k0;
   const uint16_t *brow = (n < d_c ? w_dkv + static_cast<size_t>(n) * d_model
                                   : w_kr + static_cast<size_t>(n - d_c) * d_model) + k0;
+  // two batches of 16 k-steps, every load of a batch issued before its
+  // products (a lone wave per tile: the loads' latency, not the matrix core,
+  // bounds it)
   f32x16 acc = {};
-#pragma unroll 8
-  for (int kk = 0; kk < APPEND_KS / 16; ++kk) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(arow + 16 * kk);
-    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(brow + 16 * kk);
-    acc = mfma32(a, b, acc);
+#pragma unroll
+  for (int k0 = 0; k0 < APPEND_KS / 16; k0 += 16) {
+    bf16x8 a[16], b[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      a[u] = *reinterpret_cast<const bf16x8 *>(arow + 16 * (k0 + u));
+      b[u] = *reinterpret_cast<const bf16x8 *>(brow + 16 * (k0 + u));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc = mfma32(a[u], b[u], acc);
   }
   // D: lane l, register r holds token m0 + 8(r/4) + 4(l/32) + r%4, output n
   float *out = partial + static_cast<size_t>(ks) * T * N;
@@ -482,9 +491,17 @@ __global__ __launch_bounds__(256) void append_finish_kernel(mla_dims d, mla_cach
     if (tid == 0) set_status(status, MLA_ERR_PLAN);
     return;
   }
+  // the K-split partials, up to 16 loads in flight per output
   for (int n = tid; n < N; n += 256) {
     float acc = 0.0f;
-    for (int ks = 0; ks < ksplit; ++ks) acc += partial[(static_cast<size_t>(ks) * T + t) * N + n];
+    for (int k0 = 0; k0 < ksplit; k0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        v[u] = k0 + u < ksplit ? partial[(static_cast<size_t>(k0 + u) * T + t) * N + n] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc += v[u];
+    }
     outv[n] = acc;
   }
   __syncthreads();
