@@ -229,3 +229,31 @@ def test_plan_copy_reuse_and_invalidation(gpu):
     o3 = to_np(run_a.decode(plan=plan_a))
     assert np.array_equal(o1, o3)
     check(case_a, o3, TOL_BF16_REL)
+
+
+def test_streams_and_separate_workspaces(gpu):
+    """Calls run on the stream they are given; two decodes with their own
+    workspaces on two streams at once give the default-stream result."""
+    case = v3_case([300, 1500, 64, 999], seed=57)
+    run = GpuRun(gpu, case)
+    plan = run.plan(n_workers=12)
+    ref = run.decode(plan=plan).clone()
+    assert run.status() == 0
+    m, t, c = gpu, run.t, case
+    need = m.mla_decode_workspace_bytes(run.d, plan)
+    outs, wss, streams = [], [], [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        m.mla_workspace_init(ws)
+        wss.append(ws)
+        outs.append(torch.empty((c.B, c.H, c.d_v), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for s, ws, o in zip(streams, wss, outs):
+            with torch.cuda.stream(s):
+                m.mla_decode(run.d, run.cache, plan, t["q_nope"], t["q_rope"], None, t["w_uk"], t["w_uv"],
+                             1, o, 0, ws, stream=s.cuda_stream)
+        torch.cuda.synchronize()
+        for ws, o in zip(wss, outs):
+            assert m.mla_device_error(ws, reset=True) == 0
+            assert torch.equal(o, ref)
