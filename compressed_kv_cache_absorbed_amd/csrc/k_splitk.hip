@@ -585,11 +585,11 @@ __device__ __forceinline__ void pv_rows(WaveState &st, const Softmax &sm, bool f
 
 // Work a step hides under its score products: score_step(kk) runs after
 // score product kk and issues at most one copy, one load or one
-// convert-and-store. Copies of a tile past the item's end re-read its last
-// row (in bounds, cached) into a buffer nobody reads any more, and widening
-// such a tile rewrites that dead buffer: branch-free steps let the compiler
-// count outstanding LDS operations exactly, so no wait drains the fragment
-// prefetch.
+// convert-and-store. Copies of a tile past the item's end re-read the item's
+// last tile (in bounds, cached) into a buffer nobody reads any more, and
+// widening such a tile rewrites that dead buffer: branch-free steps let the
+// compiler count outstanding LDS operations exactly, so no wait drains the
+// fragment prefetch.
 //
 // bf16 latents: the 9 copies of tile i+3 (one every fourth product, the
 // k_rope part at product 32) and the widening of this wave's rows of tile
@@ -785,7 +785,7 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H, int 
   it.tvis = min(wi.t1, seqs[wi.b].len - (q_len - 1 - jq));
 
   // prologue copies first, so they overlap the Q fetch (tiles past the end
-  // re-read the last row, like the steps)
+  // re-read the item's last tile, like the steps)
   if (FP8) {
     dma_raw<0>(it, 0, w, lane);
     dma_raw<1>(it, 1, w, lane);
