@@ -257,3 +257,26 @@ def test_streams_and_separate_workspaces(gpu):
         for ws, o in zip(wss, outs):
             assert m.mla_device_error(ws, reset=True) == 0
             assert torch.equal(o, ref)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
+def test_fast_random_shapes(gpu, seed):
+    """Seeded random batches: 1-12 sequences of 0-3000 tokens, a random worker
+    count for the plan, bf16 or fp8 latents, fp32 or bf16 output."""
+    rng = np.random.default_rng(500 + seed)
+    B = int(rng.integers(1, 13))
+    lens = [int(x) for x in rng.integers(0, 3000, size=B)]
+    lens[int(rng.integers(B))] = max(lens) + 1  # at least one non-empty sequence
+    latent = "fp8" if rng.random() < 0.4 else "bf16"
+    case = v3_case(lens, latent, seed=600 + seed)
+    run = GpuRun(gpu, case)
+    workers = int(rng.integers(1, 400))
+    o_dtype = "bf16" if rng.random() < 0.3 else "f32"
+    o = run.decode(n_workers=workers, o_dtype=o_dtype)
+    assert run.status() == 0
+    tol = TOL_FP8_REL if latent == "fp8" else TOL_BF16_REL
+    if o_dtype == "bf16":
+        o32 = run.decode(n_workers=workers)
+        assert torch.equal(o, o32.to(torch.bfloat16))
+        o = o32
+    check(case, to_np(o), tol, seed=seed)
