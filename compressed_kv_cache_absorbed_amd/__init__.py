@@ -15,7 +15,7 @@ __all__ = [
     "mla_decode_workspace_bytes", "mla_append", "mla_decode", "mla_append_decode",
     "mla_decode_multi", "mla_decode_multi_workspace_bytes",
     "mla_workspace_init", "mla_device_error", "mla_status_str", "mla_abi_version",
-    "mla_prof_begin", "mla_prof_end", "mla_calib_copy", "EXPORTED",
+    "mla_prof_begin", "mla_prof_end", "mla_calib_copy", "mla_calib_read", "EXPORTED",
 ]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
@@ -28,7 +28,7 @@ EXPORTED = [
     "mla_plan_num_items", "mla_plan_item", "mla_decode_workspace_bytes", "mla_decode",
     "mla_decode_multi_workspace_bytes", "mla_decode_multi", "mla_append_decode", "mla_workspace_init", "mla_device_error", "mla_status_str",
     "mla_abi_version", "mla_prof_begin", "mla_prof_end", "mla_prof_kernel_name",
-    "mla_prof_num_kernels", "mla_calib_copy",
+    "mla_prof_num_kernels", "mla_calib_copy", "mla_calib_read",
 ]
 
 
@@ -96,6 +96,7 @@ def load():
         "mla_prof_kernel_name": (ctypes.c_char_p, [ctypes.c_int32]),
         "mla_prof_num_kernels": (ctypes.c_int32, []),
         "mla_calib_copy": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+        "mla_calib_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -262,3 +263,7 @@ def mla_prof_end():
 
 def mla_calib_copy(dst, src, n_bytes, stream=None):
     _check(load().mla_calib_copy(_ptr(dst), _ptr(src), n_bytes, _stream(stream)), "mla_calib_copy")
+
+
+def mla_calib_read(src, n_bytes, sink, stream=None):
+    _check(load().mla_calib_read(_ptr(src), n_bytes, _ptr(sink), _stream(stream)), "mla_calib_read")

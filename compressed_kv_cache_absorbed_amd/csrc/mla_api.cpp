@@ -91,7 +91,8 @@ Profiler &prof() {
 const char *kKernelNames[K_COUNT] = {
     "init",           "append_generic", "append_gemm",    "append_finish",
     "absorb_generic", "absorb_fast",    "decode_generic", "decode_bf16",
-    "decode_fp8",     "combine_generic", "combine_fast",  "copy"};
+    "decode_fp8",     "combine_generic", "combine_fast",  "copy",
+    "read"};
 
 #define MLA_LAUNCH(stream, kid, call)          \
   do {                                         \
@@ -597,6 +598,15 @@ mla_status mla_calib_copy(void *dst, const void *src, size_t n_bytes, void *stre
   if (n_bytes == 0) return MLA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   MLA_LAUNCH(s, K_COPY, launch_copy(s, dst, src, n_bytes / 16));
+  return MLA_OK;
+}
+
+mla_status mla_calib_read(const void *src, size_t n_bytes, uint32_t *sink, void *stream) {
+  if (!src || !sink || (n_bytes & 15) || !aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3))
+    return MLA_ERR_INVALID_ARG;
+  if (n_bytes == 0) return MLA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MLA_LAUNCH(s, K_READ, launch_read(s, src, n_bytes / 16, sink));
   return MLA_OK;
 }
 

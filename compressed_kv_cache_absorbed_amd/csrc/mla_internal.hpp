@@ -34,6 +34,7 @@ enum KernelId : int {
   K_COMBINE_GENERIC,
   K_COMBINE_FAST,
   K_COPY,
+  K_READ,
   K_COUNT
 };
 
@@ -138,6 +139,7 @@ hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache
                                const uint16_t *opart, const float *lse, const uint16_t *w_uv, void *o, int o_bf16);
 
 hipError_t launch_copy(hipStream_t s, void *dst, const void *src, size_t n16);
+hipError_t launch_read(hipStream_t s, const void *src, size_t n16, uint32_t *sink);
 
 // Profiling hooks used by the launch wrappers in mla_api.cpp. While a
 // profiled call is pending, prof_take() hands its start/stop events to the

@@ -256,6 +256,16 @@ int32_t mla_prof_num_kernels(void);
  * n_bytes (multiple of 16) from src to dst. Not part of the method: it gives
  * hardware counters a kernel of known traffic to calibrate against. */
 mla_status mla_calib_copy(void *dst, const void *src, size_t n_bytes, void *stream);
+/* mla_calib_read — reads n_bytes (multiple of 16) of device memory at src
+ * (16-byte aligned) once, in 16-byte vector loads with several in flight per
+ * thread, and XORs all the 32-bit words read into the device word *sink
+ * (caller-owned, 4-byte aligned; atomic, one update per workgroup, so two
+ * calls on the same data restore it). Not part of the method: timed over a
+ * buffer larger than the on-package cache it is the achievable HBM read
+ * rate, the ceiling a read-bound kernel is compared with beside the vendor
+ * peak. Asynchronous on stream; MLA_ERR_INVALID_ARG for a null or misaligned
+ * pointer or a size not a multiple of 16. */
+mla_status mla_calib_read(const void *src, size_t n_bytes, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -174,3 +174,22 @@ def test_host_validation_before_any_launch(gpu):
         gpu.mla_decode(run.d, run.cache, plan, run.t["q_nope"], run.t["q_rope"], None,
                        run.t["w_uk"], run.t["w_uv"], 7, o, 0, ws)
     assert e.value.status == 1
+
+
+@pytest.mark.parametrize("n_bytes", [16, 4096 + 48, (1 << 20) + 16 * 7])
+def test_calib_read_folds_every_word(gpu, n_bytes):
+    """The stream-read ceiling kernel reads every word exactly once: its XOR
+    of the buffer equals the host's (sizes below, at and past the grid's
+    unrolled stride), and a second call restores the sink."""
+    import compressed_kv_cache_absorbed_amd as m
+    rng = np.random.default_rng(n_bytes)
+    host = rng.integers(0, 2**32, size=n_bytes // 4, dtype=np.uint32)
+    src = torch.from_numpy(host.view(np.int32).copy()).to("cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    m.mla_calib_read(src, n_bytes, sink)
+    torch.cuda.synchronize()
+    want = int(np.bitwise_xor.reduce(host))
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == want
+    m.mla_calib_read(src, n_bytes, sink)
+    torch.cuda.synchronize()
+    assert int(sink.cpu()[0]) == 0

@@ -169,6 +169,10 @@ def test_validation_rejects_before_launch():
     assert dec(_cache_struct(seq_start=None, block_table=P, block_tokens=0, max_blocks=4)) == 1
     # calibration copy and workspace init validate too
     assert lib.mla_calib_copy(P, P, 17, None) == 1
+    assert lib.mla_calib_read(P, 17, P, None) == 1
+    assert lib.mla_calib_read(None, 16, P, None) == 1
+    assert lib.mla_calib_read(P, 16, None, None) == 1
+    assert lib.mla_calib_read(P, 16, P + 2, None) == 1
     assert lib.mla_workspace_init(None, 256, None) == 1
 
 
