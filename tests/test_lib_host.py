@@ -182,3 +182,15 @@ def test_workspace_sizes_grow_with_plan():
     big = m.mla_decode_workspace_bytes(d, m.mla_plan_create(d, [100000] * 8, 256))
     assert 0 < small < big
     assert big >= 256 * 128 * 512 * 4  # fp32 partial per item and head
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libmla.so every entry point raises: there is no CPU fallback."""
+    monkeypatch.setattr(m, "_LIB", None)
+    monkeypatch.setattr(m, "lib_path", lambda: str(tmp_path / "libmla.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        m.load()
+    with pytest.raises(RuntimeError, match="not built"):
+        m.mla_abi_version()
+    with pytest.raises(RuntimeError, match="not built"):
+        m.mla_plan_create(d128(), [10, 20], 4)
