@@ -28,7 +28,7 @@ Sources:
   "Lo que MLA no es"; "Atención latente de múltiples cabezas", "Información
   técnica".
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent (the plainest one the rest supports):
 
 * The query token's own latent is appended first; the query sits at position
   P_b = L_b - 1 and attends to positions 0 .. L_b - 1 inclusive (``q_pos``

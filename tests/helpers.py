@@ -54,7 +54,7 @@ def paged_layout(case, block_tokens, seed, spare_blocks=3):
     return rows, scale, table
 
 
-class GpuRun:
+class DeviceRun:
     """Holds the device tensors of one case and runs the C-ABI entry points.
     ``paged`` = (rows, scale, block_table, block_tokens) from paged_layout()
     runs the same case on a paged copy of its cache."""

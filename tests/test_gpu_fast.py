@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests.helpers import (GpuRun, TOL_BF16_REL, TOL_FP8_REL, make, oracle_append, oracle_decode,
+from tests.helpers import (DeviceRun, TOL_BF16_REL, TOL_FP8_REL, make, oracle_append, oracle_decode,
                            rel_rms_err, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -42,7 +42,7 @@ def check(case, o, tol, n_def=6, seed=0):
 @pytest.mark.parametrize("latent", ["bf16", "fp8"])
 def test_fast_decode_edge_lengths(gpu, latent):
     case = v3_case(EDGE_LENS, latent, gap_rows=2)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     o = to_np(run.decode(n_workers=16))
     assert run.status() == 0
     check(case, o, TOL_FP8_REL if latent == "fp8" else TOL_BF16_REL)
@@ -52,7 +52,7 @@ def test_fast_decode_edge_lengths(gpu, latent):
 @pytest.mark.parametrize("latent", ["bf16", "fp8"])
 def test_fast_matches_generic_path(gpu, latent, monkeypatch):
     case = v3_case([77, 300, 1025], latent, seed=51)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     fast = to_np(run.decode(n_workers=8))
     monkeypatch.setenv("MLA_FORCE_GENERIC", "1")
     gen = to_np(run.decode(n_workers=8))
@@ -75,7 +75,7 @@ def test_fast_256_heads(gpu, latent):
     lens = [45, 300, 0, 97, 1024]
     case = make(B=len(lens), lens=("list", lens), latent_dtype=latent, rope_dtype="bf16", act_dtype="bf16",
                 seed=70, H=256, d_c=512, d_rope=64, d_nope=128, d_v=128)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     o = to_np(run.decode(n_workers=12))
     assert run.status() == 0
     check(case, o, TOL_FP8_REL if latent == "fp8" else TOL_BF16_REL)
@@ -92,7 +92,7 @@ def test_fast_combine_group_sizes(gpu, B, max_len, splits):
     rng = np.random.default_rng(1000 + B + max_len)
     lens = [int(x) for x in rng.integers(max_len // 2 if max_len > 1000 else 1, max_len, size=B)]
     case = v3_case(lens, seed=60 + B)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     o = to_np(run.decode(n_workers=splits * B + 3))
     assert run.status() == 0
     check(case, o, TOL_BF16_REL)
@@ -100,7 +100,7 @@ def test_fast_combine_group_sizes(gpu, B, max_len, splits):
 
 def test_fast_split_invariance_and_determinism(gpu):
     case = v3_case([2000, 513], seed=52)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     p1 = run.plan(n_workers=1)
     p64 = run.plan(n_workers=64)
     o1 = to_np(run.decode(plan=p1))
@@ -115,7 +115,7 @@ def test_fast_split_invariance_and_determinism(gpu):
 
 def test_fast_explicit_positions_and_bf16_output(gpu):
     case = v3_case([90, 257], seed=53)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     q_pos = np.array([5000, 3], dtype=np.int32)
     o = to_np(run.decode(q_pos=torch.from_numpy(q_pos).cuda(), o_dtype="bf16"))
     ref = oracle_decode(case, absorbed=True, q_pos=q_pos)
@@ -124,7 +124,7 @@ def test_fast_explicit_positions_and_bf16_output(gpu):
 
 def test_fast_plan_mismatch(gpu):
     case = v3_case([64, 40], seed=54)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     plan = run.plan(lens=[64, 41])
     o = to_np(run.decode(plan=plan))
     assert run.status() == 6
@@ -137,7 +137,7 @@ def test_fast_spiky_rows(gpu):
     """A few rows scaled x8 give peaked softmax rows (the long-context
     workload's structure at a small size)."""
     case = v3_case([3000, 1500], seed=55, spike_frac=0.01, spike_mult=8.0)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     o = to_np(run.decode())
     check(case, o, TOL_BF16_REL)
 
@@ -152,7 +152,7 @@ def test_fast_append_rows_and_canary(gpu, latent, monkeypatch):
     rope = "f32" if latent == "f32" else "bf16"
     case = make(B=5, lens=("list", [3, 0, 70001, 40, 31]), n_new=3, d_model=1024, extra_cap=1, gap_rows=2,
                 latent_dtype=latent, rope_dtype=rope, act_dtype="bf16", seed=56, **V3)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     valid = np.zeros(case.n_rows, dtype=bool)
     for b in range(case.B):
         valid[case.seq_start[b]:case.seq_start[b] + case.lens[b]] = True
@@ -193,7 +193,7 @@ def test_fast_append_rows_and_canary(gpu, latent, monkeypatch):
     tol_r = 2.0 ** -7 if rope == "bf16" else 1e-5
     assert np.all(np.abs(R - refR) <= np.abs(refR) * tol_r + 1e-6)
     # the generic append of the same tokens agrees within the same rounding
-    run2 = GpuRun(gpu, case)
+    run2 = DeviceRun(gpu, case)
     monkeypatch.setenv("MLA_FORCE_GENERIC", "1")
     run2.append()
     monkeypatch.delenv("MLA_FORCE_GENERIC")
@@ -212,8 +212,8 @@ def test_plan_copy_reuse_and_invalidation(gpu):
     case_a = v3_case([300, 77, 1025], seed=57)
     case_b = make(B=2, lens=("list", [5, 9]), n_new=2, d_model=512, latent_dtype="bf16", rope_dtype="bf16",
                   act_dtype="bf16", seed=58, **V3)
-    run_a = GpuRun(gpu, case_a)
-    run_b = GpuRun(gpu, case_b)
+    run_a = DeviceRun(gpu, case_a)
+    run_b = DeviceRun(gpu, case_b)
     plan_a = run_a.plan(n_workers=8)
     o1 = to_np(run_a.decode(plan=plan_a))
     o2 = to_np(run_a.decode(plan=plan_a))
@@ -235,7 +235,7 @@ def test_streams_and_separate_workspaces(gpu):
     """Calls run on the stream they are given; two decodes with their own
     workspaces on two streams at once give the default-stream result."""
     case = v3_case([300, 1500, 64, 999], seed=57)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     plan = run.plan(n_workers=12)
     ref = run.decode(plan=plan).clone()
     assert run.status() == 0
@@ -269,7 +269,7 @@ def test_fast_random_shapes(gpu, seed):
     lens[int(rng.integers(B))] = max(lens) + 1  # at least one non-empty sequence
     latent = "fp8" if rng.random() < 0.4 else "bf16"
     case = v3_case(lens, latent, seed=600 + seed)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     workers = int(rng.integers(1, 400))
     o_dtype = "bf16" if rng.random() < 0.3 else "f32"
     o = run.decode(n_workers=workers, o_dtype=o_dtype)

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import mla_synth
-from tests.helpers import (GpuRun, TOL_BF16_REL, TOL_F32_ABS, TOL_FP8_REL, max_abs_err, make,
+from tests.helpers import (DeviceRun, TOL_BF16_REL, TOL_F32_ABS, TOL_FP8_REL, max_abs_err, make,
                            oracle_append, oracle_decode, rel_rms_err, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -15,7 +15,7 @@ def test_tiny_f32_append_then_decode(gpu):
     """The tiny fp32 workload: 64 tokens appended from h (positions 0..63),
     then one decode step with q = W_Q h_63."""
     case = mla_synth.workload("tiny_f32")
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     run.append()
     assert run.status() == 0
     assert run.t["seq_len"].cpu().tolist() == [64]
@@ -39,7 +39,7 @@ def test_append_indexing_canary(gpu, latent):
     case = make(H=2, d_c=32, d_rope=8, d_nope=16, d_v=16, d_model=48, B=3,
                 lens=("list", [3, 0, 5]), n_new=4, extra_cap=2, gap_rows=3,
                 latent_dtype=latent, rope_dtype=rope, act_dtype="f32", seed=40)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     canary = torch.full_like(run.t["rows"], 0xA5)
     # keep the pre-existing valid rows, canary everywhere else
     valid = np.zeros(case.n_rows, dtype=bool)
@@ -90,7 +90,7 @@ def test_append_past_capacity_is_refused(gpu):
     case = make(H=2, d_c=32, d_rope=8, d_nope=16, d_v=16, d_model=32, B=2,
                 lens=("list", [5, 2]), n_new=3, latent_dtype="bf16", rope_dtype="bf16",
                 act_dtype="f32", seed=41)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     # shrink sequence 0's capacity so the append does not fit
     cap = case.seq_cap.copy()
     cap[0] = 6
@@ -111,7 +111,7 @@ def test_generic_decode_ragged(gpu, latent):
     case = make(H=4, d_c=48, d_rope=8, d_nope=16, d_v=24, B=6,
                 lens=("list", [1, 31, 32, 33, 300, 0]), gap_rows=1,
                 latent_dtype=latent, rope_dtype=rope, act_dtype=act, seed=42)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     o = to_np(run.decode(n_workers=16))
     assert run.status() == 0
     ref = oracle_decode(case)
@@ -126,7 +126,7 @@ def test_generic_decode_ragged(gpu, latent):
 def test_split_invariance_and_determinism(gpu):
     case = make(H=4, d_c=32, d_rope=8, d_nope=16, d_v=16, B=3, lens=("list", [700, 65, 1]),
                 latent_dtype="f32", rope_dtype="f32", act_dtype="f32", seed=43)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     p1 = run.plan(n_workers=1)
     p64 = run.plan(n_workers=64)
     assert p1.n_items == 3 and p64.n_items > 3
@@ -141,7 +141,7 @@ def test_split_invariance_and_determinism(gpu):
 def test_explicit_query_positions(gpu):
     case = make(H=2, d_c=32, d_rope=8, d_nope=16, d_v=16, B=2, lens=("list", [40, 9]),
                 latent_dtype="f32", rope_dtype="f32", act_dtype="f32", seed=44)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     q_pos = np.array([1000, 3], dtype=np.int32)
     o = to_np(run.decode(q_pos=torch.from_numpy(q_pos).cuda()))
     assert max_abs_err(o, oracle_decode(case, q_pos=q_pos)) <= TOL_F32_ABS
@@ -150,7 +150,7 @@ def test_explicit_query_positions(gpu):
 def test_plan_mismatch_is_reported_and_zeroed(gpu):
     case = make(H=2, d_c=32, d_rope=8, d_nope=16, d_v=16, B=2, lens=("list", [40, 9]),
                 latent_dtype="f32", rope_dtype="f32", act_dtype="f32", seed=45)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     plan = run.plan(lens=[40, 10])  # the device says 9
     o = to_np(run.decode(plan=plan))
     assert run.status() == 6  # MLA_ERR_PLAN
@@ -161,7 +161,7 @@ def test_plan_mismatch_is_reported_and_zeroed(gpu):
 def test_host_validation_before_any_launch(gpu):
     case = make(H=2, d_c=32, d_rope=8, d_nope=16, d_v=16, B=1, lens=("list", [4]),
                 latent_dtype="f32", rope_dtype="f32", act_dtype="f32", seed=46)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     plan = run.plan()
     ws = run.workspace(plan)
     o = torch.empty((1, 2, 16), device="cuda")

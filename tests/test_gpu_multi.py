@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import mla_synth
-from tests.helpers import (GpuRun, TOL_BF16_REL, TOL_FP8_REL, make, oracle_decode_multi, rel_rms_err, to_np)
+from tests.helpers import (DeviceRun, TOL_BF16_REL, TOL_FP8_REL, make, oracle_decode_multi, rel_rms_err, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +25,7 @@ def test_multi_edge_lengths(gpu, latent, q_len):
     lens = [1, 2, 3, 31, 33, 100, 700, 0, 64, 15]
     case = v3_case(lens, latent)
     qn, qr = mla_synth.multi_queries(case, q_len, seed=90 + q_len)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     o = to_np(run.decode_multi(q_len, qn, qr, n_workers=24))
     assert run.status() == 0
     ref = oracle_decode_multi(case, qn, qr)
@@ -48,7 +48,7 @@ def test_multi_edge_lengths(gpu, latent, q_len):
 def test_multi_one_token_is_decode(gpu):
     case = v3_case([5, 300, 77, 1025], seed=81)
     qn, qr = mla_synth.multi_queries(case, 1, seed=1)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     plan = run.plan(n_workers=9)
     single = to_np(run.decode(plan=plan))
     multi = to_np(run.decode_multi(1, qn, qr, plan=plan))
@@ -61,7 +61,7 @@ def test_multi_explicit_positions_bf16_output(gpu):
     case = v3_case(lens, seed=82)
     q_len = 4
     qn, qr = mla_synth.multi_queries(case, q_len, seed=3)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     pos = torch.from_numpy(np.array([1000, 7, 3], dtype=np.int32)).cuda()
     plan = run.plan(n_workers=6)
     o32 = run.decode_multi(q_len, qn, qr, plan=plan, q_pos=pos)
@@ -78,7 +78,7 @@ def test_multi_ragged_batch_sampled(gpu):
     case = mla_synth.workload("v3_b32_ragged")
     q_len = 4
     qn, qr = mla_synth.multi_queries(case, q_len, seed=5)
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     o = to_np(run.decode_multi(q_len, qn, qr))
     assert run.status() == 0
     rng = np.random.default_rng(7)

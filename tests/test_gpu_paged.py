@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import mla_synth
-from tests.helpers import GpuRun, TOL_F32_ABS, make, max_abs_err, oracle_decode, paged_layout, to_np
+from tests.helpers import DeviceRun, TOL_F32_ABS, make, max_abs_err, oracle_decode, paged_layout, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -24,8 +24,8 @@ def v3_case(latent, seed, lens=LENS, **kw):
 @pytest.mark.parametrize("latent,bt", [("bf16", 64), ("fp8", 32), ("bf16", 128)])
 def test_paged_decode_matches_contiguous(gpu, latent, bt):
     case = v3_case(latent, 100)
-    flat = GpuRun(gpu, case)
-    paged = GpuRun(gpu, case, paged=paged_layout(case, bt, seed=bt) + (bt,))
+    flat = DeviceRun(gpu, case)
+    paged = DeviceRun(gpu, case, paged=paged_layout(case, bt, seed=bt) + (bt,))
     plan = flat.plan(n_workers=20)
     a = flat.decode(plan=plan)
     b = paged.decode(plan=plan)
@@ -36,8 +36,8 @@ def test_paged_decode_matches_contiguous(gpu, latent, bt):
 def test_paged_multi_token_decode_matches_contiguous(gpu):
     case = v3_case("bf16", 101)
     qn, qr = mla_synth.multi_queries(case, 3, seed=4)
-    flat = GpuRun(gpu, case)
-    paged = GpuRun(gpu, case, paged=paged_layout(case, 64, seed=5) + (64,))
+    flat = DeviceRun(gpu, case)
+    paged = DeviceRun(gpu, case, paged=paged_layout(case, 64, seed=5) + (64,))
     plan = flat.plan(n_workers=16)
     assert torch.equal(flat.decode_multi(3, qn, qr, plan=plan), paged.decode_multi(3, qn, qr, plan=plan))
     assert flat.status() == 0 and paged.status() == 0
@@ -46,8 +46,8 @@ def test_paged_multi_token_decode_matches_contiguous(gpu):
 def test_paged_generic_path_fp32(gpu):
     case = make(B=3, lens=("list", [5, 64, 130]), latent_dtype="f32", rope_dtype="f32", act_dtype="f32", seed=102,
                 H=4, d_c=32, d_rope=8, d_nope=16, d_v=16)
-    flat = GpuRun(gpu, case)
-    paged = GpuRun(gpu, case, paged=paged_layout(case, 32, seed=6) + (32,))
+    flat = DeviceRun(gpu, case)
+    paged = DeviceRun(gpu, case, paged=paged_layout(case, 32, seed=6) + (32,))
     plan = flat.plan(n_workers=5)
     a, b = flat.decode(plan=plan), paged.decode(plan=plan)
     assert flat.status() == 0 and paged.status() == 0
@@ -60,10 +60,10 @@ def test_paged_append_then_decode_matches_contiguous(gpu, latent):
     lens = [3, 40, 63, 64, 500]
     case = make(B=len(lens), lens=("list", lens), latent_dtype=latent, rope_dtype="bf16", act_dtype="bf16",
                 seed=103, n_new=1, d_model=1024, extra_cap=30, **V3)
-    flat = GpuRun(gpu, case)
+    flat = DeviceRun(gpu, case)
     bt = 32
     layout = paged_layout(case, bt, seed=7)
-    paged = GpuRun(gpu, case, paged=layout + (bt,))
+    paged = DeviceRun(gpu, case, paged=layout + (bt,))
     plan = flat.plan()
     a = flat.append_decode(plan=plan)
     b = paged.append_decode(plan=plan)
@@ -88,6 +88,6 @@ def test_paged_bad_block_id_is_reported(gpu):
     case = v3_case("bf16", 104, lens=[100, 300])
     rows, scale, table, = paged_layout(case, 64, seed=8)
     table[1, 2] = 1 << 20  # outside the cache
-    paged = GpuRun(gpu, case, paged=(rows, scale, table, 64))
+    paged = DeviceRun(gpu, case, paged=(rows, scale, table, 64))
     paged.decode(n_workers=4)
     assert paged.status() == 6  # MLA_ERR_PLAN

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import mla_synth
-from tests.helpers import (GpuRun, TOL_BF16_REL, TOL_FP8_REL, oracle_append, oracle_cache, oracle_decode,
+from tests.helpers import (DeviceRun, TOL_BF16_REL, TOL_FP8_REL, oracle_append, oracle_cache, oracle_decode,
                            rel_rms_err, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -45,7 +45,7 @@ def test_workload_v3_b1_4k(gpu):
     """One sequence of 4096 tokens, H=128: every output against the absorbed
     oracle, two against the definition."""
     case = mla_synth.workload("v3_b1_4k")
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     o = to_np(run.decode(o_dtype="bf16"))
     assert run.status() == 0
     ref = oracle_decode(case, absorbed=True)
@@ -57,7 +57,7 @@ def test_workload_v3_b1_4k(gpu):
 def test_workload_v3_b32_ragged_bench_config(gpu):
     """The benchmark's workload and launch configuration."""
     case = mla_synth.workload("v3_b32_ragged")
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     o = to_np(run.decode(o_dtype="bf16"))
     assert run.status() == 0
     sampled_check(case, o, sample_pairs(case, 24, seed=1), TOL_BF16_REL, n_def=3)
@@ -65,7 +65,7 @@ def test_workload_v3_b32_ragged_bench_config(gpu):
 
 def test_workload_v3_b32_8k(gpu):
     case = mla_synth.workload("v3_b32_8k")
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     o = to_np(run.decode(o_dtype="bf16"))
     assert run.status() == 0
     sampled_check(case, o, sample_pairs(case, 12, seed=2), TOL_BF16_REL)
@@ -75,7 +75,7 @@ def test_workload_v3_b4_128k(gpu):
     """Four sequences of 131072 tokens with 1 % of rows scaled x8 (peaked
     softmax rows), split over many work items per sequence."""
     case = mla_synth.workload("v3_b4_128k")
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     o = to_np(run.decode(o_dtype="bf16"))
     assert run.status() == 0
     sampled_check(case, o, sample_pairs(case, 16, seed=3), TOL_BF16_REL)
@@ -88,7 +88,7 @@ def test_workload_v3_b128_fp8_append_decode(gpu):
     one fp8 step and scales within 1e-5 of the oracle's own append; the
     sampled outputs are compared end to end."""
     case = mla_synth.workload("v3_b128_fp8")
-    run = GpuRun(gpu, case)
+    run = DeviceRun(gpu, case)
     o = to_np(run.append_decode(o_dtype="bf16"))
     assert run.status() == 0
     assert np.array_equal(run.t["seq_len"].cpu().numpy(), case.lens + 1)
