@@ -248,7 +248,8 @@ struct RowBatch {
   }
 };
 template <int NB>
-__global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr, int G, const SeqInfo *__restrict__ seqs,
+__global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr, int G, int VH,
+                                                           const SeqInfo *__restrict__ seqs,
                                                            const int32_t *__restrict__ dev_len,
                                                            const uint16_t *__restrict__ opart,
                                                            const float *__restrict__ lse,
@@ -266,9 +267,17 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
   __shared__ __attribute__((aligned(16))) char sw[NW * 16 * WROW];
   __shared__ float red_m[NW], red_d[NW];
   __shared__ __attribute__((aligned(16))) float red_acc[R > 1 ? NW : 1][DC];
-  const int L = blockIdx.x, slot = L >> 3;
-  const int i = (L & 7) + 8 * (slot / G), b0 = (slot % G) * NB;
+  // workgroup L: head i (on XCD L % 8, with every group of that head),
+  // sequences b0 .. b0 + NB - 1, output rows vh * DV / VH .. +DV / VH - 1
+  // (VH = 2 only when a workgroup per (head, group) leaves compute units
+  // idle: the weight rows are then split between two workgroups, and wave
+  // w < 8 / VH takes rows 16 w .. 16 w + 15 of that half)
+  const int L = blockIdx.x, slot = L >> 3, per_head = G * VH;
+  const int i = (L & 7) + 8 * (slot / per_head), g = (slot % per_head) / VH, vh = slot % VH;
+  const int b0 = g * NB;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool wact = 16 * w < DV / VH;  // this wave has weight rows
+  const int vrow = vh * (DV / VH) + 16 * w;
 
   const int bl = tid / TPB, q = tid % TPB;
   const int b = b0 + bl;
@@ -292,10 +301,10 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
   RowBatch<NL, SB, R> rb;
   if (r < S) rb.issue(r, S, src, stride, lcol, H);
 
-  // rows 16 w .. 16 w + 15 of W_UV,i, whole: lane l holds columns 8 l .. 8 l + 7
+  // rows vrow .. vrow + 15 of W_UV,i, whole: lane l holds columns 8 l .. 8 l + 7
   u32x4 wr[16];
-  {
-    const uint16_t *wrow = w_uv + (static_cast<size_t>(i % Hr) * DV + 16 * w) * DC + 8 * lane;
+  if (wact) {
+    const uint16_t *wrow = w_uv + (static_cast<size_t>(i % Hr) * DV + vrow) * DC + 8 * lane;
 #pragma unroll
     for (int x = 0; x < 16; ++x) wr[x] = *reinterpret_cast<const u32x4 *>(wrow + x * DC);
   }
@@ -344,7 +353,7 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
   // W_UV rows into the A layout: k-half h, k-step kk = 8 h + t: lane l
   // takes row l%16, columns 256 h + 32 t + 8(l/16) .. +7
   bf16x8 wa[DC / 32];
-  {
+  if (wact) {
     char *sww = sw + w * 16 * WROW;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -396,15 +405,17 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
 
   // 3. o = W_UV,i o^
   f32x4 d = {};
-  const char *bp = so + (lane & 15) * OROW + 16 * (lane >> 4);
+  if (wact) {
+    const char *bp = so + (lane & 15) * OROW + 16 * (lane >> 4);
 #pragma unroll
-  for (int kk = 0; kk < DC / 32; ++kk) {
-    d = mfma16(wa[kk], *reinterpret_cast<const bf16x8 *>(bp + 64 * kk), d);
-    d = mfma16(wa[kk], *reinterpret_cast<const bf16x8 *>(bp + 64 * kk + 16 * OROW), d);
+    for (int kk = 0; kk < DC / 32; ++kk) {
+      d = mfma16(wa[kk], *reinterpret_cast<const bf16x8 *>(bp + 64 * kk), d);
+      d = mfma16(wa[kk], *reinterpret_cast<const bf16x8 *>(bp + 64 * kk + 16 * OROW), d);
+    }
   }
   const int bo = b0 + (lane & 15);
-  if ((lane & 15) < NB && bo < B) {
-    const size_t base = (static_cast<size_t>(bo) * H + i) * DV + 16 * w + 4 * (lane >> 4);
+  if (wact && (lane & 15) < NB && bo < B) {
+    const size_t base = (static_cast<size_t>(bo) * H + i) * DV + vrow + 4 * (lane >> 4);
     if (o_bf16) {
       bf16x4 v;
 #pragma unroll
@@ -562,11 +573,14 @@ hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache
   int nb = 1;
   while (nb < 16 && static_cast<int64_t>(H) * ((B + 2 * nb - 1) / (2 * nb)) >= 256) nb *= 2;
   const int G = (B + nb - 1) / nb;
-  const dim3 grid(H * G);
+  // still fewer workgroups than compute units (one sequence): split each
+  // head's weight rows over two workgroups
+  const int VH = static_cast<int64_t>(H) * G < 256 ? 2 : 1;
+  const dim3 grid(H * G * VH);
 #define MLA_COMBINE(NBV)                                                                                      \
   case NBV:                                                                                                  \
-    return launch_kernel(combine_fast_kernel<NBV>, grid, 512, 0, s, B, H, d.n_heads, G, seqs, c.seq_len, opart, lse, w_uv, \
-                         o, o_bf16)
+    return launch_kernel(combine_fast_kernel<NBV>, grid, 512, 0, s, B, H, d.n_heads, G, VH, seqs, c.seq_len, opart, lse, \
+                         w_uv, o, o_bf16)
   switch (nb) {
     MLA_COMBINE(1);
     MLA_COMBINE(2);
