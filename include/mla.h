@@ -186,10 +186,13 @@ mla_status mla_plan_item(const mla_plan *plan, int32_t k, int32_t *b, int32_t *t
  *   o       [batch, n_heads, d_v], o_dtype (F32 or BF16)
  *   ws      at least mla_decode_workspace_bytes(dims, plan) bytes
  * The device checks seq_len[b] against the plan (MLA_ERR_PLAN). Arithmetic:
- * fp32 accumulation throughout; the bf16 fast path (d_c = 512, d_rope = 64,
- * n_heads % 32 == 0, bf16 q/weights, bf16 or fp8 latents, bf16 k_rope)
- * feeds bf16 operands to the matrix cores; every other shape runs fp32
- * kernels. */
+ * fp32 accumulation throughout. The matrix-core path (d_c = 512,
+ * d_rope = 64, d_nope = d_v = 128, n_heads a multiple of 128, bf16 q and
+ * weights, bf16 or fp8 latents, bf16 k_rope) rounds q~ and the softmax
+ * weights to fp16 and widens the cached values to fp16 (exact for every e4m3
+ * value and for bf16 values up to 65504 in magnitude) for the matrix cores;
+ * the merged latent output enters the W_UV product as a bf16 hi + lo pair.
+ * Every other shape runs fp32 kernels. */
 size_t mla_decode_workspace_bytes(const mla_dims *dims, const mla_plan *plan);
 mla_status mla_decode(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
                       const void *q_nope, const void *q_rope, const int32_t *q_pos,
@@ -204,8 +207,8 @@ mla_status mla_decode(const mla_dims *dims, const mla_cache *cache, const mla_pl
  * at position P - (q_len - 1 - j), P = q_pos[b] if q_pos is not NULL, else
  * L - 1, and attends over rows 0 .. L - 1 - (q_len - 1 - j) exactly as
  * mla_decode does over 0 .. L - 1; a query that sees no row gives o = 0.
- *   q_nope  [batch, q_len, n_heads, d_nope], bf16, unrotated q_rope
- *   q_rope  [batch, q_len, n_heads, d_rope], bf16
+ *   q_nope  [batch, q_len, n_heads, d_nope], bf16
+ *   q_rope  [batch, q_len, n_heads, d_rope], bf16, unrotated
  *   o       [batch, q_len, n_heads, d_v], o_dtype (F32 or BF16)
  *   ws      at least mla_decode_multi_workspace_bytes(dims, plan, q_len)
  * 1 <= q_len <= 16 (MLA_ERR_INVALID_ARG otherwise). Matrix-core path only:
