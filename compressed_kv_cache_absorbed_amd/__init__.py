@@ -12,7 +12,7 @@ import os
 __all__ = [
     "F32", "BF16", "FP8_E4M3", "MLAError", "MlaDims", "MlaCache", "Plan", "load", "lib_path",
     "dims", "cache", "mla_plan_create", "mla_append_workspace_bytes",
-    "mla_decode_workspace_bytes", "mla_append", "mla_decode", "mla_append_decode",
+    "mla_decode_workspace_bytes", "mla_workspace_bytes", "mla_append", "mla_decode", "mla_append_decode",
     "mla_decode_multi", "mla_decode_multi_workspace_bytes",
     "mla_workspace_init", "mla_device_error", "mla_status_str", "mla_abi_version",
     "mla_prof_begin", "mla_prof_end", "mla_calib_copy", "mla_calib_read", "EXPORTED",
@@ -25,7 +25,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "M
 # Every extern "C" entry point of include/mla.h.
 EXPORTED = [
     "mla_append_workspace_bytes", "mla_append", "mla_plan_create", "mla_plan_destroy",
-    "mla_plan_num_items", "mla_plan_item", "mla_decode_workspace_bytes", "mla_decode",
+    "mla_plan_num_items", "mla_plan_item", "mla_decode_workspace_bytes", "mla_workspace_bytes", "mla_decode",
     "mla_decode_multi_workspace_bytes", "mla_decode_multi", "mla_append_decode", "mla_workspace_init", "mla_device_error", "mla_status_str",
     "mla_abi_version", "mla_prof_begin", "mla_prof_end", "mla_prof_kernel_name",
     "mla_prof_num_kernels", "mla_calib_copy", "mla_calib_read",
@@ -79,6 +79,7 @@ def load():
         "mla_plan_num_items": (ctypes.c_int32, [_P]),
         "mla_plan_item": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, _P]),
         "mla_decode_workspace_bytes": (ctypes.c_size_t, [_P, _P]),
+        "mla_workspace_bytes": (ctypes.c_size_t, [_P, _P]),
         "mla_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
                                       ctypes.c_int, _P, ctypes.c_size_t, _P]),
         "mla_decode_multi_workspace_bytes": (ctypes.c_size_t, [_P, _P, ctypes.c_int32]),
@@ -192,6 +193,10 @@ def mla_append_workspace_bytes(d, batch, n_new):
 
 def mla_decode_workspace_bytes(d, plan):
     return load().mla_decode_workspace_bytes(ctypes.byref(d), plan.handle)
+
+
+def mla_workspace_bytes(d, plan):
+    return load().mla_workspace_bytes(ctypes.byref(d), plan.handle)
 
 
 def mla_append(d, c, h, n_new, w_dkv, w_kr, act_w_dtype, ws, stream=None):

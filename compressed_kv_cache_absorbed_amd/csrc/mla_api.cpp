@@ -334,6 +334,13 @@ size_t mla_decode_workspace_bytes(const mla_dims *dims, const mla_plan *plan) {
   return decode_ws_layout(*dims, plan->batch, plan->n_items).total;
 }
 
+size_t mla_workspace_bytes(const mla_dims *dims, const mla_plan *plan) {
+  const size_t dec = mla_decode_workspace_bytes(dims, plan);
+  if (dec == 0 || dims->d_model < 1) return dec;
+  const size_t app = mla_append_workspace_bytes(dims, plan->batch, 1);
+  return app > dec ? app : dec;
+}
+
 size_t mla_decode_multi_workspace_bytes(const mla_dims *dims, const mla_plan *plan, int32_t q_len) {
   if (check_dims(dims, false, true) != MLA_OK || !plan || q_len < 1 || q_len > kMaxQueryTokens) return 0;
   return decode_ws_layout(*dims, plan->batch, plan->n_items, q_len).total;

@@ -194,6 +194,14 @@ mla_status mla_plan_item(const mla_plan *plan, int32_t k, int32_t *b, int32_t *t
  * the merged latent output enters the W_UV product as a bf16 hi + lo pair.
  * Every other shape runs fp32 kernels. */
 size_t mla_decode_workspace_bytes(const mla_dims *dims, const mla_plan *plan);
+/* mla_workspace_bytes — one size that serves every call on this plan with at
+ * most one new token per sequence: mla_decode, and, when dims->d_model > 0,
+ * mla_append and mla_append_decode with n_new = 1 (the append a decode step
+ * makes): the larger of mla_decode_workspace_bytes(dims, plan) and
+ * mla_append_workspace_bytes(dims, plan's batch, 1). Longer appends and
+ * several query tokens size theirs with the specific functions. 0 for
+ * invalid dims or a NULL plan. */
+size_t mla_workspace_bytes(const mla_dims *dims, const mla_plan *plan);
 mla_status mla_decode(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
                       const void *q_nope, const void *q_rope, const int32_t *q_pos,
                       const void *w_uk, const void *w_uv, mla_dtype q_w_dtype, void *o,

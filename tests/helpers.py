@@ -82,8 +82,9 @@ class DeviceRun:
         return self.m.mla_plan_create(self.d, lens, n_workers)
 
     def workspace(self, plan):
-        need = self.m.mla_decode_workspace_bytes(self.d, plan)
-        if self.case.n_new:
+        # one token per sequence or none: the one-size query covers decode and append
+        need = self.m.mla_workspace_bytes(self.d, plan)
+        if self.case.n_new > 1:
             need = max(need, self.m.mla_append_workspace_bytes(self.d, self.case.B, self.case.n_new))
         if self.ws is None or self.ws.numel() < need:
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.t["rows"].device)

@@ -184,6 +184,20 @@ def test_workspace_sizes_grow_with_plan():
     assert big >= 256 * 128 * 512 * 4  # fp32 partial per item and head
 
 
+def test_one_size_workspace_covers_decode_and_one_token_append():
+    d = d128()  # no d_model: decode only
+    plan = m.mla_plan_create(d, [100, 5000, 0], 16)
+    assert m.mla_workspace_bytes(d, plan) == m.mla_decode_workspace_bytes(d, plan)
+    dm = m.dims(128, 512, 64, 128, 128, d_model=7168)
+    for lens in ([100, 5000, 0], [1] * 300):
+        plan = m.mla_plan_create(dm, lens, 16)
+        one = m.mla_workspace_bytes(dm, plan)
+        assert one == max(m.mla_decode_workspace_bytes(dm, plan), m.mla_append_workspace_bytes(dm, len(lens), 1))
+    lib = m.load()
+    assert lib.mla_workspace_bytes(None, plan.handle) == 0
+    assert lib.mla_workspace_bytes(ctypes.byref(dm), None) == 0
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """Without libmla.so every entry point raises: there is no CPU fallback."""
     monkeypatch.setattr(m, "_LIB", None)
