@@ -16,6 +16,7 @@ __all__ = [
     "mla_decode_multi", "mla_decode_multi_workspace_bytes",
     "mla_workspace_init", "mla_device_error", "mla_status_str", "mla_abi_version",
     "mla_prof_begin", "mla_prof_end", "mla_calib_copy", "mla_calib_read", "EXPORTED",
+    "workspace", "decode", "append", "append_decode",
 ]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
@@ -272,3 +273,62 @@ def mla_calib_copy(dst, src, n_bytes, stream=None):
 
 def mla_calib_read(src, n_bytes, sink, stream=None):
     _check(load().mla_calib_read(_ptr(src), n_bytes, _ptr(sink), _stream(stream)), "mla_calib_read")
+
+
+# ------------------------------------------------------------------ tensor-level calls
+# The same entry points with the dtype codes read off the tensors, the output
+# (and, if not given, a workspace) allocated with torch on the inputs' device.
+# Nothing is computed here.
+
+def _code(t, what):
+    import torch
+    codes = {torch.float32: F32, torch.bfloat16: BF16}
+    if t.dtype not in codes:
+        raise ValueError(f"{what}: dtype {t.dtype} is not float32 or bfloat16")
+    return codes[t.dtype]
+
+
+def workspace(d, plan, device=None):
+    """A fresh workspace of mla_workspace_bytes(d, plan) bytes, status word cleared."""
+    import torch
+    ws = torch.empty(mla_workspace_bytes(d, plan), dtype=torch.uint8, device=device or "cuda")
+    mla_workspace_init(ws)
+    return ws
+
+
+def decode(d, c, plan, q_nope, q_rope, w_uk, w_uv, out=None, q_pos=None, ws=None, stream=None):
+    """mla_decode on tensors: returns out ([B, H, d_v], float32 unless given)."""
+    import torch
+    qw = _code(q_nope, "q_nope")
+    if out is None:
+        out = torch.empty((plan.batch, d.n_heads, d.d_v), dtype=torch.float32, device=q_nope.device)
+    if ws is None:
+        ws = workspace(d, plan, q_nope.device)
+    mla_decode(d, c, plan, q_nope, q_rope, q_pos, w_uk, w_uv, qw, out, _code(out, "out"), ws, stream)
+    return out
+
+
+def append(d, c, h, w_dkv, w_kr, ws=None, stream=None):
+    """mla_append on tensors: h is [B, n_new, d_model]."""
+    import torch
+    n_new = h.shape[1]
+    if ws is None:
+        ws = torch.empty(mla_append_workspace_bytes(d, h.shape[0], n_new), dtype=torch.uint8, device=h.device)
+        mla_workspace_init(ws)
+    mla_append(d, c, h, n_new, w_dkv, w_kr, _code(h, "h"), ws, stream)
+
+
+def append_decode(d, c, plan, h, w_dkv, w_kr, q_nope, q_rope, w_uk, w_uv, out=None, q_pos=None, ws=None,
+                  stream=None):
+    """mla_append_decode on tensors (the plan holds the lengths after the append)."""
+    import torch
+    n_new = h.shape[1]
+    if out is None:
+        out = torch.empty((plan.batch, d.n_heads, d.d_v), dtype=torch.float32, device=q_nope.device)
+    if ws is None:
+        need = max(mla_workspace_bytes(d, plan), mla_append_workspace_bytes(d, h.shape[0], n_new))
+        ws = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
+        mla_workspace_init(ws)
+    mla_append_decode(d, c, plan, h, n_new, w_dkv, w_kr, q_nope, q_rope, q_pos, w_uk, w_uv, _code(h, "h"), out,
+                      _code(out, "out"), ws, stream)
+    return out

@@ -280,3 +280,34 @@ def test_fast_random_shapes(gpu, seed):
         assert torch.equal(o, o32.to(torch.bfloat16))
         o = o32
     check(case, to_np(o), tol, seed=seed)
+
+
+def test_tensor_level_calls_match_the_abi(gpu):
+    """decode() / append_decode() read the dtypes off the tensors and allocate
+    the output and workspace; the results are the entry points' bit for bit."""
+    bf = lambda t: t.view(torch.bfloat16)  # noqa: E731  (bf16 bit patterns on the device)
+    case = v3_case([77, 300, 1025], "bf16", seed=58)
+    run = DeviceRun(gpu, case)
+    plan = run.plan()
+    ref = run.decode(plan=plan)
+    got = gpu.decode(run.d, run.cache, plan, bf(run.t["q_nope"]), bf(run.t["q_rope"]), bf(run.t["w_uk"]),
+                     bf(run.t["w_uv"]))
+    out16 = gpu.decode(run.d, run.cache, plan, bf(run.t["q_nope"]), bf(run.t["q_rope"]), bf(run.t["w_uk"]),
+                       bf(run.t["w_uv"]), out=torch.empty((case.B, case.H, case.d_v), dtype=torch.bfloat16,
+                                                          device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    assert torch.equal(out16, ref.to(torch.bfloat16))
+
+    case = v3_case([40, 700], "fp8", seed=59, n_new=1, d_model=7168)
+    a, b = DeviceRun(gpu, case), DeviceRun(gpu, case)
+    ref = a.append_decode()
+    plan = b.plan()
+    got = gpu.append_decode(b.d, b.cache, plan, bf(b.t["h"]), bf(b.t["w_dkv"]), bf(b.t["w_kr"]),
+                            bf(b.t["q_nope"]), bf(b.t["q_rope"]), bf(b.t["w_uk"]), bf(b.t["w_uv"]),
+                            ws=b.workspace(plan))  # a workspace of our own, to read its status word
+    torch.cuda.synchronize()
+    assert a.status() == 0 and b.status() == 0
+    assert torch.equal(got, ref)
+    with pytest.raises(ValueError):
+        gpu.decode(b.d, b.cache, plan, b.t["q_nope"], b.t["q_rope"], b.t["w_uk"], b.t["w_uv"])  # int16 bits
