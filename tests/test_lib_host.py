@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -208,3 +209,13 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         m.mla_abi_version()
     with pytest.raises(RuntimeError, match="not built"):
         m.mla_plan_create(d128(), [10, 20], 4)
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU; asking for more exits with a message and
+    touches no device."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2", "--steps", "1"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
