@@ -46,6 +46,8 @@ def d128():
 @pytest.mark.parametrize("lens,workers", [
     ([4096] * 32, 256), (list(range(4096, 8193, 128)), 256), ([131072] * 4, 256),
     ([1, 0, 33, 5000, 31, 32], 8), ([0, 0], 4), ([7], 1), ([1000] * 300, 256),
+    # total past 2^31 tokens: the planner's sums are 64-bit
+    ([2**30] * 3, 256), ([2**31 - 1, 5, 2**31 - 33], 1024),
 ])
 def test_plan_covers_every_token_once(lens, workers):
     p = m.mla_plan_create(d128(), lens, workers)
