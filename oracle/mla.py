@@ -244,6 +244,35 @@ def decode_absorbed(C, R, seq_start, seq_len, q_nope, q_rope, w_uk, w_uv,
     return out
 
 
+def decode_absorbed_heads(Cb, Rb, q_nope_b, q_rope_b, w_uk, w_uv, softmax_scale, rope_base, pos):
+    """The absorbed form of :func:`decode_absorbed` for every head of one
+    sequence at once, with the per-head vectors stacked into matrices (a
+    self-check form, pinned equal to the per-head forms; it lets whole
+    outputs be compared at full size):
+
+        Q~ [H, d_c]  with row i = W_UK,i^T q_nope[i]
+        Qr [H, d_hR] with row i = RoPE(q_rope[i], pos)
+        S  = softmax_scale * (C_b Q~^T + R_b Qr^T)      [L, H]
+        P  = column-wise softmax of S                   (each head over the L tokens)
+        O^ = P^T C_b                                    [H, d_c]
+        o[i] = W_UV,i O^[i]                             [H, d_v]
+
+    Cb [L, d_c] and Rb [L, d_hR] are the sequence's own cached rows (fp64);
+    q_nope_b [H, d_nope], q_rope_b [H, d_hR] (unrotated); pos the query
+    position. L = 0 gives zeros."""
+    H = q_nope_b.shape[0]
+    d_v = w_uv.shape[1]
+    if Cb.shape[0] == 0:
+        return np.zeros((H, d_v), dtype=np.float64)
+    q_lat = np.einsum("hnc,hn->hc", w_uk, q_nope_b)
+    q_r = rope(q_rope_b, pos, rope_base)
+    s = softmax_scale * (Cb @ q_lat.T + Rb @ q_r.T)
+    e = np.exp(s - s.max(axis=0, keepdims=True))
+    p = e / e.sum(axis=0, keepdims=True)
+    o_hat = p.T @ Cb
+    return np.einsum("hvc,hc->hv", w_uv, o_hat)
+
+
 # ------------------------------------------------------ several query tokens
 
 

@@ -126,6 +126,32 @@ def test_absorbed_equals_non_absorbed_deepseek_shape_sampled():
     assert rel_rms(a, n) < 1e-12
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_absorbed_heads_form_equals_per_head_forms(seed):
+    """The all-heads matrix form equals the per-(sequence, head) absorbed form
+    and the non-absorbed definition, on ragged random problems (an empty
+    sequence included) and explicit query positions."""
+    rng = np.random.default_rng(300 + seed)
+    B, H, d_c, d_r, d_n, d_v = 4, 5, 24, 8, 12, 10
+    lens = np.array([17, 1, 0, 40])
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]) + 3
+    n = int(starts[-1] + lens[-1] + 2)
+    C, R = rng.standard_normal((n, d_c)), rng.standard_normal((n, d_r))
+    qn, qr = rng.standard_normal((B, H, d_n)), rng.standard_normal((B, H, d_r))
+    wuk, wuv = rng.standard_normal((H, d_n, d_c)) / 5, rng.standard_normal((H, d_v, d_c)) / 5
+    pos = np.array([16, 7, 3, 100])
+    for q_pos in (None, pos):
+        ref = mla.decode(C, R, starts, lens, qn, qr, wuk, wuv, 0.3, 10000.0, q_pos=q_pos)
+        ref_abs = mla.decode_absorbed(C, R, starts, lens, qn, qr, wuk, wuv, 0.3, 10000.0, q_pos=q_pos)
+        for b in range(B):
+            P = lens[b] - 1 if q_pos is None else q_pos[b]
+            s0, L = int(starts[b]), int(lens[b])
+            got = mla.decode_absorbed_heads(C[s0:s0 + L], R[s0:s0 + L], qn[b], qr[b], wuk, wuv, 0.3, 10000.0, P)
+            scale = max(np.sqrt(np.mean(ref ** 2)), 1e-300)
+            assert np.max(np.abs(got - ref[b])) <= 1e-12 * scale
+            assert np.max(np.abs(got - ref_abs[b])) <= 1e-12 * scale
+
+
 def test_single_token_gives_value_of_that_token():
     p = random_problem(4, lens=(1, 1))
     o = run(mla.decode, p)
