@@ -288,6 +288,40 @@ def _code(t, what):
     return codes[t.dtype]
 
 
+def _expect(t, what, shape, dtype=None):
+    """t must have exactly `shape` (and `dtype` if given)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype} (one dtype for activations and weights)")
+
+
+def _check_decode_args(d, plan, q_nope, q_rope, w_uk, w_uv, q_len=1):
+    B, H = plan.batch, d.n_heads
+    lead = (B, H) if q_len == 1 else (B, q_len, H)
+    _code(q_nope, "q_nope")
+    _expect(q_nope, "q_nope", lead + (d.d_nope,))
+    _expect(q_rope, "q_rope", lead + (d.d_rope,), q_nope.dtype)
+    _expect(w_uk, "w_uk", (H, d.d_nope, d.d_c), q_nope.dtype)
+    _expect(w_uv, "w_uv", (H, d.d_v, d.d_c), q_nope.dtype)
+
+
+def _check_append_args(d, c, h, w_dkv, w_kr):
+    _code(h, "h")
+    if h.dim() != 3 or h.shape[0] != c.batch or h.shape[2] != d.d_model:
+        raise ValueError(f"h: shape {tuple(h.shape)}, expected ({c.batch}, n_new, {d.d_model})")
+    _expect(w_dkv, "w_dkv", (d.d_c, d.d_model), h.dtype)
+    _expect(w_kr, "w_kr", (d.d_rope, d.d_model), h.dtype)
+
+
+def _temp_ws_stream(stream):
+    """A workspace the call allocates itself is freed on return; with an
+    explicit stream its kernels may still be queued there, so that case
+    needs a caller-owned workspace."""
+    if stream is not None:
+        raise ValueError("pass ws (a workspace the caller keeps alive) when giving an explicit stream")
+
+
 def workspace(d, plan, device=None):
     """A fresh workspace of mla_workspace_bytes(d, plan) bytes, status word cleared."""
     import torch
@@ -297,22 +331,31 @@ def workspace(d, plan, device=None):
 
 
 def decode(d, c, plan, q_nope, q_rope, w_uk, w_uv, out=None, q_pos=None, ws=None, stream=None):
-    """mla_decode on tensors: returns out ([B, H, d_v], float32 unless given)."""
+    """mla_decode on tensors: returns out ([B, H, d_v], float32 unless given).
+    q_nope, q_rope, w_uk and w_uv share one dtype (float32 or bfloat16)."""
     import torch
+    _check_decode_args(d, plan, q_nope, q_rope, w_uk, w_uv)
     qw = _code(q_nope, "q_nope")
     if out is None:
         out = torch.empty((plan.batch, d.n_heads, d.d_v), dtype=torch.float32, device=q_nope.device)
+    _expect(out, "out", (plan.batch, d.n_heads, d.d_v))
+    if q_pos is not None:
+        _expect(q_pos, "q_pos", (plan.batch,), torch.int32)
     if ws is None:
+        _temp_ws_stream(stream)
         ws = workspace(d, plan, q_nope.device)
     mla_decode(d, c, plan, q_nope, q_rope, q_pos, w_uk, w_uv, qw, out, _code(out, "out"), ws, stream)
     return out
 
 
 def append(d, c, h, w_dkv, w_kr, ws=None, stream=None):
-    """mla_append on tensors: h is [B, n_new, d_model]."""
+    """mla_append on tensors: h is [B, n_new, d_model]; h, w_dkv and w_kr share
+    one dtype."""
     import torch
+    _check_append_args(d, c, h, w_dkv, w_kr)
     n_new = h.shape[1]
     if ws is None:
+        _temp_ws_stream(stream)
         ws = torch.empty(mla_append_workspace_bytes(d, h.shape[0], n_new), dtype=torch.uint8, device=h.device)
         mla_workspace_init(ws)
     mla_append(d, c, h, n_new, w_dkv, w_kr, _code(h, "h"), ws, stream)
@@ -320,12 +363,21 @@ def append(d, c, h, w_dkv, w_kr, ws=None, stream=None):
 
 def append_decode(d, c, plan, h, w_dkv, w_kr, q_nope, q_rope, w_uk, w_uv, out=None, q_pos=None, ws=None,
                   stream=None):
-    """mla_append_decode on tensors (the plan holds the lengths after the append)."""
+    """mla_append_decode on tensors (the plan holds the lengths after the
+    append); every activation and weight shares h's dtype."""
     import torch
+    _check_append_args(d, c, h, w_dkv, w_kr)
+    _check_decode_args(d, plan, q_nope, q_rope, w_uk, w_uv)
+    if q_nope.dtype != h.dtype:
+        raise ValueError(f"q_nope: dtype {q_nope.dtype}, expected {h.dtype} (one dtype for activations and weights)")
     n_new = h.shape[1]
     if out is None:
         out = torch.empty((plan.batch, d.n_heads, d.d_v), dtype=torch.float32, device=q_nope.device)
+    _expect(out, "out", (plan.batch, d.n_heads, d.d_v))
+    if q_pos is not None:
+        _expect(q_pos, "q_pos", (plan.batch,), torch.int32)
     if ws is None:
+        _temp_ws_stream(stream)
         need = max(mla_workspace_bytes(d, plan), mla_append_workspace_bytes(d, h.shape[0], n_new))
         ws = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
         mla_workspace_init(ws)

@@ -128,6 +128,29 @@ __device__ __forceinline__ void set_status(int32_t *status, int32_t code) {
   atomicCAS(status, 0, code);
 }
 
+// Run by every thread of one workgroup of the first kernel of a decode: the
+// checksum of the workspace's plan copy against the plan's; on a mismatch
+// the copy is fetched again from the plan's pinned host block (the kernels
+// that read the copy run after this one, in stream order).
+__device__ __forceinline__ void plan_verify(const PlanRef &p) {
+  typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
+  __shared__ unsigned long long sum;
+  if (threadIdx.x == 0) sum = 0;
+  __syncthreads();
+  const u32x4_ *dev = static_cast<const u32x4_ *>(p.dev);
+  uint64_t h = 0;
+  for (int x = threadIdx.x; x < p.nchunks; x += blockDim.x) {
+    const u32x4_ v = dev[x];
+    h += plan_chunk_hash(static_cast<uint32_t>(x), v[0], v[1], v[2], v[3]);
+  }
+  atomicAdd(&sum, static_cast<unsigned long long>(h));
+  __syncthreads();
+  if (sum != p.hash) {
+    const u32x4_ *host = static_cast<const u32x4_ *>(p.host);
+    for (int x = threadIdx.x; x < p.nchunks; x += blockDim.x) const_cast<u32x4_ *>(dev)[x] = host[x];
+  }
+}
+
 // Token range [0, t1) of sequence b lies in the cache: within its reserved
 // tokens, and (contiguous) within the rows or (paged) within its block
 // table row.
@@ -136,6 +159,26 @@ __device__ __forceinline__ bool seq_range_ok(const mla_cache &c, int b, int64_t 
   if (c.block_table == nullptr)
     return static_cast<int64_t>(c.seq_start[b]) >= 0 && static_cast<int64_t>(c.seq_start[b]) + t1 <= c.n_rows;
   return t1 <= static_cast<int64_t>(c.max_blocks) * c.block_tokens;
+}
+
+// Whether n_new >= 1 tokens can be appended to sequence b at its current
+// length len: the range [0, len + n_new) passes seq_range_ok and, in a
+// paged cache, every block the new tokens fall in is inside the cache.
+// MLA_OK, MLA_ERR_CAPACITY or MLA_ERR_PLAN (a block id outside the cache).
+// The append kernels write a sequence's rows, and advance_len_kernel adds
+// n_new to its length, only when this gives MLA_OK: a refused sequence is
+// left untouched.
+__device__ __forceinline__ int32_t append_check(const mla_cache &c, int b, int32_t len, int32_t n_new) {
+  if (len < 0 || !seq_range_ok(c, b, static_cast<int64_t>(len) + n_new)) return MLA_ERR_CAPACITY;
+  if (c.block_table != nullptr) {
+    const int64_t bt = c.block_tokens;
+    const int64_t last = (static_cast<int64_t>(len) + n_new - 1) / bt;
+    for (int64_t x = len / bt; x <= last; ++x) {
+      const int64_t blk = c.block_table[static_cast<int64_t>(b) * c.max_blocks + x];
+      if (blk < 0 || (blk + 1) * bt > c.n_rows) return MLA_ERR_PLAN;
+    }
+  }
+  return MLA_OK;
 }
 
 // Row of token t of sequence b (t inside a range seq_range_ok accepted):

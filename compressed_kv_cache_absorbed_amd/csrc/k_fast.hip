@@ -92,8 +92,8 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
                                                           const uint16_t *__restrict__ q_rope,
                                                           const int32_t *__restrict__ q_pos,
                                                           const uint16_t *__restrict__ w_uk,
-                                                          const SeqInfo *__restrict__ seqs,
-                                                          uint16_t *__restrict__ Q) {
+                                                          const int32_t *__restrict__ dev_len,
+                                                          uint16_t *__restrict__ Q, PlanRef plan) {
   using namespace fast;
   constexpr int WROW = 288;  // LDS bytes per W row (128 columns = 256 bytes + 32)
   __shared__ __attribute__((aligned(16))) char smem[DNOPE * WROW];
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
   int64_t P = 0;
   uint32_t xr = 0;
   if (rb < B) {
-    P = (q_pos ? q_pos[rb] : static_cast<int64_t>(seqs[rb].len) - 1) - back;
+    P = (q_pos ? q_pos[rb] : static_cast<int64_t>(dev_len[rb]) - 1) - back;
     xr = *reinterpret_cast<const uint32_t *>(q_rope + (static_cast<size_t>(rb) * H + i) * DR + 2 * rp);
   }
   // B operand: q_nope^T [16 n x 32 b]: lane holds sequence b0 + l%32, n = 16 kk + 8(l/32) .. +7
@@ -178,6 +178,8 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
       *reinterpret_cast<f16x4 *>(dst + 8 * g4) = v;
     }
   }
+  // the plan copy the split-K and combine kernels read
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) plan_verify(plan);
 }
 
 // ---------------------------------------------------------------- combine
@@ -248,12 +250,13 @@ struct RowBatch {
   }
 };
 template <int NB>
-__global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr, int G, int VH,
+__global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr, int G, int VH, int n_items,
                                                            const SeqInfo *__restrict__ seqs,
                                                            const int32_t *__restrict__ dev_len,
                                                            const uint16_t *__restrict__ opart,
                                                            const float *__restrict__ lse,
-                                                           const uint16_t *__restrict__ w_uv, void *o, int o_bf16) {
+                                                           const uint16_t *__restrict__ w_uv, void *o, int o_bf16,
+                                                           int32_t *__restrict__ status) {
   using namespace fast;
   constexpr int NW = 8;                            // waves
   constexpr int TPB = 64 * NW / NB;                // threads per sequence
@@ -284,7 +287,11 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
   int S = 0, ib = 0;
   if (b < B) {
     const SeqInfo si = seqs[b];
-    if (si.item_count > 0 && dev_len[b] == si.len) {
+    // (a sequence's items must lie in the item list; the plan copy was
+    // checked, so this only guards the reads below)
+    const bool in_list = si.item_begin >= 0 && si.item_count >= 0 && si.item_begin <= n_items - si.item_count;
+    if (!in_list && q == 0 && i == 0) set_status(status, MLA_ERR_PLAN);
+    if (in_list && si.item_count > 0 && dev_len[b] == si.len) {
       S = si.item_count;
       ib = si.item_begin;
     }
@@ -492,16 +499,13 @@ __global__ __launch_bounds__(256) void append_finish_kernel(mla_dims d, mla_cach
   const int N = d.d_c + d.d_rope;
   const int32_t len = c.seq_len[b];
   const int64_t pos = static_cast<int64_t>(len) + j;
-  if (len < 0 || !seq_range_ok(c, b, static_cast<int64_t>(len) + n_new)) {
-    if (tid == 0 && j == 0) set_status(status, MLA_ERR_CAPACITY);
+  const int32_t chk = append_check(c, b, len, n_new);
+  if (chk != MLA_OK) {
+    if (tid == 0 && j == 0) set_status(status, chk);
     return;
   }
   bool bad = false;
-  const int64_t row = cache_row(c, b, pos, bad);
-  if (bad) {
-    if (tid == 0) set_status(status, MLA_ERR_PLAN);
-    return;
-  }
+  const int64_t row = cache_row(c, b, pos, bad);  // (every block was checked)
   // the K-split partials, up to 16 loads in flight per output
   for (int n = tid; n < N; n += 256) {
     float acc = 0.0f;
@@ -557,15 +561,16 @@ hipError_t launch_append_finish(hipStream_t s, const mla_dims &d, const mla_cach
 
 hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, int32_t q_len, const void *q_nope,
                               const void *q_rope, const int32_t *q_pos, const void *w_uk,
-                              const SeqInfo *seqs, uint16_t *q_out) {
+                              const int32_t *seq_len, uint16_t *q_out, const PlanRef &plan) {
   const int H = d.n_heads * q_len;
   return launch_kernel(absorb_fast_kernel, dim3(H, fast::DC / 128, (batch + 31) / 32), 256, 0, s, batch, H,
                        d.n_heads, q_len, d.softmax_scale * kLog2e, d.rope_base, static_cast<const uint16_t *>(q_nope),
-                       static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seqs, q_out);
+                       static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seq_len, q_out, plan);
 }
 
-hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, const SeqInfo *seqs,
-                               const uint16_t *opart, const float *lse, const uint16_t *w_uv, void *o, int o_bf16) {
+hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, int32_t n_items,
+                               const SeqInfo *seqs, const uint16_t *opart, const float *lse, const uint16_t *w_uv,
+                               void *o, int o_bf16, int32_t *status) {
   const int B = c.batch, H = d.n_heads * q_len;
   if (B == 0) return hipSuccess;
   // the largest group (up to the 16 columns of one product) that still
@@ -579,8 +584,8 @@ hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache
   const dim3 grid(H * G * VH);
 #define MLA_COMBINE(NBV)                                                                                      \
   case NBV:                                                                                                  \
-    return launch_kernel(combine_fast_kernel<NBV>, grid, 512, 0, s, B, H, d.n_heads, G, VH, seqs, c.seq_len, opart, lse, \
-                         w_uv, o, o_bf16)
+    return launch_kernel(combine_fast_kernel<NBV>, grid, 512, 0, s, B, H, d.n_heads, G, VH, n_items, seqs, c.seq_len, \
+                         opart, lse, w_uv, o, o_bf16, status)
   switch (nb) {
     MLA_COMBINE(1);
     MLA_COMBINE(2);

@@ -33,18 +33,14 @@ __global__ __launch_bounds__(256) void append_generic_kernel(mla_dims d, mla_cac
   float *red = outv + R;         // [4]
 
   const int32_t len = c.seq_len[b];
-  const int32_t cap = c.seq_cap[b];
   const int64_t pos = static_cast<int64_t>(len) + j;
-  if (len < 0 || static_cast<int64_t>(len) + n_new > cap || !seq_range_ok(c, b, static_cast<int64_t>(len) + n_new)) {
-    if (tid == 0 && j == 0) set_status(status, MLA_ERR_CAPACITY);
+  const int32_t chk = append_check(c, b, len, n_new);
+  if (chk != MLA_OK) {
+    if (tid == 0 && j == 0) set_status(status, chk);
     return;
   }
   bool bad = false;
-  const int64_t row = cache_row(c, b, pos, bad);
-  if (bad) {
-    if (tid == 0) set_status(status, MLA_ERR_PLAN);
-    return;
-  }
+  const int64_t row = cache_row(c, b, pos, bad);  // (every block was checked)
 
   const int64_t hoff = (static_cast<int64_t>(b) * n_new + j) * d.d_model;
   for (int k = tid; k < d.d_model; k += 256) hs[k] = load_elem(h, hoff + k, act);
@@ -77,13 +73,13 @@ __global__ void advance_len_kernel(mla_cache c, int32_t n_new) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= c.batch) return;
   const int32_t len = c.seq_len[b];
-  if (len >= 0 && static_cast<int64_t>(len) + n_new <= c.seq_cap[b]) c.seq_len[b] = len + n_new;
+  if (append_check(c, b, len, n_new) == MLA_OK) c.seq_len[b] = len + n_new;
 }
 
 __global__ __launch_bounds__(256) void absorb_generic_kernel(mla_dims d, const void *q_nope,
                                                             const void *q_rope, const int32_t *q_pos,
                                                             const void *w_uk, mla_dtype qw,
-                                                            const SeqInfo *seqs, float *q_out) {
+                                                            const int32_t *dev_len, float *q_out, PlanRef plan) {
   extern __shared__ float qn[];  // [d_nope]
   const int b = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
   const int H = d.n_heads, D = d.d_c + d.d_rope;
@@ -98,7 +94,7 @@ __global__ __launch_bounds__(256) void absorb_generic_kernel(mla_dims d, const v
       acc = fmaf(load_elem(w_uk, (static_cast<int64_t>(i) * d.d_nope + n) * d.d_c + cc, qw), qn[n], acc);
     out[cc] = acc * qs;
   }
-  const int64_t P = q_pos ? q_pos[b] : static_cast<int64_t>(seqs[b].len) - 1;
+  const int64_t P = q_pos ? q_pos[b] : static_cast<int64_t>(dev_len[b]) - 1;
   for (int p = tid; p < d.d_rope / 2; p += 256) {
     float cs, sn;
     rope_cos_sin(P, p, d.d_rope, d.rope_base, &cs, &sn);
@@ -107,12 +103,16 @@ __global__ __launch_bounds__(256) void absorb_generic_kernel(mla_dims d, const v
     out[d.d_c + 2 * p] = (x0 * cs - x1 * sn) * qs;
     out[d.d_c + 2 * p + 1] = (x0 * sn + x1 * cs) * qs;
   }
+  // the plan copy the decode and combine kernels read
+  if (blockIdx.x == 0 && blockIdx.y == 0) plan_verify(plan);
 }
 
-// True when the device length agrees with the plan and the item's rows lie in
-// the sequence's reserved range and in the cache.
-__device__ __forceinline__ bool item_ok(const mla_cache &c, const WorkItem &it, const SeqInfo &si) {
-  return c.seq_len[it.b] == si.len && it.t0 >= 0 && it.t0 < it.t1 && seq_range_ok(c, it.b, it.t1);
+// True when the item names a sequence of the batch, the device length agrees
+// with the plan and the item's rows lie in the sequence's reserved range and
+// in the cache.
+__device__ __forceinline__ bool item_ok(const mla_cache &c, const WorkItem &it, const SeqInfo *seqs) {
+  if (it.b < 0 || it.b >= c.batch) return false;
+  return c.seq_len[it.b] == seqs[it.b].len && it.t0 >= 0 && it.t0 < it.t1 && seq_range_ok(c, it.b, it.t1);
 }
 
 __global__ __launch_bounds__(256) void decode_generic_kernel(mla_dims d, mla_cache c,
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(mla_dims d, mla_cac
   float *red = ps + 256;
   float *op = opart + (static_cast<int64_t>(k) * H + i) * d.d_c;
 
-  if (!item_ok(c, it, seqs[it.b])) {
+  if (!item_ok(c, it, seqs)) {
     if (tid == 0 && i == 0) set_status(status, MLA_ERR_PLAN);
     for (int cc = tid; cc < d.d_c; cc += 256) op[cc] = 0.0f;
     if (tid == 0) lse[static_cast<int64_t>(k) * H + i] = -INFINITY;
@@ -189,16 +189,18 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(mla_dims d, mla_cac
   if (bad && tid == 0) set_status(status, MLA_ERR_PLAN);  // a block id outside the cache: block 0 was read
 }
 
-__global__ __launch_bounds__(256) void combine_generic_kernel(mla_dims d, mla_cache c,
+__global__ __launch_bounds__(256) void combine_generic_kernel(mla_dims d, mla_cache c, int n_items,
                                                              const SeqInfo *seqs, const float *opart,
                                                              const float *lse, const void *w_uv,
-                                                             mla_dtype qw, void *o, mla_dtype od) {
+                                                             mla_dtype qw, void *o, mla_dtype od, int32_t *status) {
   extern __shared__ float oh[];  // [d_c]
   const int b = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int H = d.n_heads;
   const SeqInfo si = seqs[b];
-  const bool ok = si.item_count > 0 && c.seq_len[b] == si.len;
+  const bool in_list = si.item_begin >= 0 && si.item_count >= 0 && si.item_begin <= n_items - si.item_count;
+  if (!in_list && tid == 0 && i == 0) set_status(status, MLA_ERR_PLAN);
+  const bool ok = in_list && si.item_count > 0 && c.seq_len[b] == si.len;
   if (ok) {
     float M = -INFINITY;
     for (int s = 0; s < si.item_count; ++s) M = fmaxf(M, lse[static_cast<int64_t>(si.item_begin + s) * H + i]);
@@ -300,9 +302,9 @@ hipError_t launch_append_generic(hipStream_t s, const mla_dims &d, const mla_cac
 
 hipError_t launch_absorb_generic(hipStream_t s, const mla_dims &d, int32_t batch, const void *q_nope,
                                  const void *q_rope, const int32_t *q_pos, const void *w_uk,
-                                 mla_dtype qw, const SeqInfo *seqs, float *q_out) {
+                                 mla_dtype qw, const int32_t *seq_len, float *q_out, const PlanRef &plan) {
   return launch_kernel(absorb_generic_kernel, dim3(batch, d.n_heads), 256, sizeof(float) * d.d_nope, s, d, q_nope,
-                       q_rope, q_pos, w_uk, qw, seqs, q_out);
+                       q_rope, q_pos, w_uk, qw, seq_len, q_out, plan);
 }
 
 hipError_t launch_decode_generic(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,
@@ -314,11 +316,11 @@ hipError_t launch_decode_generic(hipStream_t s, const mla_dims &d, const mla_cac
                        lse, status);
 }
 
-hipError_t launch_combine_generic(hipStream_t s, const mla_dims &d, const mla_cache &c,
+hipError_t launch_combine_generic(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,
                                   const SeqInfo *seqs, const float *opart, const float *lse,
-                                  const void *w_uv, mla_dtype qw, void *o, mla_dtype od) {
-  return launch_kernel(combine_generic_kernel, dim3(c.batch, d.n_heads), 256, sizeof(float) * d.d_c, s, d, c, seqs,
-                       opart, lse, w_uv, qw, o, od);
+                                  const void *w_uv, mla_dtype qw, void *o, mla_dtype od, int32_t *status) {
+  return launch_kernel(combine_generic_kernel, dim3(c.batch, d.n_heads), 256, sizeof(float) * d.d_c, s, d, c, n_items,
+                       seqs, opart, lse, w_uv, qw, o, od, status);
 }
 
 hipError_t launch_copy(hipStream_t s, void *dst, const void *src, size_t n16) {

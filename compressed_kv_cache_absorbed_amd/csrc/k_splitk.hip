@@ -41,6 +41,7 @@
 #include <cmath>
 
 #include "device_util.hpp"
+#include "splitk_addr.hpp"
 
 namespace mla {
 
@@ -115,8 +116,11 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// k_rope chunk swizzle: chunk c of token t's row sits at c ^ rsw(t).
-__device__ __forceinline__ int rsw(int t) { return (t >> 1) & 7; }
+// k_rope chunk swizzle: chunk c of token t's row sits at c ^ rsw(t) (the
+// copies' source chunks use the same function).
+using sa::rsw;
+static_assert(sk::T == sa::T && sk::RAW_DMA_PER_WAVE == sa::RAW_DMA_PER_WAVE && sk::RAW_ROWB == sa::RAW_ROWB,
+              "tile geometry shared with the copy addresses");
 
 // A copy of a thread index the compiler cannot see through, so per-tile
 // address arithmetic is recomputed in place instead of hoisted into live
@@ -155,61 +159,12 @@ __device__ __forceinline__ void lds_dma4(const char *base, uint32_t voff, uint32
                : "memory", "m0");
 }
 
-struct Item {
-  const char *rows;
-  const float *scale;
-  const int32_t *blocks;  // paged cache: this sequence's block table row, else nullptr
-  int64_t stride, row0;
-  int block_tokens, n_blocks;  // paged: rows per block, blocks in the cache
-  int t0, t1, ntiles;
-  int tvis;  // this wave's queries see tokens < tvis (t1, or less for an earlier one of several new tokens)
-};
-
-// Where tile `tile` of an item starts in global memory, and its last valid
-// token (tokens past it repeat that row: finite data, masked out of the
-// softmax). A tile past the item's end reads the item's last tile instead
-// (its data is never scored). Tiles start at multiples of 32 tokens, so a
-// tile never straddles two blocks of a paged cache: one lookup per tile.
-struct TileSrc {
-  const char *base;   // row of the tile's first token
-  const char *sbase;  // fp8 scales
-  int64_t stride;
-  int tmax;
-};
-__device__ __forceinline__ TileSrc tile_src(const Item &it, int tile) {
-  const int ts = it.t0 + min(tile, it.ntiles - 1) * sk::T;
-  int64_t row = it.row0 + ts;
-  if (it.blocks != nullptr) {
-    // (ids outside the cache were reported when the item started; clamped here)
-    const int blk = min(max(it.blocks[ts / it.block_tokens], 0), it.n_blocks - 1);
-    row = static_cast<int64_t>(blk) * it.block_tokens + ts % it.block_tokens;
-  }
-  TileSrc r;
-  r.base = it.rows + row * it.stride;
-  r.sbase = reinterpret_cast<const char *>(it.scale + row);
-  r.stride = it.stride;
-  r.tmax = it.t1 - 1 - ts;
-  return r;
-}
-
-// Source of the k_rope copy of wave w: lane i reads chunk (i % 8) ^ rsw(t)
-// of token t = 8 w + i / 8, clamped to the item's last token. The base is
-// the wave's first (clamped) row, so the lane offset stays within 8 rows and
-// never goes negative, also for a tile past the item's end (tmax < 0).
-struct RopeSrc {
-  const char *base;
-  uint32_t voff;
-};
-__device__ __forceinline__ RopeSrc rope_src(const TileSrc &src, int w, int lane) {
-  const int ln = opaque(lane);
-  const int t = 8 * w + (ln >> 3);
-  const int t0 = min(8 * w, src.tmax);
-  RopeSrc r;
-  r.base = src.base + static_cast<int64_t>(t0) * src.stride;
-  r.voff = static_cast<uint32_t>(min(t, src.tmax) - t0) * static_cast<uint32_t>(src.stride) + 1024u +
-           16u * static_cast<uint32_t>((ln & 7) ^ rsw(t));
-  return r;
-}
+using sa::Item;
+using sa::RawSrc;
+using sa::RopeSrc;
+using sa::TileSrc;
+using sa::raw_src;
+using sa::tile_src;
 
 // bf16 tile copy, 9 loads per wave (w uniform): x < 8 copies the 1024 latent
 // bytes of token 8 w + x into its LDS row (lane i: bytes 16 i .. 16 i + 15);
@@ -220,11 +175,9 @@ __device__ __forceinline__ void dma_bf16_piece(const TileSrc &src, int w, int la
   using M = sk::Map<false>;
   const uint32_t lds0 = LDS_OFF(g_lds);
   if (x < 8) {
-    const int t = 8 * w + x;
-    const char *row = src.base + static_cast<int64_t>(min(t, src.tmax)) * src.stride;
-    lds_dma16(row, static_cast<uint32_t>(16 * lane), lds0 + M::lat(B) + sk::LROW * t);
+    lds_dma16(sa::latent_row(src, w, x), static_cast<uint32_t>(16 * lane), lds0 + M::lat(B) + sk::LROW * (8 * w + x));
   } else {
-    const RopeSrc r = rope_src(src, w, lane);
+    const RopeSrc r = sa::rope_src(src, w, opaque(lane));
     lds_dma16(r.base, r.voff, lds0 + M::rope(B) + 1024 * w);
   }
 }
@@ -235,26 +188,6 @@ __device__ __forceinline__ void dma_bf16(const Item &it, int tile, int w, int la
   for (int x = 0; x < 9; ++x) dma_bf16_piece<B>(src, w, lane, x);
 }
 
-// Source of wave w's part of a raw fp8 tile copy: its 8 rows (tokens
-// 8 w .. 8 w + 7; 5 copies of 1 KB cover them) and the tile's 32 scales,
-// each clamped to the item's last token. The bases are the first clamped
-// row and scale, so lane offsets stay small and never go negative, also
-// for a tile past the item's end (tmax < 0).
-struct RawSrc {
-  const char *base, *sbase;
-  int64_t stride;
-  int tmax, t0, s0;
-};
-__device__ __forceinline__ RawSrc raw_src(const TileSrc &src, int w) {
-  RawSrc r;
-  r.t0 = min(8 * w, src.tmax);
-  r.s0 = min(0, src.tmax);
-  r.base = src.base + static_cast<int64_t>(r.t0) * src.stride;
-  r.sbase = src.sbase + 4 * static_cast<int64_t>(r.s0);
-  r.stride = src.stride;
-  r.tmax = src.tmax;
-  return r;
-}
 // Raw fp8 tile copy, 6 loads per wave: x < 5 copies 1 KB of wave w's rows
 // (the raw tile is the rows back to back, 40 chunks of 16 bytes each:
 // chunk P = 64 (5 w + x) + lane holds token P / 40, bytes 16 (P % 40)), x = 5
@@ -267,15 +200,9 @@ __device__ __forceinline__ void dma_raw_piece(const RawSrc &rs, int w, int lane,
   const int ln = opaque(lane);
   if (x < sk::RAW_DMA_PER_WAVE) {
     const int q = sk::RAW_DMA_PER_WAVE * w + x;
-    const int P = 64 * q + ln;
-    const int t = P / 40;
-    const int ch = P - 40 * t;
-    const uint32_t voff = static_cast<uint32_t>(min(t, rs.tmax) - rs.t0) * static_cast<uint32_t>(rs.stride) +
-                          static_cast<uint32_t>(16 * ch);
-    lds_dma16(rs.base, voff, __builtin_amdgcn_readfirstlane(lds0 + M::raw(R) + 1024u * q));
+    lds_dma16(rs.base, sa::raw_piece_off(rs, w, ln, x), __builtin_amdgcn_readfirstlane(lds0 + M::raw(R) + 1024u * q));
   } else {
-    lds_dma4(rs.sbase, static_cast<uint32_t>(min(ln & 31, rs.tmax) - rs.s0) * 4u,
-             __builtin_amdgcn_readfirstlane(lds0 + M::scl(R, 0) + 256u * w));
+    lds_dma4(rs.sbase, sa::raw_scale_off(rs, ln), __builtin_amdgcn_readfirstlane(lds0 + M::scl(R, 0) + 256u * w));
   }
 }
 template <int R>
@@ -613,7 +540,7 @@ struct HideBf16 {
     if (kk % 4 == 0 && kk / 4 < 8) {
       const int x = kk / 4;
       lds_dma16(row, static_cast<uint32_t>(16 * lane), LDS_OFF(g_lds) + M::lat(DMA_BUF) + sk::LROW * (8 * w + x));
-      row += x + 1 <= lim ? stride : 0;
+      row = sa::latent_row_next(row, stride, lim, x);
     }
     if (kk == 32) lds_dma16(rope_base, rope_voff, LDS_OFF(g_lds) + M::rope(DMA_BUF) + 1024 * w);
     if (kk == 16) {
@@ -662,8 +589,8 @@ template <int I> struct StepHide<false, I> {
   __device__ __forceinline__ static void init(type &h, const TileSrc &src, int w, int lane, int tid) {
     h.stride = src.stride;
     h.lim = src.tmax - 8 * w;
-    h.row = src.base + static_cast<int64_t>(min(8 * w, src.tmax)) * src.stride;
-    const RopeSrc r = rope_src(src, w, lane);
+    h.row = sa::latent_row_first(src, w);
+    const RopeSrc r = sa::rope_src(src, w, opaque(lane));
     h.rope_base = r.base;
     h.rope_voff = r.voff;
     h.w = w;
@@ -756,7 +683,9 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H, int 
   // this workgroup's 128 heads of item k: 128 rows of 512 fp16 partials
   uint16_t *ob = opart + (static_cast<size_t>(k) * H + y * 128) * DC;
 
-  const bool ok = c.seq_len[wi.b] == seqs[wi.b].len && wi.t0 >= 0 && wi.t0 < wi.t1 && seq_range_ok(c, wi.b, wi.t1);
+  // (the item must name a sequence of the batch before anything is indexed by it)
+  const bool ok = wi.b >= 0 && wi.b < c.batch && c.seq_len[wi.b] == seqs[wi.b].len && wi.t0 >= 0 && wi.t0 < wi.t1 &&
+                  seq_range_ok(c, wi.b, wi.t1);
   if (!ok) {
     if (tid == 0 && y == 0) set_status(status, MLA_ERR_PLAN);
     for (int x = tid; x < 128 * DC / 8; x += 256) reinterpret_cast<u32x4 *>(ob)[x] = u32x4{0, 0, 0, 0};

@@ -9,7 +9,6 @@
 #include <cstring>
 #include <mutex>
 #include <new>
-#include <unordered_map>
 #include <vector>
 
 #include "mla_internal.hpp"
@@ -106,10 +105,13 @@ const char *kKernelNames[K_COUNT] = {
 
 namespace mla {
 
-void prof_before(hipStream_t, int kernel_id) {
+void prof_before(hipStream_t s, int kernel_id) {
   Profiler &p = prof();
   std::lock_guard<std::mutex> g(p.mu);
   if (!p.on || static_cast<int>(p.recs.size()) >= p.max_records) return;
+  // start each recorded kernel on an idle stream: a dispatch queued behind
+  // running work can take its start time before that work has ended
+  (void)hipStreamSynchronize(s);
   hipEvent_t a = p.get();
   hipEvent_t b = a ? p.get() : nullptr;
   if (!b) {
@@ -149,20 +151,21 @@ void prof_after(hipStream_t, int kernel_id) {
   p.taken = false;
 }
 
-DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items, int32_t q_len) {
+DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items, int32_t q_len, bool fast) {
   DecodeWs w;
+  const size_t eb = fast ? 2 : sizeof(float);  // query and partial element size
+  const size_t hq = static_cast<size_t>(d.n_heads) * std::max(q_len, 1);
+  const size_t ni = static_cast<size_t>(std::max(n_items, 1));
   size_t off = kStatusBytes;
-  // items and seq info are contiguous: one copy of the plan's host block
+  w.q = off;
+  off = align_up(off + eb * batch * hq * (d.d_c + d.d_rope), 256);
+  w.opart = off;
+  off = align_up(off + eb * ni * hq * d.d_c, 256);
+  w.lse = off;
+  off = align_up(off + sizeof(float) * ni * hq, 256);
   w.items = off;
   w.seqs = off + sizeof(WorkItem) * n_items;
   off = align_up(w.seqs + sizeof(SeqInfo) * batch, 256);
-  w.q = off;
-  const size_t hq = static_cast<size_t>(d.n_heads) * std::max(q_len, 1);
-  off = align_up(off + sizeof(float) * batch * hq * (d.d_c + d.d_rope), 256);
-  w.opart = off;
-  off = align_up(off + sizeof(float) * static_cast<size_t>(std::max(n_items, 1)) * hq * d.d_c, 256);
-  w.lse = off;
-  off = align_up(off + sizeof(float) * static_cast<size_t>(std::max(n_items, 1)) * hq, 256);
   w.total = off;
   return w;
 }
@@ -281,25 +284,32 @@ mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32
   p->chunk = static_cast<int32_t>(C);
   p->n_workers = n_workers;
   p->lens.assign(host_lens, host_lens + batch);
-  static std::atomic<uint64_t> next_id{1};
-  p->id = next_id.fetch_add(1);
   p->host_block_bytes = sizeof(WorkItem) * kept.size() + sizeof(SeqInfo) * batch;
-  void *blk = nullptr;
-  if (hipHostMalloc(&blk, p->host_block_bytes, hipHostMallocDefault) == hipSuccess && blk) {
+  // pinned and mapped: the first kernel of a decode reads it directly when
+  // the workspace's copy does not match. Without a device (host-side
+  // planning, inspection) the block is ordinary memory and decodes refuse
+  // the plan.
+  void *blk = nullptr, *dev = nullptr;
+  if (hipHostMalloc(&blk, p->host_block_bytes, hipHostMallocMapped) == hipSuccess && blk) {
     p->pinned = true;
+    if (hipHostGetDevicePointer(&dev, blk, 0) != hipSuccess) dev = nullptr;
   } else {
-    (void)hipGetLastError();
     blk = std::malloc(p->host_block_bytes);
-    p->pinned = false;
   }
+  (void)hipGetLastError();
   if (!blk) {
     delete p;
     return MLA_ERR_INVALID_ARG;
   }
   p->host_block = blk;
+  p->host_dev = dev;
   std::memcpy(blk, kept.data(), sizeof(WorkItem) * kept.size());
-  std::memcpy(static_cast<char *>(blk) + sizeof(WorkItem) * kept.size(), seqs.data(),
-              sizeof(SeqInfo) * batch);
+  std::memcpy(static_cast<char *>(blk) + sizeof(WorkItem) * kept.size(), seqs.data(), sizeof(SeqInfo) * batch);
+  const uint32_t *words = static_cast<const uint32_t *>(blk);
+  uint64_t h = 0;
+  for (size_t i = 0; i < p->host_block_bytes / 16; ++i)
+    h += plan_chunk_hash(static_cast<uint32_t>(i), words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]);
+  p->hash = h;
   *out = p;
   return MLA_OK;
 }
@@ -331,7 +341,8 @@ size_t mla_append_workspace_bytes(const mla_dims *dims, int32_t batch, int32_t n
 
 size_t mla_decode_workspace_bytes(const mla_dims *dims, const mla_plan *plan) {
   if (check_dims(dims, false, true) != MLA_OK || !plan) return 0;
-  return decode_ws_layout(*dims, plan->batch, plan->n_items).total;
+  // sized for the generic path's fp32 arrays, so one size serves either path
+  return decode_ws_layout(*dims, plan->batch, plan->n_items, 1, false).total;
 }
 
 size_t mla_workspace_bytes(const mla_dims *dims, const mla_plan *plan) {
@@ -343,49 +354,15 @@ size_t mla_workspace_bytes(const mla_dims *dims, const mla_plan *plan) {
 
 size_t mla_decode_multi_workspace_bytes(const mla_dims *dims, const mla_plan *plan, int32_t q_len) {
   if (check_dims(dims, false, true) != MLA_OK || !plan || q_len < 1 || q_len > kMaxQueryTokens) return 0;
-  return decode_ws_layout(*dims, plan->batch, plan->n_items, q_len).total;
+  return decode_ws_layout(*dims, plan->batch, plan->n_items, q_len, false).total;
 }
 
 }  // extern "C"
-
-// The device copy of a plan's work list lives in the workspace. A decode
-// whose workspace already holds the copy of the same plan (made by an
-// earlier call on it, and not overwritten since) skips the upload: one fewer
-// copy per step. mla_workspace_init and the matrix-core append (whose
-// partial products share that region) forget the workspace's entry.
-namespace {
-struct PlanCopies {
-  std::mutex mu;
-  std::unordered_map<const void *, uint64_t> last;
-};
-PlanCopies &plan_copies() {
-  static PlanCopies *p = new PlanCopies();
-  return *p;
-}
-}  // namespace
-
-static bool plan_copy_current(const void *ws, uint64_t id) {
-  PlanCopies &c = plan_copies();
-  std::lock_guard<std::mutex> g(c.mu);
-  auto it = c.last.find(ws);
-  return it != c.last.end() && it->second == id;
-}
-static void plan_copy_record(const void *ws, uint64_t id) {
-  PlanCopies &c = plan_copies();
-  std::lock_guard<std::mutex> g(c.mu);
-  c.last[ws] = id;
-}
-static void plan_copy_forget(const void *ws) {
-  PlanCopies &c = plan_copies();
-  std::lock_guard<std::mutex> g(c.mu);
-  c.last.erase(ws);
-}
 
 extern "C" {
 
 mla_status mla_workspace_init(void *ws, size_t ws_bytes, void *stream) {
   if (!ws || ws_bytes < kStatusBytes || !aligned16(ws)) return MLA_ERR_INVALID_ARG;
-  plan_copy_forget(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   MLA_LAUNCH(s, K_INIT, launch_init(s, static_cast<int32_t *>(ws)));
   return MLA_OK;
@@ -430,7 +407,6 @@ static mla_status do_append(const mla_dims *dims, const mla_cache *cache, const 
   if (append_fast_path(*dims, cache->batch * n_new, act)) {
     const AppendWs w = append_ws_layout(*dims, cache->batch, n_new);
     float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + w.partial);
-    plan_copy_forget(ws);  // the partial products overwrite the plan's copy
     MLA_LAUNCH(s, K_APPEND_GEMM,
                launch_append_fast(s, *dims, *cache, h, n_new, w_dkv, w_kr, partial, w.ksplit, status));
     MLA_LAUNCH(s, K_APPEND_FINISH, launch_append_finish(s, *dims, *cache, n_new, partial, w.ksplit, status));
@@ -466,7 +442,7 @@ static mla_status validate_decode(const mla_dims *dims, const mla_cache *cache, 
       !aligned16(o) || !aligned16(ws))
     return MLA_ERR_INVALID_ARG;
   if (q_len < 1 || q_len > kMaxQueryTokens) return MLA_ERR_INVALID_ARG;
-  if (ws_bytes < decode_ws_layout(*dims, plan->batch, plan->n_items, q_len).total) return MLA_ERR_WORKSPACE;
+  if (ws_bytes < decode_ws_layout(*dims, plan->batch, plan->n_items, q_len, false).total) return MLA_ERR_WORKSPACE;
   if (!decode_fast_path(*dims, *cache, qw)) {
     if (q_len > 1) return MLA_ERR_UNSUPPORTED;
     if (dims->d_c > 1024) return MLA_ERR_UNSUPPORTED;
@@ -474,43 +450,46 @@ static mla_status validate_decode(const mla_dims *dims, const mla_cache *cache, 
         sizeof(float) * static_cast<size_t>(dims->d_nope) > 64 * 1024)
       return MLA_ERR_UNSUPPORTED;
   }
+  if (!plan->host_dev) return MLA_ERR_HIP;  // made where no pinned, device-mapped memory was available
   return MLA_OK;
 }
 
+// compact: the workspace is laid out for the path that runs (2-byte query
+// and partials on the matrix-core path), not for the size the workspace
+// queries report (which serves either path).
 static mla_status do_decode(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
                             const void *q_nope, const void *q_rope, const int32_t *q_pos,
                             const void *w_uk, const void *w_uv, mla_dtype qw, void *o, mla_dtype od,
-                            void *ws, hipStream_t s, int32_t q_len = 1) {
-  const DecodeWs w = decode_ws_layout(*dims, plan->batch, plan->n_items, q_len);
+                            void *ws, hipStream_t s, int32_t q_len = 1, bool compact = false) {
+  const bool fast = decode_fast_path(*dims, *cache, qw);
+  const DecodeWs w = decode_ws_layout(*dims, plan->batch, plan->n_items, q_len, compact && fast);
   char *base = static_cast<char *>(ws);
   int32_t *status = reinterpret_cast<int32_t *>(base + w.status);
   WorkItem *items = reinterpret_cast<WorkItem *>(base + w.items);
   SeqInfo *seqs = reinterpret_cast<SeqInfo *>(base + w.seqs);
-  if (!plan_copy_current(ws, plan->id)) {
-    if (hipMemcpyAsync(items, plan->host_block, plan->host_block_bytes, hipMemcpyHostToDevice, s) != hipSuccess)
-      return MLA_ERR_HIP;
-    plan_copy_record(ws, plan->id);
-  }
+  // the absorb kernel checks this copy against the plan (and refetches it)
+  // before the kernels after it read it
+  const PlanRef pr{plan->host_dev, items, static_cast<int32_t>(plan->host_block_bytes / 16), plan->hash};
   float *opart = reinterpret_cast<float *>(base + w.opart);
   uint16_t *opart16 = reinterpret_cast<uint16_t *>(base + w.opart);
   float *lse = reinterpret_cast<float *>(base + w.lse);
-  if (decode_fast_path(*dims, *cache, qw)) {
+  if (fast) {
     uint16_t *q = reinterpret_cast<uint16_t *>(base + w.q);
     MLA_LAUNCH(s, K_ABSORB_FAST,
-               launch_absorb_fast(s, *dims, plan->batch, q_len, q_nope, q_rope, q_pos, w_uk, seqs, q));
+               launch_absorb_fast(s, *dims, plan->batch, q_len, q_nope, q_rope, q_pos, w_uk, cache->seq_len, q, pr));
     MLA_LAUNCH(s, cache->latent_dtype == MLA_FP8_E4M3 ? K_DECODE_FP8 : K_DECODE_BF16,
                launch_decode_fast(s, *dims, *cache, q_len, plan->n_items, items, seqs, q, opart16, lse, status));
     MLA_LAUNCH(s, K_COMBINE_FAST,
-               launch_combine_fast(s, *dims, *cache, q_len, seqs, opart16, lse, static_cast<const uint16_t *>(w_uv),
-                                   o, od));
+               launch_combine_fast(s, *dims, *cache, q_len, plan->n_items, seqs, opart16, lse,
+                                   static_cast<const uint16_t *>(w_uv), o, od, status));
   } else {
     float *q = reinterpret_cast<float *>(base + w.q);
     MLA_LAUNCH(s, K_ABSORB_GENERIC,
-               launch_absorb_generic(s, *dims, plan->batch, q_nope, q_rope, q_pos, w_uk, qw, seqs, q));
+               launch_absorb_generic(s, *dims, plan->batch, q_nope, q_rope, q_pos, w_uk, qw, cache->seq_len, q, pr));
     MLA_LAUNCH(s, K_DECODE_GENERIC,
                launch_decode_generic(s, *dims, *cache, plan->n_items, items, seqs, q, opart, lse, status));
     MLA_LAUNCH(s, K_COMBINE_GENERIC,
-               launch_combine_generic(s, *dims, *cache, seqs, opart, lse, w_uv, qw, o, od));
+               launch_combine_generic(s, *dims, *cache, plan->n_items, seqs, opart, lse, w_uv, qw, o, od, status));
   }
   return MLA_OK;
 }

@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "../../include/mla.h"
+#include "plan_hash.hpp"
 
 namespace mla {
 
@@ -53,16 +54,19 @@ struct alignas(16) SeqInfo {
 }  // namespace mla
 
 // The plan is host-owned; items and seq info live in one pinned host block
-// that each decode call copies into the workspace.
+// (device-readable). The first kernel of each decode checks the workspace's
+// copy of it against the block's checksum and fetches the block again when
+// they differ.
 struct mla_plan {
   int32_t batch = 0;
   int32_t n_items = 0;
   int32_t chunk = 0;
   int32_t n_workers = 0;
-  uint64_t id = 0;             // unique per plan made in this process
-  void *host_block = nullptr;  // pinned: [n_items WorkItem][batch SeqInfo]
-  size_t host_block_bytes = 0;
+  void *host_block = nullptr;      // [n_items WorkItem][batch SeqInfo], pinned when a device is there
+  const void *host_dev = nullptr;  // the same block's device address (nullptr: not pinned)
   bool pinned = false;
+  size_t host_block_bytes = 0;
+  uint64_t hash = 0;               // plan_chunk_hash sum over the block
   std::vector<int32_t> lens;
   const mla::WorkItem *items() const { return static_cast<const mla::WorkItem *>(host_block); }
   const mla::SeqInfo *seqs() const {
@@ -73,18 +77,22 @@ struct mla_plan {
 
 namespace mla {
 
-// Workspace layout for decode (byte offsets from ws).
+// Workspace layout for decode (byte offsets from ws). The plan copy comes
+// last, past the region an append's partial products use whenever the
+// decode arrays are larger than those (so a decode step's append leaves it
+// intact; if it does not, the copy is fetched again).
 struct DecodeWs {
   size_t status = 0;  // int32 status word (256 bytes reserved)
-  size_t items = 0;   // WorkItem[n_items]
-  size_t seqs = 0;    // SeqInfo[batch]
-  size_t q = 0;       // absorbed query [batch, H, d_c + d_rope]: bf16 (fast) or f32
-  size_t opart = 0;   // normalised split partials [n_items, H, d_c]: f32, or fp16 on the matrix-core path
+  size_t q = 0;       // absorbed query [batch, H, d_c + d_rope]: fp16 (matrix-core path) or f32
+  size_t opart = 0;   // normalised split partials [n_items, H, d_c]: fp16 (matrix-core path) or f32
   size_t lse = 0;     // f32 [n_items, H]
+  size_t items = 0;   // WorkItem[n_items]
+  size_t seqs = 0;    // SeqInfo[batch] (directly after the items: one copy of the plan's block)
   size_t total = 0;
 };
-// q_len new query tokens per sequence multiply every per-head array.
-DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items, int32_t q_len = 1);
+// q_len new query tokens per sequence multiply every per-head array; fast
+// selects the matrix-core path's 2-byte query and partials.
+DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items, int32_t q_len, bool fast);
 
 struct AppendWs {
   size_t status = 0;
@@ -116,14 +124,19 @@ hipError_t launch_append_finish(hipStream_t s, const mla_dims &d, const mla_cach
                                 const float *partial, int ksplit, int32_t *status);
 hipError_t launch_advance_len(hipStream_t s, const mla_cache &c, int32_t n_new);
 
+// The absorb kernels, the first of every decode, also check the
+// workspace's plan copy (one workgroup, see PlanRef). They take the query
+// position from the cache's seq_len (equal to the plan's length, or the
+// split-K kernel reports MLA_ERR_PLAN and zeroes the output).
 hipError_t launch_absorb_generic(hipStream_t s, const mla_dims &d, int32_t batch,
                                  const void *q_nope, const void *q_rope, const int32_t *q_pos,
-                                 const void *w_uk, mla_dtype qw, const SeqInfo *seqs, float *q_out);
+                                 const void *w_uk, mla_dtype qw, const int32_t *seq_len, float *q_out,
+                                 const PlanRef &plan);
 // The matrix-core launchers take q_len new query tokens per sequence (1 for
 // a plain decode): heads become (token, head) pairs, token-major.
 hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, int32_t q_len,
                               const void *q_nope, const void *q_rope, const int32_t *q_pos,
-                              const void *w_uk, const SeqInfo *seqs, uint16_t *q_out);
+                              const void *w_uk, const int32_t *seq_len, uint16_t *q_out, const PlanRef &plan);
 
 hipError_t launch_decode_generic(hipStream_t s, const mla_dims &d, const mla_cache &c,
                                  int32_t n_items, const WorkItem *items, const SeqInfo *seqs,
@@ -132,11 +145,12 @@ hipError_t launch_decode_fast(hipStream_t s, const mla_dims &d, const mla_cache 
                               int32_t n_items, const WorkItem *items, const SeqInfo *seqs,
                               const uint16_t *q, uint16_t *opart, float *lse, int32_t *status);
 
-hipError_t launch_combine_generic(hipStream_t s, const mla_dims &d, const mla_cache &c,
+hipError_t launch_combine_generic(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,
                                   const SeqInfo *seqs, const float *opart, const float *lse,
-                                  const void *w_uv, mla_dtype qw, void *o, mla_dtype od);
-hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, const SeqInfo *seqs,
-                               const uint16_t *opart, const float *lse, const uint16_t *w_uv, void *o, int o_bf16);
+                                  const void *w_uv, mla_dtype qw, void *o, mla_dtype od, int32_t *status);
+hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, int32_t n_items,
+                               const SeqInfo *seqs, const uint16_t *opart, const float *lse, const uint16_t *w_uv,
+                               void *o, int o_bf16, int32_t *status);
 
 hipError_t launch_copy(hipStream_t s, void *dst, const void *src, size_t n16);
 hipError_t launch_read(hipStream_t s, const void *src, size_t n16, uint32_t *sink);

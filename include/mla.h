@@ -33,8 +33,15 @@
  *    its output is set to zero.
  *  - The library never allocates device memory. The caller owns the cache,
  *    weights, activations, outputs and workspace; the library owns only the
- *    host-side plan (pinned host memory) between mla_plan_create() and
- *    mla_plan_destroy().
+ *    host-side plan (pinned, device-mapped host memory) between
+ *    mla_plan_create() and mla_plan_destroy().
+ *  - A workspace carries nothing a later call depends on except its status
+ *    word: between calls the caller may reuse it for other data, or pass it
+ *    to calls on other plans. (Each decode keeps a copy of its plan's work
+ *    list in the workspace; the first kernel of every decode checks that
+ *    copy against the plan's checksum and fetches the plan again from its
+ *    pinned host block when they differ. The library keeps no record of
+ *    which workspace holds which plan.)
  *  - No C++ exception crosses this boundary.
  *  - Calls on different streams may run concurrently if they use different
  *    workspaces.
@@ -133,8 +140,12 @@ typedef struct mla_plan mla_plan;
  *   ws      workspace of at least mla_append_workspace_bytes() bytes; its
  *           first 256 bytes hold the device status word (see
  *           mla_workspace_init).
- * A sequence with seq_len[b] + n_new > seq_cap[b] is left untouched and
- * MLA_ERR_CAPACITY is recorded in the status word. */
+ * A sequence whose new tokens do not fit is left untouched (no row
+ * written, seq_len unchanged) and its error recorded in the status word:
+ * MLA_ERR_CAPACITY when seq_len[b] + n_new > seq_cap[b], or (contiguous)
+ * seq_start[b] + seq_len[b] + n_new > n_rows, or (paged) the new tokens
+ * pass max_blocks * block_tokens; MLA_ERR_PLAN when a block a new token
+ * falls in has an id outside the cache. The other sequences append. */
 size_t mla_append_workspace_bytes(const mla_dims *dims, int32_t batch, int32_t n_new);
 mla_status mla_append(const mla_dims *dims, const mla_cache *cache, const void *h,
                       int32_t n_new, const void *w_dkv, const void *w_kr,
@@ -154,7 +165,11 @@ mla_status mla_append(const mla_dims *dims, const mla_cache *cache, const void *
  * sequence alone runs fastest in 64 items of two tiles).
  * With an explicit n_workers the chunks are as short as that count needs
  * (one 32-token tile at the least). The plan is deterministic in its inputs
- * and reusable across layers and calls with the same lengths. Returns
+ * and reusable across layers and calls with the same lengths. Its work list
+ * lives in pinned host memory mapped for the current device, which the
+ * decode's first kernel reads when a workspace's copy of it does not match;
+ * where no such memory can be had (no device), the plan is made in ordinary
+ * memory for inspection and decodes refuse it (MLA_ERR_HIP). Returns
  * MLA_ERR_INVALID_ARG for batch < 1, a negative length or a null pointer. */
 mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32_t batch,
                            int32_t n_workers, mla_plan **out);
@@ -252,7 +267,10 @@ int32_t mla_abi_version(void);
 
 /* ------------------------------------------------------------- profiling
  * Optional per-kernel timing with HIP events recorded around each kernel
- * this library launches (kernel ids: see mla_prof_kernel_name).
+ * this library launches (kernel ids: see mla_prof_kernel_name). While
+ * recording, every call synchronises its stream before each kernel it
+ * launches, so each recorded kernel starts on an idle stream (its time is
+ * its own, not the wait for earlier work); calls are therefore slower.
  * mla_prof_begin enables recording of up to max_records launches;
  * mla_prof_end synchronises the recorded events, writes the summed
  * milliseconds and launch counts per kernel id into ms[n] / count[n] and

@@ -179,6 +179,52 @@ def test_validation_rejects_before_launch():
     assert lib.mla_workspace_init(None, 256, None) == 1
 
 
+def test_tensor_calls_check_dtypes_and_shapes():
+    """The tensor-level calls refuse, before touching a device, activations
+    and weights of mixed dtypes or of sizes that do not match the dims and
+    the plan's batch (either would make a kernel read past a buffer), and a
+    self-allocated workspace on an explicit stream (it would be freed while
+    the stream may still use it)."""
+    import torch
+    d = d128()
+    plan = m.mla_plan_create(d, [10, 20], 4)
+    c = _cache_struct()
+    bf = torch.bfloat16
+
+    def z(*shape, dt=bf):
+        return torch.zeros(shape, dtype=dt)
+
+    ok = dict(q_nope=z(2, 128, 128), q_rope=z(2, 128, 64), w_uk=z(128, 128, 512), w_uv=z(128, 128, 512))
+    bad = [
+        dict(w_uk=z(128, 128, 512, dt=torch.float32)),  # f32 weights with bf16 queries
+        dict(q_rope=z(2, 128, 64, dt=torch.float32)),
+        dict(q_nope=z(3, 128, 128)),                    # batch differs from the plan
+        dict(q_nope=z(2, 128, 128, dt=torch.float16)),  # not f32 or bf16
+        dict(w_uv=z(128, 128, 256)),
+    ]
+    for over in bad:
+        args = dict(ok, **over)
+        with pytest.raises(ValueError):
+            m.decode(d, c, plan, args["q_nope"], args["q_rope"], args["w_uk"], args["w_uv"])
+    with pytest.raises(ValueError):
+        m.decode(d, c, plan, **ok, out=z(2, 128, 64, dt=torch.float32))
+    with pytest.raises(ValueError):
+        m.decode(d, c, plan, **ok, stream=1234)
+    da = m.dims(128, 512, 64, 128, 128, d_model=256)
+    h, wd, wk = z(2, 1, 256), z(512, 256), z(64, 256)
+    with pytest.raises(ValueError):
+        m.append(da, c, h, wd, z(64, 256, dt=torch.float32))
+    with pytest.raises(ValueError):
+        m.append(da, c, z(2, 1, 128), wd, wk)
+    with pytest.raises(ValueError):
+        m.append(da, c, z(3, 1, 256), wd, wk)
+    with pytest.raises(ValueError):
+        m.append(da, c, h, wd, wk, stream=1234)
+    with pytest.raises(ValueError):
+        m.append_decode(da, c, plan, h, wd, wk, ok["q_nope"].float(), ok["q_rope"].float(), ok["w_uk"].float(),
+                        ok["w_uv"].float())
+
+
 def test_workspace_sizes_grow_with_plan():
     d = d128()
     small = m.mla_decode_workspace_bytes(d, m.mla_plan_create(d, [100], 4))
