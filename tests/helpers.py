@@ -186,6 +186,35 @@ def oracle_decode(case, pairs=None, absorbed=False, with_append=True, q_pos=None
               q_pos=q_pos, pairs=pairs)
 
 
+def oracle_full(case, with_append=True, rows=None, scale=None):
+    """Every output [B, H, d_v] of the case from the oracle's all-heads
+    absorbed form (pinned equal to the definition), one sequence at a time:
+    only that sequence's rows are decoded to fp64, so full-size workloads fit
+    in host memory. When the case appends, the oracle's own appended rows
+    stand at their positions (end to end, as the GPU appends them itself).
+    ``rows`` / ``scale`` replace the case's stored rows (e.g. read back)."""
+    rows = case.rows if rows is None else rows
+    scale = case.scale if scale is None else scale
+    lens = case.lens.astype(np.int64)
+    ap = oracle_append(case) if (case.n_new and with_append) else None
+    qn = act_to_f64(case.q_nope, case.act_dtype)
+    qr = act_to_f64(case.q_rope, case.act_dtype)
+    wuk = act_to_f64(case.w_uk, case.act_dtype)
+    wuv = act_to_f64(case.w_uv, case.act_dtype)
+    out = np.zeros((case.B, case.H, case.d_v))
+    for b in range(case.B):
+        L = int(lens[b])
+        s0 = int(case.seq_start[b])
+        sc = None if scale is None else scale[s0:s0 + L]
+        C, R = omla.decode_rows(rows[s0:s0 + L], case.latent_dtype, case.rope_dtype, case.d_c, case.d_rope, sc)
+        if ap is not None:
+            C = np.concatenate([C, ap["c"][b]])
+            R = np.concatenate([R, ap["k_rope"][b]])
+            L += case.n_new
+        out[b] = omla.decode_absorbed_heads(C, R, qn[b], qr[b], wuk, wuv, case.softmax_scale, case.rope_base, L - 1)
+    return out
+
+
 def oracle_decode_multi(case, q_nope, q_rope, triples=None, absorbed=True, q_pos=None, C=None, R=None):
     """Oracle output of a several-token decode (queries [B, q_len, H, *] in
     storage dtype)."""

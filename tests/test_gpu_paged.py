@@ -2,13 +2,21 @@
 32 rows): decode, several-token decode and append on a shuffled paged copy
 of a case give bit-for-bit the results of the contiguous cache (the kernels
 see the same rows, only their addresses move), on the matrix-core and the
-generic path; a block id outside the cache is reported, not followed."""
+generic path, and every paged output is also compared with the oracle at
+the workloads' tolerances (rms over the whole output); a block id outside
+the cache is reported, not followed, and an append into such a block, or
+past the cache's rows, leaves the sequence untouched."""
 import numpy as np
 import pytest
 import torch
 
 import mla_synth
-from tests.helpers import DeviceRun, TOL_F32_ABS, make, max_abs_err, oracle_decode, paged_layout, to_np
+from tests.helpers import (DeviceRun, TOL_BF16_REL, TOL_F32_ABS, TOL_FP8_REL, make, max_abs_err, oracle_decode,
+                           oracle_decode_multi, oracle_full, paged_layout, rel_rms_err, to_np)
+
+
+def tol(latent):
+    return TOL_FP8_REL if latent == "fp8" else TOL_BF16_REL
 
 pytestmark = pytest.mark.gpu
 
@@ -31,16 +39,22 @@ def test_paged_decode_matches_contiguous(gpu, latent, bt):
     b = paged.decode(plan=plan)
     assert flat.status() == 0 and paged.status() == 0
     assert torch.equal(a, b)
+    assert rel_rms_err(to_np(b), oracle_full(case)) <= tol(latent)
 
 
-def test_paged_multi_token_decode_matches_contiguous(gpu):
-    case = v3_case("bf16", 101)
+@pytest.mark.parametrize("latent", ["bf16", "fp8"])
+def test_paged_multi_token_decode_matches_contiguous(gpu, latent):
+    case = v3_case(latent, 101)
     qn, qr = mla_synth.multi_queries(case, 3, seed=4)
     flat = DeviceRun(gpu, case)
     paged = DeviceRun(gpu, case, paged=paged_layout(case, 64, seed=5) + (64,))
     plan = flat.plan(n_workers=16)
-    assert torch.equal(flat.decode_multi(3, qn, qr, plan=plan), paged.decode_multi(3, qn, qr, plan=plan))
+    a = flat.decode_multi(3, qn, qr, plan=plan)
+    b = paged.decode_multi(3, qn, qr, plan=plan)
     assert flat.status() == 0 and paged.status() == 0
+    assert torch.equal(a, b)
+    ref = oracle_decode_multi(case, qn, qr, absorbed=True)
+    assert rel_rms_err(to_np(b), ref) <= tol(latent)
 
 
 def test_paged_generic_path_fp32(gpu):
@@ -69,6 +83,7 @@ def test_paged_append_then_decode_matches_contiguous(gpu, latent):
     b = paged.append_decode(plan=plan)
     assert flat.status() == 0 and paged.status() == 0
     assert torch.equal(a, b)
+    assert rel_rms_err(to_np(b), oracle_full(case)) <= tol(latent)
     # the appended rows sit where the block table maps them, byte for byte
     rows_f = flat.t["rows"].cpu().numpy()
     rows_p = paged.t["rows"].cpu().numpy()
@@ -91,3 +106,46 @@ def test_paged_bad_block_id_is_reported(gpu):
     paged = DeviceRun(gpu, case, paged=(rows, scale, table, 64))
     paged.decode(n_workers=4)
     assert paged.status() == 6  # MLA_ERR_PLAN
+
+
+def test_paged_append_into_a_bad_block_leaves_the_sequence_untouched(gpu):
+    """The new token of sequence 1 falls in a block whose id is outside the
+    cache: that sequence's rows and length stay as they were (MLA_ERR_PLAN),
+    the other sequences append."""
+    lens = [3, 64, 40]
+    case = make(B=len(lens), lens=("list", lens), latent_dtype="bf16", rope_dtype="bf16", act_dtype="bf16",
+                seed=105, n_new=1, d_model=1024, extra_cap=30, **V3)
+    rows, scale, table = paged_layout(case, 32, seed=9)
+    table[1, 64 // 32] = 1 << 20  # the block of sequence 1's token 64
+    run = DeviceRun(gpu, case, paged=(rows, scale, table, 32))
+    before = run.t["rows"].cpu().numpy().copy()
+    run.append()
+    assert run.status() == 6  # MLA_ERR_PLAN
+    assert run.t["seq_len"].cpu().tolist() == [4, 64, 41]
+    after = run.t["rows"].cpu().numpy()
+    changed = np.flatnonzero(np.any(after != before, axis=1))
+    expect = sorted(int(table[b, L // 32]) * 32 + L % 32 for b, L in ((0, 3), (2, 40)))
+    assert changed.tolist() == expect
+
+
+@pytest.mark.parametrize("path", ["fast", "generic"])
+def test_append_past_the_cache_rows_leaves_the_sequence_untouched(gpu, path, monkeypatch):
+    """A contiguous sequence whose capacity still has room but whose next row
+    lies past the cache's last row (n_rows) is refused: length and rows
+    unchanged (MLA_ERR_CAPACITY); the others append. Both append paths."""
+    lens = [5, 9]
+    case = make(B=2, lens=("list", lens), latent_dtype="bf16", rope_dtype="bf16", act_dtype="bf16", seed=106,
+                n_new=1, d_model=1024, extra_cap=8, **V3)
+    if path == "generic":
+        monkeypatch.setenv("MLA_FORCE_GENERIC", "1")
+    run = DeviceRun(gpu, case)
+    # the cache as the caller describes it ends right after sequence 1's 9th row
+    last = int(case.seq_start[1]) + lens[1]
+    run.cache.n_rows = last
+    before = run.t["rows"].cpu().numpy().copy()
+    run.append()
+    assert run.status() == 3  # MLA_ERR_CAPACITY
+    assert run.t["seq_len"].cpu().tolist() == [6, 9]
+    after = run.t["rows"].cpu().numpy()
+    changed = np.flatnonzero(np.any(after != before, axis=1)).tolist()
+    assert changed == [int(case.seq_start[0]) + lens[0]]
