@@ -10,10 +10,15 @@ resident in HBM before timing; each step reads a different copy of the cache
 and weights so that no step is served from the 256 MB Infinity Cache.
 
 Prints one JSON line. value = latent-cache bytes read per step / step time
-(GB/s), timed over exactly `--steps` steps as a caller runs them. The same
-steps then run once more with an event pair recorded by every kernel dispatch
-(hipExtLaunchKernelGGL, on the launch stream): those give the per-kernel
-durations and the roofline object, which reports the split-K kernel alone.
+(GB/s), timed over exactly `--steps` steps as a caller runs them (an event
+pair in the stream around each step gives the p10/p50/p90 of the step time).
+The same steps then run once more with the library's per-kernel profiling on
+(each kernel starts on an idle stream and records its own start and end):
+those give the per-kernel durations and the roofline object, which reports
+the split-K kernel alone. The other workloads (uniform 8K batch, one 4K
+sequence, 4 x 128K, 128 sequences with fp8 latents and a fused append, and
+the ragged batch with 4 query tokens per sequence) are measured the same way
+and reported under "workloads".
 """
 import argparse
 import hashlib
@@ -23,10 +28,13 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+FP16_PEAK_FLOPS = 2.5e15  # MI355X dense fp16 / bf16 matrix cores, published
 METRIC = "MLA decode latent-cache read GB/s (% of HBM peak) + tokens/s, B=32 ctx=8K"
 DEFAULT_WORKLOAD = "v3_b32_ragged"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "splitk_decode_bf16_traffic.json")
@@ -40,8 +48,8 @@ def parse():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
-    p.add_argument("--extra", action="store_true",
-                   help="also time the other workloads (uniform 8K batch, one 4K sequence, 4 x 128K, fp8 + append)")
+    p.add_argument("--headline-only", action="store_true",
+                   help="time only the headline workload (the others are measured by default)")
     p.add_argument("--calib-mib", type=int, default=0,
                    help="first run one plain device copy of this many MiB (mla_calib_copy), a kernel of known "
                         "traffic for scaling hardware byte counters")
@@ -50,7 +58,7 @@ def parse():
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("k_splitk.hip", "device_util.hpp", "mla_internal.hpp"):
+    for f in ("k_splitk.hip", "device_util.hpp", "mla_internal.hpp", "splitk_addr.hpp", "plan_hash.hpp"):
         with open(os.path.join(ROOT, "compressed_kv_cache_absorbed_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -103,7 +111,6 @@ def run_workload(m, torch, name, steps, warmup, q_len=1):
     plan = m.mla_plan_create(d, lens.tolist(), 0)
     nbytes = m.mla_decode_workspace_bytes(d, plan)
     if q_len > 1:
-        import numpy as np
         qn, qr = mla_synth.multi_queries(case, q_len, seed=17)
         qn = torch.from_numpy(qn.view(np.int16)).to(dev)
         qr = torch.from_numpy(qr.view(np.int16)).to(dev)
@@ -132,48 +139,63 @@ def run_workload(m, torch, name, steps, warmup, q_len=1):
         step(k)
     torch.cuda.synchronize()
     assert m.mla_device_error(ws) == 0
-    # timed region 1: the steps as a caller runs them (no profiling events)
+    # timed region 1: the steps as a caller runs them (no profiling), with an
+    # event pair in the stream around each step for the step-time spread
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
+        ev[k][0].record()
         step(k)
+        ev[k][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
-    # timed region 2: the same steps again with an event pair recorded by
-    # every kernel dispatch (per-kernel durations; the events themselves add
-    # some microseconds per dispatch, so region 1 gives the step time)
-    m.mla_prof_begin(max_records=8 * steps + 16)
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    # timed region 2: the same steps with the library's per-kernel profiling
+    # (each kernel starts on an idle stream and records its own start and end)
+    per_kernel = {}
     torch.cuda.synchronize()
     t2 = time.perf_counter()
     for k in range(steps):
+        m.mla_prof_begin(max_records=16)
         step(k)
+        for name, (ms, n) in m.mla_prof_end().items():
+            per_kernel.setdefault(name, []).append(ms / n)
     torch.cuda.synchronize()
     t3 = time.perf_counter()
-    prof = m.mla_prof_end()
     assert m.mla_device_error(ws) == 0
     ms_step_profiled = (t3 - t2) * 1e3 / steps
     kname = "decode_fp8" if case.latent_dtype == "fp8" else "decode_bf16"
-    kms, kn = prof[kname]
-    splitk_ms = kms / kn
-    return dict(case=case, t=t, o=o, d=d, plan=plan, cache_bytes=cache_bytes, ms_step=ms_step,
-                ms_step_profiled=ms_step_profiled, splitk_ms=splitk_ms, splitk_name=kname,
-                prof={k: v[0] / v[1] for k, v in prof.items()}, n_items=plan.n_items, ncopy=ncopy, q_len=q_len)
+    return dict(case=case, t=t, o=o, d=d, plan=plan, cache_bytes=cache_bytes, ms_step=ms_step, step_ms=step_ms,
+                ms_step_profiled=ms_step_profiled, splitk=per_kernel[kname], splitk_ms=float(np.mean(per_kernel[kname])),
+                splitk_name=kname, per_kernel=per_kernel, n_items=plan.n_items, ncopy=ncopy, q_len=q_len)
+
+
+def pct(xs):
+    """p10 / p50 / p90 of a list of times (ms), rounded."""
+    q = np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])
+    return {"p10": round(float(q[0]), 5), "p50": round(float(q[1]), 5), "p90": round(float(q[2]), 5)}
 
 
 def workload_summary(res):
-    """One line per extra workload: step and split-K rates, per-kernel times."""
+    """One workload: step time (mean and spread), rates against the HBM and
+    fp16 matrix-core peaks for the split-K kernel, per-kernel medians."""
     case, ql = res["case"], res["q_len"]
     flops = 2.0 * case.H * ql * (2 * case.d_c + case.d_rope) * float((case.lens + case.n_new).sum())
+    sk = res["splitk_ms"]
     return {"batch": case.B, "query_tokens_per_seq": ql, "cache_tokens": int((case.lens + case.n_new).sum()),
-            "latent_dtype": case.latent_dtype, "appends": int(case.n_new),
-            "ms_per_step": round(res["ms_step"], 5),
+            "latent_dtype": case.latent_dtype, "appends": int(case.n_new), "split_items": res["n_items"],
+            "cache_bytes_per_step": res["cache_bytes"],
+            "ms_per_step": round(res["ms_step"], 5), "step_ms": pct(res["step_ms"]),
             "tokens_per_s": round(case.B * ql / (res["ms_step"] * 1e-3), 1),
             "cache_GBs_step": round(res["cache_bytes"] / (res["ms_step"] * 1e-3) / 1e9, 2),
-            "splitk_GBs": round(res["cache_bytes"] / (res["splitk_ms"] * 1e-3) / 1e9, 2),
-            "splitk_hbm_frac": round(res["cache_bytes"] / (res["splitk_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "splitk_mfma_frac_fp16": round(flops / (res["splitk_ms"] * 1e-3) / 2.5e15, 4),
-            "kernel_ms": {k: round(v, 5) for k, v in res["prof"].items()}}
+            "splitk_ms_mean": round(sk, 5), "splitk_ms": pct(res["splitk"]),
+            "splitk_GBs": round(res["cache_bytes"] / (sk * 1e-3) / 1e9, 2),
+            "splitk_hbm_frac": round(res["cache_bytes"] / (sk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "splitk_mfma_frac_fp16": round(flops / (sk * 1e-3) / FP16_PEAK_FLOPS, 4),
+            "step_over_splitk": round(res["ms_step"] / sk, 3),
+            "kernel_ms_p50": {k: round(float(np.median(v)), 5) for k, v in res["per_kernel"].items()}}
 
 
 def sampled_parity(res, n=8):
@@ -198,11 +220,24 @@ def cpu_baseline(res, budget_s):
     import numpy as np
     from oracle import mla as omla
     from tests.helpers import act_to_f64, oracle_cache
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] + [1])
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:
         cores = os.cpu_count()
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     case = res["case"]
     rng = np.random.default_rng(11)
     seqs = sorted(set(int(x) for x in rng.choice(case.B, size=min(4, case.B), replace=False)))
@@ -225,7 +260,8 @@ def cpu_baseline(res, budget_s):
     per_tok_head = elapsed / tokens
     step_s = per_tok_head * float(case.lens.sum()) * case.H
     return {"value": round(res["cache_bytes"] / step_s / 1e9, 6), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle", "step_seconds": round(step_s, 3),
+            "kind": "oracle", "step_seconds": round(step_s, 3), "cpu_model": cpu_model,
+            "host_cpus": os.cpu_count(), "blas": blas,
             "sample": f"{done} (sequence, head) pairs of the workload ({tokens} token-heads, "
                       f"{elapsed:.1f} s of fp64 non-absorbed decode), scaled to {case.B} sequences x {case.H} heads"}
 
@@ -276,6 +312,7 @@ def main():
     ach = res["cache_bytes"] / (res["splitk_ms"] * 1e-3) / 1e9
     traffic = measured_traffic(res["cache_bytes"])
     par = sampled_parity(res)
+    head = workload_summary(res)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -296,21 +333,26 @@ def main():
                    "split_items": res["n_items"], "input_copies_rotated": res["ncopy"]},
         "tokens_per_s": round(case.B / (res["ms_step"] * 1e-3), 1),
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "kernel_ms": {k: round(v, 5) for k, v in res["prof"].items()},
-        "ms_per_step_with_kernel_events": round(res["ms_step_profiled"], 5),
+        "step_ms": head["step_ms"],
+        "step_over_splitk": head["step_over_splitk"],
+        "kernel_ms_p50": head["kernel_ms_p50"],
+        "ms_per_step_profiled": round(res["ms_step_profiled"], 5),
         "parity_sampled_max_err_over_rms": round(par, 6),
         "roofline": {"kernel": "splitk_decode (bf16 latent)", "bound": "hbm", "achieved": round(ach, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "per_launch_bytes": res["cache_bytes"], "avg_launch_ms": round(res["splitk_ms"], 5),
+                     "launch_ms": head["splitk_ms"], "mfma_frac_fp16": head["splitk_mfma_frac_fp16"],
                      "stream_read_GBs": round(ceiling, 1), "frac_of_stream_read": round(ach / ceiling, 4)},
     }
-    if a.extra:
-        out["other_workloads"] = {}
+    if not a.headline_only:
+        out["workloads"] = {}
         for name, ql in (("v3_b32_8k", 1), ("v3_b1_4k", 1), ("v3_b4_128k", 1), ("v3_b128_fp8", 1),
                          ("v3_b32_ragged", 4)):
             r = run_workload(m, torch, name, a.steps, a.warmup, q_len=ql)
-            out["other_workloads"][name if ql == 1 else f"{name}_{ql}_query_tokens"] = workload_summary(r)
+            out["workloads"][name if ql == 1 else f"{name}_{ql}_query_tokens"] = workload_summary(r)
+            print(f"# {name} q_len {ql}: {out['workloads'][name if ql == 1 else f'{name}_{ql}_query_tokens']['ms_per_step']} ms/step",
+                  file=sys.stderr, flush=True)
             del r
             torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
