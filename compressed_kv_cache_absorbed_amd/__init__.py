@@ -13,7 +13,7 @@ __all__ = [
     "F32", "BF16", "FP8_E4M3", "MLAError", "MlaDims", "MlaCache", "Plan", "load", "lib_path",
     "dims", "cache", "mla_plan_create", "mla_append_workspace_bytes",
     "mla_decode_workspace_bytes", "mla_workspace_bytes", "mla_append", "mla_decode", "mla_append_decode",
-    "mla_decode_multi", "mla_decode_multi_workspace_bytes",
+    "mla_decode_multi", "mla_decode_multi_workspace_bytes", "mla_decode_noalloc",
     "mla_workspace_init", "mla_device_error", "mla_status_str", "mla_abi_version",
     "mla_prof_begin", "mla_prof_end", "mla_calib_copy", "mla_calib_read", "EXPORTED",
     "workspace", "decode", "append", "append_decode",
@@ -27,7 +27,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "M
 EXPORTED = [
     "mla_append_workspace_bytes", "mla_append", "mla_plan_create", "mla_plan_destroy",
     "mla_plan_num_items", "mla_plan_item", "mla_decode_workspace_bytes", "mla_workspace_bytes", "mla_decode",
-    "mla_decode_multi_workspace_bytes", "mla_decode_multi", "mla_append_decode", "mla_workspace_init", "mla_device_error", "mla_status_str",
+    "mla_decode_multi_workspace_bytes", "mla_decode_multi", "mla_decode_noalloc", "mla_append_decode",
+    "mla_workspace_init", "mla_device_error", "mla_status_str",
     "mla_abi_version", "mla_prof_begin", "mla_prof_end", "mla_prof_kernel_name",
     "mla_prof_num_kernels", "mla_calib_copy", "mla_calib_read",
 ]
@@ -86,6 +87,8 @@ def load():
         "mla_decode_multi_workspace_bytes": (ctypes.c_size_t, [_P, _P, ctypes.c_int32]),
         "mla_decode_multi": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_int, _P,
                                             ctypes.c_int, _P, ctypes.c_size_t, _P]),
+        "mla_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
+                                              _P]),
         "mla_append_decode": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P,
                                              _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
                                              ctypes.c_size_t, _P]),
@@ -222,6 +225,13 @@ def mla_decode_multi(d, c, plan, q_len, q_nope, q_rope, q_pos, w_uk, w_uv, q_w_d
                                    _ptr(q_rope), _ptr(q_pos), _ptr(w_uk), _ptr(w_uv), q_w_dtype, _ptr(o),
                                    o_dtype, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "mla_decode_multi")
+
+
+def mla_decode_noalloc(d, c, plan, q_nope, q_rope, q_pos, w_uk, w_uv, q_w_dtype, o, o_dtype, dev_status=None,
+                       stream=None):
+    _check(load().mla_decode_noalloc(ctypes.byref(d), ctypes.byref(c), plan.handle, _ptr(q_nope), _ptr(q_rope),
+                                     _ptr(q_pos), _ptr(w_uk), _ptr(w_uv), q_w_dtype, _ptr(o), o_dtype,
+                                     _ptr(dev_status), _stream(stream)), "mla_decode_noalloc")
 
 
 def mla_append_decode(d, c, plan, h, n_new, w_dkv, w_kr, q_nope, q_rope, q_pos, w_uk, w_uv,

@@ -93,7 +93,8 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
                                                           const int32_t *__restrict__ q_pos,
                                                           const uint16_t *__restrict__ w_uk,
                                                           const int32_t *__restrict__ dev_len,
-                                                          uint16_t *__restrict__ Q, PlanRef plan) {
+                                                          uint16_t *__restrict__ Q, PlanRef plan,
+                                                          int32_t *__restrict__ clear_status) {
   using namespace fast;
   constexpr int WROW = 288;  // LDS bytes per W row (128 columns = 256 bytes + 32)
   __shared__ __attribute__((aligned(16))) char smem[DNOPE * WROW];
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
   const int i = blockIdx.x, cq = blockIdx.y, b0 = blockIdx.z * 32;
   const int iw = i % Hr, back = q_len - 1 - i / Hr;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (clear_status != nullptr && i == 0 && cq == 0 && b0 == 0 && tid == 0) clear_status[0] = 0;
   // every global load first, in the order of use: the RoPE inputs, the
   // q_nope fragments, the weight quarter (32 KB: 128 rows x 16 chunks of
   // 16 bytes, 8 per thread)
@@ -561,11 +563,12 @@ hipError_t launch_append_finish(hipStream_t s, const mla_dims &d, const mla_cach
 
 hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, int32_t q_len, const void *q_nope,
                               const void *q_rope, const int32_t *q_pos, const void *w_uk,
-                              const int32_t *seq_len, uint16_t *q_out, const PlanRef &plan) {
+                              const int32_t *seq_len, uint16_t *q_out, const PlanRef &plan,
+                              int32_t *clear_status) {
   const int H = d.n_heads * q_len;
   return launch_kernel(absorb_fast_kernel, dim3(H, fast::DC / 128, (batch + 31) / 32), 256, 0, s, batch, H,
                        d.n_heads, q_len, d.softmax_scale * kLog2e, d.rope_base, static_cast<const uint16_t *>(q_nope),
-                       static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seq_len, q_out, plan);
+                       static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seq_len, q_out, plan, clear_status);
 }
 
 hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, int32_t n_items,

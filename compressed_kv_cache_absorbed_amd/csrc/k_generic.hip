@@ -20,6 +20,10 @@ __global__ void init_kernel(int32_t *status) {
   if (threadIdx.x == 0 && blockIdx.x == 0) status[0] = 0;
 }
 
+__global__ void status_copy_kernel(const int32_t *src, int32_t *dst) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) dst[0] = src[0];
+}
+
 __global__ __launch_bounds__(256) void append_generic_kernel(mla_dims d, mla_cache c, const void *h,
                                                             int32_t n_new, const void *w_dkv,
                                                             const void *w_kr, mla_dtype act,
@@ -79,9 +83,11 @@ __global__ void advance_len_kernel(mla_cache c, int32_t n_new) {
 __global__ __launch_bounds__(256) void absorb_generic_kernel(mla_dims d, const void *q_nope,
                                                             const void *q_rope, const int32_t *q_pos,
                                                             const void *w_uk, mla_dtype qw,
-                                                            const int32_t *dev_len, float *q_out, PlanRef plan) {
+                                                            const int32_t *dev_len, float *q_out, PlanRef plan,
+                                                            int32_t *clear_status) {
   extern __shared__ float qn[];  // [d_nope]
   const int b = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
+  if (clear_status != nullptr && b == 0 && i == 0 && tid == 0) clear_status[0] = 0;
   const int H = d.n_heads, D = d.d_c + d.d_rope;
   const int64_t bi = static_cast<int64_t>(b) * H + i;
   for (int n = tid; n < d.d_nope; n += 256) qn[n] = load_elem(q_nope, bi * d.d_nope + n, qw);
@@ -286,6 +292,10 @@ hipError_t launch_init(hipStream_t s, int32_t *status) {
   return launch_kernel(init_kernel, 1, 64, 0, s, status);
 }
 
+hipError_t launch_status_copy(hipStream_t s, const int32_t *src, int32_t *dst) {
+  return launch_kernel(status_copy_kernel, 1, 64, 0, s, src, dst);
+}
+
 hipError_t launch_advance_len(hipStream_t s, const mla_cache &c, int32_t n_new) {
   return launch_kernel(advance_len_kernel, (c.batch + 255) / 256, 256, 0, s, c, n_new);
 }
@@ -302,9 +312,10 @@ hipError_t launch_append_generic(hipStream_t s, const mla_dims &d, const mla_cac
 
 hipError_t launch_absorb_generic(hipStream_t s, const mla_dims &d, int32_t batch, const void *q_nope,
                                  const void *q_rope, const int32_t *q_pos, const void *w_uk,
-                                 mla_dtype qw, const int32_t *seq_len, float *q_out, const PlanRef &plan) {
+                                 mla_dtype qw, const int32_t *seq_len, float *q_out, const PlanRef &plan,
+                                 int32_t *clear_status) {
   return launch_kernel(absorb_generic_kernel, dim3(batch, d.n_heads), 256, sizeof(float) * d.d_nope, s, d, q_nope,
-                       q_rope, q_pos, w_uk, qw, seq_len, q_out, plan);
+                       q_rope, q_pos, w_uk, qw, seq_len, q_out, plan, clear_status);
 }
 
 hipError_t launch_decode_generic(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,

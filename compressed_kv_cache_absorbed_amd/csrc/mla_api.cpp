@@ -426,10 +426,14 @@ mla_status mla_append(const mla_dims *dims, const mla_cache *cache, const void *
 }
 
 // ---------------------------------------------------------------- decode
-static mla_status validate_decode(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
-                                  const void *q_nope, const void *q_rope, const void *w_uk,
-                                  const void *w_uv, mla_dtype qw, const void *o, mla_dtype od,
-                                  void *ws, size_t ws_bytes, int32_t q_len = 1) {
+}  // extern "C"
+
+namespace mla {
+
+mla_status decode_check_args(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
+                             const void *q_nope, const void *q_rope, const void *w_uk, const void *w_uv,
+                             mla_dtype qw, const void *o, mla_dtype od, const void *ws, size_t ws_bytes,
+                             int32_t q_len) {
   mla_status st = check_dims(dims, false, true);
   if (st != MLA_OK) return st;
   st = check_cache(*dims, cache);
@@ -454,13 +458,14 @@ static mla_status validate_decode(const mla_dims *dims, const mla_cache *cache, 
   return MLA_OK;
 }
 
-// compact: the workspace is laid out for the path that runs (2-byte query
-// and partials on the matrix-core path), not for the size the workspace
-// queries report (which serves either path).
-static mla_status do_decode(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
-                            const void *q_nope, const void *q_rope, const int32_t *q_pos,
-                            const void *w_uk, const void *w_uv, mla_dtype qw, void *o, mla_dtype od,
-                            void *ws, hipStream_t s, int32_t q_len = 1, bool compact = false) {
+size_t decode_compact_bytes(const mla_dims &d, const mla_cache &c, const mla_plan &plan, mla_dtype qw) {
+  return decode_ws_layout(d, plan.batch, plan.n_items, 1, decode_fast_path(d, c, qw)).total;
+}
+
+mla_status decode_launch(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan, const void *q_nope,
+                         const void *q_rope, const int32_t *q_pos, const void *w_uk, const void *w_uv, mla_dtype qw,
+                         void *o, mla_dtype od, void *ws, hipStream_t s, int32_t q_len, bool compact,
+                         bool clear_status) {
   const bool fast = decode_fast_path(*dims, *cache, qw);
   const DecodeWs w = decode_ws_layout(*dims, plan->batch, plan->n_items, q_len, compact && fast);
   char *base = static_cast<char *>(ws);
@@ -476,7 +481,8 @@ static mla_status do_decode(const mla_dims *dims, const mla_cache *cache, const 
   if (fast) {
     uint16_t *q = reinterpret_cast<uint16_t *>(base + w.q);
     MLA_LAUNCH(s, K_ABSORB_FAST,
-               launch_absorb_fast(s, *dims, plan->batch, q_len, q_nope, q_rope, q_pos, w_uk, cache->seq_len, q, pr));
+               launch_absorb_fast(s, *dims, plan->batch, q_len, q_nope, q_rope, q_pos, w_uk, cache->seq_len, q, pr,
+                                  clear_status ? status : nullptr));
     MLA_LAUNCH(s, cache->latent_dtype == MLA_FP8_E4M3 ? K_DECODE_FP8 : K_DECODE_BF16,
                launch_decode_fast(s, *dims, *cache, q_len, plan->n_items, items, seqs, q, opart16, lse, status));
     MLA_LAUNCH(s, K_COMBINE_FAST,
@@ -485,7 +491,8 @@ static mla_status do_decode(const mla_dims *dims, const mla_cache *cache, const 
   } else {
     float *q = reinterpret_cast<float *>(base + w.q);
     MLA_LAUNCH(s, K_ABSORB_GENERIC,
-               launch_absorb_generic(s, *dims, plan->batch, q_nope, q_rope, q_pos, w_uk, qw, cache->seq_len, q, pr));
+               launch_absorb_generic(s, *dims, plan->batch, q_nope, q_rope, q_pos, w_uk, qw, cache->seq_len, q, pr,
+                                     clear_status ? status : nullptr));
     MLA_LAUNCH(s, K_DECODE_GENERIC,
                launch_decode_generic(s, *dims, *cache, plan->n_items, items, seqs, q, opart, lse, status));
     MLA_LAUNCH(s, K_COMBINE_GENERIC,
@@ -494,26 +501,30 @@ static mla_status do_decode(const mla_dims *dims, const mla_cache *cache, const 
   return MLA_OK;
 }
 
+}  // namespace mla
+
+extern "C" {
+
 mla_status mla_decode(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
                       const void *q_nope, const void *q_rope, const int32_t *q_pos, const void *w_uk,
                       const void *w_uv, mla_dtype q_w_dtype, void *o, mla_dtype o_dtype, void *ws,
                       size_t ws_bytes, void *stream) {
-  mla_status st = validate_decode(dims, cache, plan, q_nope, q_rope, w_uk, w_uv, q_w_dtype, o, o_dtype,
-                                  ws, ws_bytes);
+  mla_status st = decode_check_args(dims, cache, plan, q_nope, q_rope, w_uk, w_uv, q_w_dtype, o, o_dtype, ws,
+                                    ws_bytes, 1);
   if (st != MLA_OK) return st;
-  return do_decode(dims, cache, plan, q_nope, q_rope, q_pos, w_uk, w_uv, q_w_dtype, o, o_dtype, ws,
-                   static_cast<hipStream_t>(stream));
+  return decode_launch(dims, cache, plan, q_nope, q_rope, q_pos, w_uk, w_uv, q_w_dtype, o, o_dtype, ws,
+                       static_cast<hipStream_t>(stream), 1, false, false);
 }
 
 mla_status mla_decode_multi(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan, int32_t q_len,
                             const void *q_nope, const void *q_rope, const int32_t *q_pos, const void *w_uk,
                             const void *w_uv, mla_dtype q_w_dtype, void *o, mla_dtype o_dtype, void *ws,
                             size_t ws_bytes, void *stream) {
-  mla_status st = validate_decode(dims, cache, plan, q_nope, q_rope, w_uk, w_uv, q_w_dtype, o, o_dtype,
-                                  ws, ws_bytes, q_len);
+  mla_status st = decode_check_args(dims, cache, plan, q_nope, q_rope, w_uk, w_uv, q_w_dtype, o, o_dtype, ws,
+                                    ws_bytes, q_len);
   if (st != MLA_OK) return st;
-  return do_decode(dims, cache, plan, q_nope, q_rope, q_pos, w_uk, w_uv, q_w_dtype, o, o_dtype, ws,
-                   static_cast<hipStream_t>(stream), q_len);
+  return decode_launch(dims, cache, plan, q_nope, q_rope, q_pos, w_uk, w_uv, q_w_dtype, o, o_dtype, ws,
+                       static_cast<hipStream_t>(stream), q_len, false, false);
 }
 
 mla_status mla_append_decode(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
@@ -523,13 +534,13 @@ mla_status mla_append_decode(const mla_dims *dims, const mla_cache *cache, const
                              mla_dtype o_dtype, void *ws, size_t ws_bytes, void *stream) {
   mla_status st = validate_append(dims, cache, h, n_new, w_dkv, w_kr, act_w_dtype, ws, ws_bytes);
   if (st != MLA_OK) return st;
-  st = validate_decode(dims, cache, plan, q_nope, q_rope, w_uk, w_uv, act_w_dtype, o, o_dtype, ws,
-                       ws_bytes);
+  st = decode_check_args(dims, cache, plan, q_nope, q_rope, w_uk, w_uv, act_w_dtype, o, o_dtype, ws, ws_bytes, 1);
   if (st != MLA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = do_append(dims, cache, h, n_new, w_dkv, w_kr, act_w_dtype, ws, s);
   if (st != MLA_OK) return st;
-  return do_decode(dims, cache, plan, q_nope, q_rope, q_pos, w_uk, w_uv, act_w_dtype, o, o_dtype, ws, s);
+  return decode_launch(dims, cache, plan, q_nope, q_rope, q_pos, w_uk, w_uv, act_w_dtype, o, o_dtype, ws, s, 1, false,
+                       false);
 }
 
 // ------------------------------------------------------------- profiling

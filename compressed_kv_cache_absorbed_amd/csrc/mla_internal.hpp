@@ -125,18 +125,21 @@ hipError_t launch_append_finish(hipStream_t s, const mla_dims &d, const mla_cach
 hipError_t launch_advance_len(hipStream_t s, const mla_cache &c, int32_t n_new);
 
 // The absorb kernels, the first of every decode, also check the
-// workspace's plan copy (one workgroup, see PlanRef). They take the query
-// position from the cache's seq_len (equal to the plan's length, or the
-// split-K kernel reports MLA_ERR_PLAN and zeroes the output).
+// workspace's plan copy (one workgroup, see PlanRef) and, when clear_status
+// is not null, zero that status word before the later kernels can set it.
+// They take the query position from the cache's seq_len (equal to the
+// plan's length, or the split-K kernel reports MLA_ERR_PLAN and zeroes the
+// output).
 hipError_t launch_absorb_generic(hipStream_t s, const mla_dims &d, int32_t batch,
                                  const void *q_nope, const void *q_rope, const int32_t *q_pos,
                                  const void *w_uk, mla_dtype qw, const int32_t *seq_len, float *q_out,
-                                 const PlanRef &plan);
+                                 const PlanRef &plan, int32_t *clear_status);
 // The matrix-core launchers take q_len new query tokens per sequence (1 for
 // a plain decode): heads become (token, head) pairs, token-major.
 hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, int32_t q_len,
                               const void *q_nope, const void *q_rope, const int32_t *q_pos,
-                              const void *w_uk, const int32_t *seq_len, uint16_t *q_out, const PlanRef &plan);
+                              const void *w_uk, const int32_t *seq_len, uint16_t *q_out, const PlanRef &plan,
+                              int32_t *clear_status);
 
 hipError_t launch_decode_generic(hipStream_t s, const mla_dims &d, const mla_cache &c,
                                  int32_t n_items, const WorkItem *items, const SeqInfo *seqs,
@@ -153,6 +156,24 @@ hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache
                                void *o, int o_bf16, int32_t *status);
 
 hipError_t launch_copy(hipStream_t s, void *dst, const void *src, size_t n16);
+// *dst = *src for one int32 (a one-thread kernel: capturable, no memcpy node)
+hipError_t launch_status_copy(hipStream_t s, const int32_t *src, int32_t *dst);
+
+// The decode entry points' shared steps (mla_api.cpp). decode_launch runs
+// absorb, split-K and combine with the workspace at ws; compact lays the
+// workspace out for the path that runs (2-byte query and partials on the
+// matrix-core path; decode_compact_bytes gives that size) instead of the
+// size the workspace queries report; clear_status zeroes the status word
+// inside the first kernel.
+mla_status decode_check_args(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
+                             const void *q_nope, const void *q_rope, const void *w_uk, const void *w_uv,
+                             mla_dtype qw, const void *o, mla_dtype od, const void *ws, size_t ws_bytes,
+                             int32_t q_len);
+size_t decode_compact_bytes(const mla_dims &d, const mla_cache &c, const mla_plan &plan, mla_dtype qw);
+mla_status decode_launch(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan, const void *q_nope,
+                         const void *q_rope, const int32_t *q_pos, const void *w_uk, const void *w_uv, mla_dtype qw,
+                         void *o, mla_dtype od, void *ws, hipStream_t s, int32_t q_len, bool compact,
+                         bool clear_status);
 hipError_t launch_read(hipStream_t s, const void *src, size_t n16, uint32_t *sink);
 
 // Profiling hooks used by the launch wrappers in mla_api.cpp. While a

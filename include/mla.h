@@ -254,6 +254,33 @@ mla_status mla_append_decode(const mla_dims *dims, const mla_cache *cache, const
                              const void *w_uk, const void *w_uv, mla_dtype act_w_dtype, void *o,
                              mla_dtype o_dtype, void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------- no workspace
+ * mla_decode_noalloc — mla_decode for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments and results as mla_decode (one
+ * query token per sequence), with no workspace argument. Its workspace is a
+ * fixed array of MLA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held from the library's first use on that GPU until the process ends;
+ * the call allocates nothing (no hipMalloc, no allocating library call).
+ *   dev_status  NULL, or a device int32 (4-byte aligned) that receives the
+ *               call's device status word (an mla_status value: MLA_ERR_PLAN
+ *               for lengths that differ from the plan) once the call's
+ *               kernels have run. The word is cleared at the start of every
+ *               call.
+ * Returns MLA_ERR_WORKSPACE when the plan needs more than the array holds:
+ * on the matrix-core path 2 * (batch * n_heads * (d_c + d_rope) + n_items *
+ * n_heads * d_c) bytes plus small per-item and per-sequence arrays (batch
+ * 32 with 256 work items: about 38 MB; the default plan of 128 sequences:
+ * about 53 MB); the fp32 path needs twice that. Every call on one GPU uses
+ * that GPU's one array, which keeps the last call's contents: calls that
+ * overlap on one GPU (several streams, several host threads) race and must
+ * be ordered by the caller. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mla_status mla_decode_noalloc(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
+                              const void *q_nope, const void *q_rope, const int32_t *q_pos, const void *w_uk,
+                              const void *w_uv, mla_dtype q_w_dtype, void *o, mla_dtype o_dtype,
+                              int32_t *dev_status, void *stream);
+
 /* ------------------------------------------------------------------ status
  * mla_workspace_init — clear the device status word at the start of ws
  * (a one-thread kernel, no memset, so it can sit in a captured graph).
