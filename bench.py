@@ -10,8 +10,8 @@ resident in HBM before timing; each step reads a different copy of the cache
 and weights so that no step is served from the 256 MB Infinity Cache.
 
 Prints one JSON line. value = latent-cache bytes read per step / step time
-(GB/s), timed over exactly `--steps` steps as a caller runs them (an event
-pair in the stream around each step gives the p10/p50/p90 of the step time).
+(GB/s), timed over exactly `--steps` steps as a caller runs them (the same
+region repeated ten more times gives the p10/p50/p90 of the step time).
 The same steps then run once more with the library's per-kernel profiling on
 (each kernel starts on an idle stream and records its own start and end):
 those give the per-kernel durations and the roofline object, which reports
@@ -80,7 +80,7 @@ def measured_traffic(bytes_alg):
 DT = {"f32": 0, "bf16": 1, "fp8": 2}
 
 
-def run_workload(m, torch, name, steps, warmup, q_len=1):
+def run_workload(m, torch, name, steps, warmup, q_len=1, repeats=10):
     """Times `steps` decode steps of one workload (after `warmup` untimed ones).
     A step is one mla_decode call, or one mla_append_decode call for the
     workload that appends a token per sequence; that step also restores
@@ -139,19 +139,27 @@ def run_workload(m, torch, name, steps, warmup, q_len=1):
         step(k)
     torch.cuda.synchronize()
     assert m.mla_device_error(ws) == 0
-    # timed region 1: the steps as a caller runs them (no profiling), with an
-    # event pair in the stream around each step for the step-time spread
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # timed region 1: the steps as a caller runs them, nothing else in the
+    # stream (this gives `value`)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        ev[k][0].record()
         step(k)
-        ev[k][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
-    step_ms = [a.elapsed_time(b) for a, b in ev]
+    # the spread: the same region repeated (an event pair around every step
+    # would cost more than the spread itself: each timed event record adds
+    # about 14 us to a step here); step_ms holds the per-step time of each
+    # repeat
+    step_ms = []
+    for _ in range(repeats):
+        torch.cuda.synchronize()
+        r0 = time.perf_counter()
+        for k in range(steps):
+            step(k)
+        torch.cuda.synchronize()
+        step_ms.append((time.perf_counter() - r0) * 1e3 / steps)
     # timed region 2: the same steps with the library's per-kernel profiling
     # (each kernel starts on an idle stream and records its own start and end)
     per_kernel = {}
