@@ -50,6 +50,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_S16X4(p) ((__attribute__((address_space(3))) s16x4 *)(p))
@@ -70,7 +71,8 @@ constexpr int SLACK = 8;             // running max is kept unless exceeded by 2
 constexpr int SPF = 3;               // score fragments read ahead of their product
 constexpr int VPF = 4;               // value fragments read ahead of their product
 constexpr int VBLK = 15;             // the output block kept in VGPRs (its AGPRs hold the scores)
-constexpr int OROW = 1040;           // partial row stride of the closing transpose in LDS (bytes)
+constexpr int OROW = 1040;           // partial row stride of the closing transpose in LDS (bytes), fp8
+constexpr int OROWQ = 272;           // the same for the bf16 kernel's quarter rows (128 columns + 16 bytes)
 
 // LDS map. bf16 latents: four fp16 tiles (copied and widened in place).
 // fp8 latents: three fp16 tiles, two raw tiles and their per-token scales,
@@ -83,11 +85,17 @@ template <bool FP8> struct Map {
   static constexpr int rope(int b) { return LTILE * NBUF + RTILE * b; }
   static constexpr int raw(int r) { return LTILE * NBUF + RTILE * NBUF + RAW_TILE * r; }
   static constexpr int scl(int r, int w) { return raw(2) + 1024 * r + 256 * w; }
-  static constexpr int end() { return FP8 ? raw(2) + 2048 : rope(NBUF); }
+  // bf16 only: one tile's softmax weights of all 128 heads in the value
+  // products' operand layout ([head block][k-step][lane] x 16 bytes), and a
+  // per-head float for each head block ([head % 32][head block]: alpha
+  // during the loop, the softmax denominator at the end)
+  static constexpr int pex() { return rope(NBUF); }
+  static constexpr int aex() { return pex() + 8192; }
+  static constexpr int end() { return FP8 ? raw(2) + 2048 : aex() + 512; }
 };
 constexpr int LDS_BYTES = Map<false>::end() > Map<true>::end() ? Map<false>::end() : Map<true>::end();
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-static_assert(4 * 32 * OROW <= Map<false>::end() && 4 * 32 * OROW <= Map<true>::end(), "transpose area");
+static_assert(4 * 32 * OROW <= Map<true>::end() && 4 * 128 * OROWQ <= Map<false>::pex(), "transpose area");
 }  // namespace sk
 
 __shared__ __attribute__((aligned(1024))) char g_lds[sk::LDS_BYTES];
@@ -416,6 +424,7 @@ __device__ __forceinline__ void softmax_piece(WaveState &st, Softmax &sm, const 
 // own hazard handling needs no blanket wait before each product, so the
 // softmax's vector work runs in the products' shadow (with a VGPR-form
 // chain, or an s_nop before each product, it mostly serialises).
+__device__ __forceinline__ void px_write_part(const WaveState &st, const Softmax &sm, int part);
 template <bool FP8, int B, bool SOFTMAX, class Hide>
 __device__ __forceinline__ void score_chain(WaveState &st, f32x16 &S, const f32x16 &Sv, Softmax &sm, Hide &hide) {
   using namespace sk;
@@ -431,6 +440,7 @@ __device__ __forceinline__ void score_chain(WaveState &st, f32x16 &S, const f32x
     asm volatile("" : "+a"(S));
     hide.score_step(kk);
     if (SOFTMAX) softmax_piece(st, sm, Sv, kk);
+    if (SOFTMAX && !FP8 && (kk == 7 || kk == 16 || kk == 24)) px_write_part(st, sm, kk == 7 ? 0 : (kk == 16 ? 1 : 2));
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -510,6 +520,92 @@ __device__ __forceinline__ void pv_rows(WaveState &st, const Softmax &sm, bool f
   }
 }
 
+// bf16 kernel: value products split by latent columns instead of heads.
+// Wave w owns columns 128 w .. 128 w + 127 of all 128 heads: block
+// O[4 cb + hb] is O^T [32 cols x 32 heads] for columns 128 w + 32 cb .. and
+// heads 32 hb ..; per tile
+//   O^T block (cb, hb) += C^T [32 cols x 16 tok] P^T [16 tok x 32 heads]
+// over two k-steps: 32 products, as with the row split, but each transposed
+// value fragment serves four products (8 fragments per wave and tile, a
+// quarter of the row split's transposed reads), and the weights of every
+// head come from LDS, where each head block's score wave left them in the
+// B-operand layout (the P registers of lane l of wave hb are the B operand
+// lane l of any wave needs for head block hb; same token order as the
+// transposed reads deliver). Each lane's alpha for its head in every head
+// block comes from LDS too.
+// The exchange writes of this wave's softmax results, each issued as soon as
+// the softmax piece that completes it has run (the previous tile's readers
+// of the exchange area are past the previous step's closing barrier): after
+// piece 7 alpha, after piece 16 the weights of k-step 0, after piece 24
+// those of k-step 1; px_write writes all three (an item's last tile).
+__device__ __forceinline__ void px_write_part(const WaveState &st, const Softmax &sm, int part) {
+  using M = sk::Map<false>;
+  if (part == 0) {
+    if (st.lane < 32) reinterpret_cast<float *>(g_lds + M::aex() + 16 * st.lane)[st.w] = sm.alpha;
+  } else {
+    const int kb = part - 1;
+    *reinterpret_cast<u32x4 *>(g_lds + M::pex() + 1024 * (2 * st.w + kb) + 16 * st.lane) =
+        u32x4{sm.P[4 * kb], sm.P[4 * kb + 1], sm.P[4 * kb + 2], sm.P[4 * kb + 3]};
+  }
+}
+__device__ __forceinline__ void px_write(const WaveState &st, const Softmax &sm) {
+#pragma unroll
+  for (int part = 0; part < 3; ++part) px_write_part(st, sm, part);
+}
+// The first two value fragments come from the tile itself (complete since
+// an earlier step), so they are read before the exchange barrier.
+template <int B>
+__device__ __forceinline__ void pv_cols_pre(const WaveState &st, f16x8 (&va)[3]) {
+  const int vl = value_base<false, B>(st.lane) + 256 * st.w;
+  va[0] = value_frag<false, B>(vl, 0, 0);
+  va[1] = value_frag<false, B>(vl, 1, 0);
+}
+template <int B, class Hide>
+__device__ __forceinline__ void pv_cols(WaveState &st, bool fresh, Hide &hide, f16x8 (&va)[3]) {
+  using namespace sk;
+  using M = Map<false>;
+  const int vl = value_base<false, B>(st.lane) + 256 * st.w;  // this wave's 128 columns
+  const int ln = opaque(st.lane);
+  // alpha first: the rescale test waits for it alone, the fragments keep flying
+  const f32x4 a4 = *reinterpret_cast<const f32x4 *>(g_lds + M::aex() + 16 * (ln & 31));
+  f16x8 pf[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+    pf[hb] = *reinterpret_cast<const f16x8 *>(g_lds + M::pex() + 1024 * (2 * hb) + 16 * ln);
+  // (an item's first tile needs none: the accumulators are still zero)
+  if (!fresh && __any(a4[0] != 1.0f || a4[1] != 1.0f || a4[2] != 1.0f || a4[3] != 1.0f)) {
+#pragma unroll
+    for (int x = 0; x < DC / 32; ++x) {
+      f32x16 t = st.O[x];
+      asm volatile("" : "+v"(t));
+      t *= a4[x & 3];
+      st.O[x] = t;
+      if (x == VBLK) asm volatile("" : "+v"(st.O[x]));
+      else asm volatile("" : "+a"(st.O[x]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int cb = n & 3;
+    if (n == 4) {
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        pf[hb] = *reinterpret_cast<const f16x8 *>(g_lds + M::pex() + 1024 * (2 * hb + 1) + 16 * ln);
+    }
+    if (n + 2 < 8) va[(n + 2) % 3] = value_frag<false, B>(vl, (n + 2) & 3, (n + 2) >> 2);
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const int x = 4 * cb + hb;
+      if (x == VBLK) mfma_acc_v(st.O[x], va[n % 3], pf[hb]);
+      else mfma_acc_a(st.O[x], va[n % 3], pf[hb]);
+      hide.value_step(4 * n + hb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // Work a step hides under its score products: score_step(kk) runs after
 // score product kk and issues at most one copy, one load or one
 // convert-and-store. Copies of a tile past the item's end re-read the item's
@@ -518,14 +614,15 @@ __device__ __forceinline__ void pv_rows(WaveState &st, const Softmax &sm, bool f
 // compiler count outstanding LDS operations exactly, so no wait drains the
 // fragment prefetch.
 //
-// bf16 latents: the 9 copies of tile i+3 (one every fourth product, the
-// k_rope part at product 32) and the widening of this wave's rows of tile
-// i+2, in place, 9 chunks of 16 bytes per thread: chunk x loaded after
-// product 16 + 2 x, once this wave's copies of tile i+2 have landed (waited
-// for at product 16: only this step's first 5 copies may still fly), and
-// converted and stored two products later. The latent copy's source row
-// pointer advances by the stride per row (no multiply), and stops at the
-// item's last row.
+// bf16 latents: the 9 copies of tile i+3 under the score products (one
+// every fourth product, the k_rope part at product 32), and the widening of
+// this wave's rows of tile i+2, in place, under the value products (which,
+// split by columns, leave the LDS and the issue slots room for it): 9 chunks
+// of 16 bytes per thread, chunk x loaded after value product 3 x, once this
+// wave's copies of tile i+2 have landed (only this step's 9 copies of tile
+// i+3 may still fly), and converted and stored two products later. The
+// latent copy's source row pointer advances by the stride per row (no
+// multiply), and stops at the item's last row.
 template <int DMA_BUF, int WIDEN_BUF>
 struct HideBf16 {
   const char *row;        // latent source of the next copy
@@ -543,16 +640,19 @@ struct HideBf16 {
       row = sa::latent_row_next(row, stride, lim, x);
     }
     if (kk == 32) lds_dma16(rope_base, rope_voff, LDS_OFF(g_lds) + M::rope(DMA_BUF) + 1024 * w);
-    if (kk == 16) {
-      wait_vm<5>();
+  }
+  // after value product m (0 .. 31)
+  __device__ __forceinline__ void value_step(int m) {
+    if (m == 0) {
+      wait_vm<9>();
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (kk >= 18 && kk % 2 == 0 && (kk - 18) / 2 < 9) {
-      const int x = (kk - 18) / 2;
+    if (m % 3 == 2 && (m - 2) / 3 < 9) {
+      const int x = (m - 2) / 3;
       widen_bf16_store<WIDEN_BUF>(tid, x, v[x & 1]);
     }
-    if (kk >= 16 && kk % 2 == 0 && (kk - 16) / 2 < 9) {
-      const int x = (kk - 16) / 2;
+    if (m % 3 == 0 && m / 3 < 9) {
+      const int x = m / 3;
       v[x & 1] = widen_bf16_load<WIDEN_BUF>(tid, x);
     }
   }
@@ -640,7 +740,20 @@ __device__ __forceinline__ void step(WaveState &st, f32x16 &S, const Item &it, i
 #pragma unroll
     for (int kk = 0; kk <= 24; ++kk) softmax_piece(st, sm, Sv, kk);
   }
-  pv_rows<FP8, I % NB>(st, sm, i == 0);
+  if constexpr (FP8) {
+    pv_rows<FP8, I % NB>(st, sm, i == 0);
+  } else {
+    // every head's weights and alpha in LDS (written by the score chain as
+    // the softmax produced them; an item's last tile writes them here)
+    // before any wave's value products read them
+    if (i + 1 >= it.ntiles) px_write(st, sm);
+    f16x8 va[3];
+    pv_cols_pre<I % NB>(st, va);
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    pv_cols<I % NB>(st, i == 0, h, va);
+  }
   wait_lds();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -799,25 +912,60 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H, int 
   __builtin_amdgcn_s_barrier();
   // (a row that saw no token, possible with several new tokens, has l = 0:
   // partial 0, log-sum-exp -inf)
-  const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
   if (half == 0) lse[static_cast<size_t>(k) * H + head] = st.l > 0.0f ? st.m + log2f(st.l) : -INFINITY;
-  char *tb = g_lds + w * 32 * OROW;
+  if (FP8) {
+    const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+    char *tb = g_lds + w * 32 * OROW;
 #pragma unroll
-  for (int cb = 0; cb < DC / 32; ++cb) {
+    for (int cb = 0; cb < DC / 32; ++cb) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      f16x4 v;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f16x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(st.O[cb][4 * g4 + e] * inv);
-      // head lane%32, columns 32 cb + 8 g4 + 4 half .. +3
-      *reinterpret_cast<f16x4 *>(tb + (lane & 31) * OROW + 64 * cb + 16 * g4 + 8 * half) = v;
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(st.O[cb][4 * g4 + e] * inv);
+        // head lane%32, columns 32 cb + 8 g4 + 4 half .. +3
+        *reinterpret_cast<f16x4 *>(tb + (lane & 31) * OROW + 64 * cb + 16 * g4 + 8 * half) = v;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the rows come from other lanes
+    uint16_t *orow = ob + static_cast<size_t>(32 * w) * DC + 8 * lane;
+#pragma unroll
+    for (int h = 0; h < 32; ++h)
+      *reinterpret_cast<u32x4 *>(orow + h * DC) = *reinterpret_cast<const u32x4 *>(tb + h * OROW + 16 * lane);
+  } else {
+    // this wave holds columns 128 w .. of every head: every head's softmax
+    // denominator through LDS, then each head's 128 columns (256 bytes) as
+    // one quarter row in LDS, stored as 16-byte pieces of the head's row
+    using M = Map<false>;
+    if (lane < 32) reinterpret_cast<float *>(g_lds + M::aex() + 16 * lane)[w] = st.l;
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    const f32x4 l4 = *reinterpret_cast<const f32x4 *>(g_lds + M::aex() + 16 * (lane & 31));
+    f32x4 inv4;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) inv4[hb] = l4[hb] > 0.0f ? 1.0f / l4[hb] : 0.0f;
+    char *tb = g_lds + w * 128 * OROWQ;
+#pragma unroll
+    for (int x = 0; x < DC / 32; ++x) {
+      const int cb = x >> 2, hb = x & 3;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(st.O[x][4 * g4 + e] * inv4[hb]);
+        // head 32 hb + lane%32, columns 32 cb + 8 g4 + 4 half .. +3 of this wave's 128
+        *reinterpret_cast<f16x4 *>(tb + (32 * hb + (lane & 31)) * OROWQ + 64 * cb + 16 * g4 + 8 * half) = v;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the rows come from other lanes
+    uint16_t *orow = ob + 128 * w + 8 * (lane & 15);
+#pragma unroll
+    for (int x = 0; x < 32; ++x) {
+      const int h = 4 * x + (lane >> 4);
+      *reinterpret_cast<u32x4 *>(orow + static_cast<size_t>(h) * DC) =
+          *reinterpret_cast<const u32x4 *>(tb + h * OROWQ + 16 * (lane & 15));
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the rows come from other lanes
-  uint16_t *orow = ob + static_cast<size_t>(32 * w) * DC + 8 * lane;
-#pragma unroll
-  for (int h = 0; h < 32; ++h)
-    *reinterpret_cast<u32x4 *>(orow + h * DC) = *reinterpret_cast<const u32x4 *>(tb + h * OROW + 16 * lane);
 }
 
 }  // namespace
