@@ -21,7 +21,7 @@ __all__ = [
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "MLA_ERR_CAPACITY",
-          4: "MLA_ERR_HIP", 5: "MLA_ERR_WORKSPACE", 6: "MLA_ERR_PLAN"}
+          4: "MLA_ERR_HIP", 5: "MLA_ERR_WORKSPACE", 6: "MLA_ERR_PLAN", 7: "MLA_ERR_RANGE"}
 
 # Every extern "C" entry point of include/mla.h.
 EXPORTED = [

@@ -12,6 +12,9 @@ namespace mla {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFp8Max = 448.0f;
+// Largest finite fp16 magnitude: the matrix-core path carries cached values
+// (bf16, or fp8 codes times their scale) and the absorbed query in fp16.
+constexpr float kF16Max = 65504.0f;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -95,14 +98,26 @@ __device__ __forceinline__ float block_max_256(float v, float *red) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// First error wins.
+__device__ __forceinline__ void set_status(int32_t *status, int32_t code);
+
 // Finish one appended row from its fp32 projections outv[0 .. d_c + d_rope)
 // (already in LDS, k_rope part rotated): round to the storage dtypes and
 // store it at `row`. fp8 latents get the per-token scale amax / 448 (1 for a
-// zero row). Called by all 256 threads of the block; `red` is 4 floats of LDS.
+// zero row). A bf16 or fp8 row (the dtypes the matrix-core decode widens to
+// fp16) with a magnitude of 65504 or more is stored as it is and reported
+// (MLA_ERR_RANGE). Called by all 256 threads of the block; `red` is 4 floats
+// of LDS.
 __device__ __forceinline__ void store_appended_row(const mla_dims &d, const mla_cache &c, int64_t row,
-                                                   const float *outv, float *red) {
+                                                   const float *outv, float *red, int32_t *status) {
   const int tid = threadIdx.x;
   char *rowp = static_cast<char *>(c.rows) + row * c.row_stride;
+  if (c.latent_dtype != MLA_F32) {
+    float am = 0.0f;
+    for (int k = tid; k < d.d_c + d.d_rope; k += 256) am = fmaxf(am, fabsf(outv[k]));
+    am = block_max_256(am, red);
+    if (tid == 0 && !(am < kF16Max)) set_status(status, MLA_ERR_RANGE);
+  }
   if (c.latent_dtype == MLA_FP8_E4M3) {
     float am = 0.0f;
     for (int k = tid; k < d.d_c; k += 256) am = fmaxf(am, fabsf(outv[k]));

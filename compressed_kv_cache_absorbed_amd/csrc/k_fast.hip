@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
                                                           const uint16_t *__restrict__ w_uk,
                                                           const int32_t *__restrict__ dev_len,
                                                           uint16_t *__restrict__ Q, PlanRef plan,
-                                                          int32_t *__restrict__ clear_status) {
+                                                          int32_t *__restrict__ status) {
   using namespace fast;
   constexpr int WROW = 288;  // LDS bytes per W row (128 columns = 256 bytes + 32)
   __shared__ __attribute__((aligned(16))) char smem[DNOPE * WROW];
@@ -102,7 +102,6 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
   const int i = blockIdx.x, cq = blockIdx.y, b0 = blockIdx.z * 32;
   const int iw = i % Hr, back = q_len - 1 - i / Hr;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (clear_status != nullptr && i == 0 && cq == 0 && b0 == 0 && tid == 0) clear_status[0] = 0;
   // every global load first, in the order of use: the RoPE inputs, the
   // q_nope fragments, the weight quarter (32 KB: 128 rows x 16 chunks of
   // 16 bytes, 8 per thread)
@@ -140,8 +139,10 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
     const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(xr & 0xffffu));
     const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(xr >> 16));
     f16x2 r;
-    r[0] = static_cast<_Float16>((x0 * cs - x1 * sn) * qscale);
-    r[1] = static_cast<_Float16>((x0 * sn + x1 * cs) * qscale);
+    const float r0 = (x0 * cs - x1 * sn) * qscale, r1 = (x0 * sn + x1 * cs) * qscale;
+    if (!(fmaxf(fabsf(r0), fabsf(r1)) < kF16Max)) set_status(status, MLA_ERR_RANGE);
+    r[0] = static_cast<_Float16>(r0);
+    r[1] = static_cast<_Float16>(r1);
     *reinterpret_cast<f16x2 *>(Q + (static_cast<size_t>(rb) * H + i) * D + DC + 2 * rp) = r;
   }
 #pragma unroll
@@ -172,13 +173,19 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
   // D [32 c x 32 b]: lane holds sequence b0 + l%32, c = c0 + 8(r/4) + 4(l/32) + r%4
   if (bb < B) {
     uint16_t *dst = Q + (static_cast<size_t>(bb) * H + i) * D + 128 * cq + c0 + 4 * (lane >> 5);
+    float amax = 0.0f;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       f16x4 v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = static_cast<_Float16>(acc[4 * g4 + r] * qscale);
+      for (int r = 0; r < 4; ++r) {
+        const float x = acc[4 * g4 + r] * qscale;
+        amax = fmaxf(amax, fabsf(x));
+        v[r] = static_cast<_Float16>(x);
+      }
       *reinterpret_cast<f16x4 *>(dst + 8 * g4) = v;
     }
+    if (!(amax < kF16Max)) set_status(status, MLA_ERR_RANGE);
   }
   // the plan copy the split-K and combine kernels read
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) plan_verify(plan);
@@ -530,7 +537,7 @@ __global__ __launch_bounds__(256) void append_finish_kernel(mla_dims d, mla_cach
     outv[d.d_c + 2 * p + 1] = x0 * sn + x1 * cs;
   }
   __syncthreads();
-  store_appended_row(d, c, row, outv, red);
+  store_appended_row(d, c, row, outv, red, status);
 }
 
 }  // namespace
@@ -564,11 +571,11 @@ hipError_t launch_append_finish(hipStream_t s, const mla_dims &d, const mla_cach
 hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, int32_t q_len, const void *q_nope,
                               const void *q_rope, const int32_t *q_pos, const void *w_uk,
                               const int32_t *seq_len, uint16_t *q_out, const PlanRef &plan,
-                              int32_t *clear_status) {
+                              int32_t *status) {
   const int H = d.n_heads * q_len;
   return launch_kernel(absorb_fast_kernel, dim3(H, fast::DC / 128, (batch + 31) / 32), 256, 0, s, batch, H,
                        d.n_heads, q_len, d.softmax_scale * kLog2e, d.rope_base, static_cast<const uint16_t *>(q_nope),
-                       static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seq_len, q_out, plan, clear_status);
+                       static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seq_len, q_out, plan, status);
 }
 
 hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, int32_t n_items,

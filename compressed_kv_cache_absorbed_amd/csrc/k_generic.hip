@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void append_generic_kernel(mla_dims d, mla_cac
   }
   __syncthreads();
 
-  store_appended_row(d, c, row, outv, red);
+  store_appended_row(d, c, row, outv, red, status);
 }
 
 __global__ void advance_len_kernel(mla_cache c, int32_t n_new) {
@@ -83,11 +83,9 @@ __global__ void advance_len_kernel(mla_cache c, int32_t n_new) {
 __global__ __launch_bounds__(256) void absorb_generic_kernel(mla_dims d, const void *q_nope,
                                                             const void *q_rope, const int32_t *q_pos,
                                                             const void *w_uk, mla_dtype qw,
-                                                            const int32_t *dev_len, float *q_out, PlanRef plan,
-                                                            int32_t *clear_status) {
+                                                            const int32_t *dev_len, float *q_out, PlanRef plan) {
   extern __shared__ float qn[];  // [d_nope]
   const int b = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
-  if (clear_status != nullptr && b == 0 && i == 0 && tid == 0) clear_status[0] = 0;
   const int H = d.n_heads, D = d.d_c + d.d_rope;
   const int64_t bi = static_cast<int64_t>(b) * H + i;
   for (int n = tid; n < d.d_nope; n += 256) qn[n] = load_elem(q_nope, bi * d.d_nope + n, qw);
@@ -313,9 +311,9 @@ hipError_t launch_append_generic(hipStream_t s, const mla_dims &d, const mla_cac
 hipError_t launch_absorb_generic(hipStream_t s, const mla_dims &d, int32_t batch, const void *q_nope,
                                  const void *q_rope, const int32_t *q_pos, const void *w_uk,
                                  mla_dtype qw, const int32_t *seq_len, float *q_out, const PlanRef &plan,
-                                 int32_t *clear_status) {
+                                 int32_t *) {
   return launch_kernel(absorb_generic_kernel, dim3(batch, d.n_heads), 256, sizeof(float) * d.d_nope, s, d, q_nope,
-                       q_rope, q_pos, w_uk, qw, seq_len, q_out, plan, clear_status);
+                       q_rope, q_pos, w_uk, qw, seq_len, q_out, plan);
 }
 
 hipError_t launch_decode_generic(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,

@@ -199,6 +199,7 @@ const char *mla_status_str(mla_status s) {
     case MLA_ERR_HIP: return "MLA_ERR_HIP";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
     case MLA_ERR_PLAN: return "MLA_ERR_PLAN";
+    case MLA_ERR_RANGE: return "MLA_ERR_RANGE";
   }
   return "MLA_ERR_UNKNOWN";
 }
@@ -478,11 +479,12 @@ mla_status decode_launch(const mla_dims *dims, const mla_cache *cache, const mla
   float *opart = reinterpret_cast<float *>(base + w.opart);
   uint16_t *opart16 = reinterpret_cast<uint16_t *>(base + w.opart);
   float *lse = reinterpret_cast<float *>(base + w.lse);
+  if (clear_status) MLA_LAUNCH(s, K_INIT, launch_init(s, status));
   if (fast) {
     uint16_t *q = reinterpret_cast<uint16_t *>(base + w.q);
     MLA_LAUNCH(s, K_ABSORB_FAST,
                launch_absorb_fast(s, *dims, plan->batch, q_len, q_nope, q_rope, q_pos, w_uk, cache->seq_len, q, pr,
-                                  clear_status ? status : nullptr));
+                                  status));
     MLA_LAUNCH(s, cache->latent_dtype == MLA_FP8_E4M3 ? K_DECODE_FP8 : K_DECODE_BF16,
                launch_decode_fast(s, *dims, *cache, q_len, plan->n_items, items, seqs, q, opart16, lse, status));
     MLA_LAUNCH(s, K_COMBINE_FAST,
@@ -492,7 +494,7 @@ mla_status decode_launch(const mla_dims *dims, const mla_cache *cache, const mla
     float *q = reinterpret_cast<float *>(base + w.q);
     MLA_LAUNCH(s, K_ABSORB_GENERIC,
                launch_absorb_generic(s, *dims, plan->batch, q_nope, q_rope, q_pos, w_uk, qw, cache->seq_len, q, pr,
-                                     clear_status ? status : nullptr));
+                                     status));
     MLA_LAUNCH(s, K_DECODE_GENERIC,
                launch_decode_generic(s, *dims, *cache, plan->n_items, items, seqs, q, opart, lse, status));
     MLA_LAUNCH(s, K_COMBINE_GENERIC,

@@ -125,21 +125,21 @@ hipError_t launch_append_finish(hipStream_t s, const mla_dims &d, const mla_cach
 hipError_t launch_advance_len(hipStream_t s, const mla_cache &c, int32_t n_new);
 
 // The absorb kernels, the first of every decode, also check the
-// workspace's plan copy (one workgroup, see PlanRef) and, when clear_status
-// is not null, zero that status word before the later kernels can set it.
-// They take the query position from the cache's seq_len (equal to the
-// plan's length, or the split-K kernel reports MLA_ERR_PLAN and zeroes the
-// output).
+// workspace's plan copy (one workgroup, see PlanRef); the matrix-core one
+// reports MLA_ERR_RANGE in the status word when a query value leaves fp16's
+// range. They take the query position from the cache's seq_len (equal to
+// the plan's length, or the split-K kernel reports MLA_ERR_PLAN and zeroes
+// the output).
 hipError_t launch_absorb_generic(hipStream_t s, const mla_dims &d, int32_t batch,
                                  const void *q_nope, const void *q_rope, const int32_t *q_pos,
                                  const void *w_uk, mla_dtype qw, const int32_t *seq_len, float *q_out,
-                                 const PlanRef &plan, int32_t *clear_status);
+                                 const PlanRef &plan, int32_t *status);
 // The matrix-core launchers take q_len new query tokens per sequence (1 for
 // a plain decode): heads become (token, head) pairs, token-major.
 hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, int32_t q_len,
                               const void *q_nope, const void *q_rope, const int32_t *q_pos,
                               const void *w_uk, const int32_t *seq_len, uint16_t *q_out, const PlanRef &plan,
-                              int32_t *clear_status);
+                              int32_t *status);
 
 hipError_t launch_decode_generic(hipStream_t s, const mla_dims &d, const mla_cache &c,
                                  int32_t n_items, const WorkItem *items, const SeqInfo *seqs,
@@ -164,7 +164,7 @@ hipError_t launch_status_copy(hipStream_t s, const int32_t *src, int32_t *dst);
 // workspace out for the path that runs (2-byte query and partials on the
 // matrix-core path; decode_compact_bytes gives that size) instead of the
 // size the workspace queries report; clear_status zeroes the status word
-// inside the first kernel.
+// first (a one-thread kernel).
 mla_status decode_check_args(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan,
                              const void *q_nope, const void *q_rope, const void *w_uk, const void *w_uv,
                              mla_dtype qw, const void *o, mla_dtype od, const void *ws, size_t ws_bytes,

@@ -65,7 +65,9 @@ typedef enum {
   MLA_ERR_CAPACITY = 3,    /* device: append would pass seq_cap             */
   MLA_ERR_HIP = 4,         /* a HIP runtime call or launch failed           */
   MLA_ERR_WORKSPACE = 5,   /* ws_bytes below the required size              */
-  MLA_ERR_PLAN = 6         /* device: seq_len differs from the plan         */
+  MLA_ERR_PLAN = 6,        /* device: seq_len differs from the plan         */
+  MLA_ERR_RANGE = 7        /* device: a value the matrix-core path carries
+                              in fp16 is beyond fp16's range (see mla_decode) */
 } mla_status;
 
 typedef enum {
@@ -203,11 +205,31 @@ mla_status mla_plan_item(const mla_plan *plan, int32_t k, int32_t *b, int32_t *t
  * The device checks seq_len[b] against the plan (MLA_ERR_PLAN). Arithmetic:
  * fp32 accumulation throughout. The matrix-core path (d_c = 512,
  * d_rope = 64, d_nope = d_v = 128, n_heads a multiple of 128, bf16 q and
- * weights, bf16 or fp8 latents, bf16 k_rope) rounds q~ and the softmax
- * weights to fp16 and widens the cached values to fp16 (exact for every e4m3
- * value and for bf16 values up to 65504 in magnitude) for the matrix cores;
- * the merged latent output enters the W_UV product as a bf16 hi + lo pair.
- * Every other shape runs fp32 kernels. */
+ * weights, bf16 or fp8 latents, bf16 k_rope) rounds q~ (times softmax_scale
+ * * log2 e) and the softmax weights to fp16 and widens the cached values
+ * (bf16, or e4m3 codes times their scale) to fp16 for the matrix cores; the
+ * merged latent output enters the W_UV product as a bf16 hi + lo pair.
+ * Every other shape runs fp32 kernels.
+ * Numeric domain of the matrix-core path: a widened cached value is exact
+ * when its magnitude lies in [2^-14, 65504) (every bf16 value there has a
+ * significand fp16 holds; e4m3 codes times a scale are rounded once to
+ * fp16's 11 bits); below 2^-14 it becomes an fp16 subnormal (absolute
+ * precision 2^-24: the relative error grows as the value shrinks), below
+ * 2^-24 it reads as zero (bf16 values are converted rounding toward zero);
+ * at 65504 and above a bf16 value saturates to +-65504. q~ obeys the same
+ * range (rounded to nearest; beyond 65504 it is reported). The scores' relative
+ * precision does not matter for tiny values (they are tiny in absolute
+ * terms); the value product's does: a cache whose rows are uniformly below
+ * 2^-14, or that reach 65504, is outside the domain and belongs on the fp32
+ * path. The decode reports a query value beyond fp16's range, and
+ * mla_append a row it writes beyond it, as MLA_ERR_RANGE (the row is
+ * stored as it is); rows the caller writes itself are not checked.
+ * Accuracy inside that range: the absorbed query (times softmax_scale and
+ * log2 e) is rounded to fp16, relative 2^-11, so a score's error grows with
+ * the score's own size. With s the scores in log2 units, the output's max
+ * error over its rms stays within 2e-2 while max|s| <= 64, and within
+ * 2e-2 + 2^-13 max|s| beyond (measured and emulated: near 0.12 at
+ * max|s| = 1800). A bf16 query would carry 8 significand bits, not 11. */
 size_t mla_decode_workspace_bytes(const mla_dims *dims, const mla_plan *plan);
 /* mla_workspace_bytes — one size that serves every call on this plan with at
  * most one new token per sequence: mla_decode, and, when dims->d_model > 0,
