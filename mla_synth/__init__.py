@@ -254,6 +254,19 @@ def multi_queries(case, q_len, seed):
     return q_nope, q_rope
 
 
+def merged_inputs(case, d_x, d_out, seed):
+    """Inputs of a decode from precomputed absorbed weights, drawn from their
+    own generator (``seed``) so the case's own draws are unchanged, in this
+    order: x [B, d_x] N(0, 1) (each sequence's query input), W_Q
+    [H, d_nope, d_x] N(0, 1/d_x), W_O [d_out, H d_v] N(0, 1/(H d_v)); all in
+    the case's activation dtype. The rotary query is the case's q_rope."""
+    rng = np.random.default_rng(seed)
+    x = _normal(rng, (case.B, d_x))
+    w_q = _normal(rng, (case.H, case.d_nope, d_x), 1.0 / math.sqrt(d_x))
+    w_o = _normal(rng, (d_out, case.H * case.d_v), 1.0 / math.sqrt(case.H * case.d_v))
+    return to_storage(x, case.act_dtype), to_storage(w_q, case.act_dtype), to_storage(w_o, case.act_dtype)
+
+
 def workload(name, seed=None, **overrides):
     """Build one of the named workloads (see the module docstring)."""
     kw = dict(WORKLOADS[name])

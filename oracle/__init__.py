@@ -28,6 +28,8 @@ Modules:
                            non-absorbed decode (the definition), absorbed decode
                            (self-check), log-sum-exp merge of split partials.
 * :mod:`oracle.cache_size` the pages' per-token cache-size closed forms.
+* :mod:`oracle.merged`     precomputed absorbed weights (W_UK^T W_Q per head,
+                           W_O W_UV) and the decode that consumes them.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against something other
 than itself (brute force, a library routine, closed forms, printed values).
@@ -35,4 +37,4 @@ Parity unpinned: none of the functions here; the pages' 93.3 %, "~1/4 HBM",
 "1/8 SSD" and "~5 % parameters" figures are not functions of this package.
 """
 
-from . import codecs, rope, mla, cache_size  # noqa: F401
+from . import codecs, rope, mla, cache_size, merged  # noqa: F401
