@@ -180,6 +180,74 @@ def run_workload(m, torch, name, steps, warmup, q_len=1, repeats=10):
                 splitk_name=kname, per_kernel=per_kernel, n_items=plan.n_items, ncopy=ncopy, q_len=q_len)
 
 
+def run_merged(m, torch, steps, warmup, d_x=1536, d_out=7168, repeats=10):
+    """Decode from precomputed absorbed weights (mla_decode_merged) on the
+    headline workload: x is a 1536-wide query latent, y the 7168-wide layer
+    output. The merges run once before timing. A step reads the cache, the
+    merged query weight [128, 512, 1536] and the merged output weight
+    [7168, 128 x 512] (bf16); the weights alone are far larger than the
+    on-package cache, so nothing of the previous step survives in it."""
+    import mla_synth
+    from mla_synth.device import _t, upload
+
+    case = mla_synth.workload(DEFAULT_WORKLOAD)
+    dev = torch.device("cuda", 0)
+    t = upload(case, dev)
+    d = m.dims(case.H, case.d_c, case.d_rope, case.d_nope, case.d_v, 0, case.softmax_scale, case.rope_base)
+    x, w_q, w_o = mla_synth.merged_inputs(case, d_x, d_out, seed=230)
+    tx, tq, to = _t(x, dev), _t(w_q, dev), _t(w_o, dev)
+    a = torch.empty((case.H, case.d_c, d_x), dtype=torch.bfloat16, device=dev)
+    bm = torch.empty((d_out, case.H * case.d_c), dtype=torch.bfloat16, device=dev)
+    m.mla_merge_query_weight(d, d_x, tq, t["w_uk"], DT["bf16"], a)
+    m.mla_merge_output_weight(d, d_out, to, t["w_uv"], DT["bf16"], bm)
+    torch.cuda.synchronize()
+    del tq, to
+    c = m.cache(t["rows"], case.row_stride, DT[case.latent_dtype], DT[case.rope_dtype], t["seq_start"], t["seq_cap"],
+                t["seq_len"], None)
+    plan = m.mla_plan_create(d, case.lens.tolist(), 0)
+    ws = torch.empty(m.mla_decode_merged_workspace_bytes(d, plan, d_out), dtype=torch.uint8, device=dev)
+    m.mla_workspace_init(ws)
+    y = torch.empty((case.B, d_out), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        m.mla_decode_merged(d, c, plan, d_x, tx, t["q_rope"], None, a, d_out, bm, DT["bf16"], y, DT["bf16"], ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    assert m.mla_device_error(ws) == 0
+    step_ms = []
+    for _ in range(repeats + 1):
+        torch.cuda.synchronize()
+        r0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        step_ms.append((time.perf_counter() - r0) * 1e3 / steps)
+    per_kernel = {}
+    for _ in range(steps):
+        m.mla_prof_begin(max_records=16)
+        step()
+        for name, (ms, n) in m.mla_prof_end().items():
+            per_kernel.setdefault(name, []).append(ms / n)
+    torch.cuda.synchronize()
+    assert m.mla_device_error(ws) == 0
+    cache_bytes = int(case.lens.sum()) * case.row_bytes
+    a_bytes, bm_bytes = a.numel() * 2, bm.numel() * 2
+    ms = step_ms[0]
+    med = {k: float(np.median(v)) for k, v in per_kernel.items()}
+    unmerged = 2 * (case.H * case.d_nope * d_x + 2 * case.H * case.d_nope * case.d_c + d_out * case.H * case.d_v)
+    return {"batch": case.B, "d_x": d_x, "d_out": d_out, "cache_bytes_per_step": cache_bytes,
+            "merged_weight_bytes": a_bytes + bm_bytes, "unmerged_weight_bytes_w_q_w_uk_w_uv_w_o": unmerged,
+            "ms_per_step": round(ms, 5), "step_ms": pct(step_ms[1:]),
+            "tokens_per_s": round(case.B / (ms * 1e-3), 1),
+            "GBs_step_all_bytes": round((cache_bytes + a_bytes + bm_bytes) / (ms * 1e-3) / 1e9, 2),
+            "kernel_ms_p50": {k: round(v, 5) for k, v in med.items()},
+            "absorb_merged_GBs": round(a_bytes / (med["absorb_merged"] * 1e-3) / 1e9, 2),
+            "out_merged_GBs": round(bm_bytes / (med["out_merged"] * 1e-3) / 1e9, 2),
+            "out_merged_hbm_frac": round(bm_bytes / (med["out_merged"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def pct(xs):
     """p10 / p50 / p90 of a list of times (ms), rounded."""
     q = np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])
@@ -206,25 +274,10 @@ def workload_summary(res):
             "kernel_ms_p50": {k: round(float(np.median(v)), 5) for k, v in res["per_kernel"].items()}}
 
 
-def sampled_parity(res, n=8):
-    """Sampled outputs of the last step against the oracle (absorbed form,
-    pinned equal to the definition): max|err| / rms over the sample."""
-    import numpy as np
-    from tests.helpers import oracle_cache, oracle_decode
-    case = res["case"]
-    rng = np.random.default_rng(7)
-    pairs = [(int(rng.integers(case.B)), int(rng.integers(case.H))) for _ in range(n)]
-    seqs = sorted({b for b, _ in pairs})
-    C, R = oracle_cache(case, seqs=seqs)
-    ref = oracle_decode(case, pairs=pairs, absorbed=True, C=C, R=R)
-    o = res["o"].float().cpu().numpy()
-    got = np.stack([o[b, i] for b, i in pairs])
-    return float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)))
-
-
 def cpu_baseline(res, budget_s):
     """The oracle's non-absorbed fp64 decode timed on the host on a bounded
-    sample of (sequence, head) pairs, scaled to the whole step."""
+    sample of (sequence, head) pairs, scaled to the whole step; its outputs
+    double as a sampled parity check of the last timed step."""
     import numpy as np
     from oracle import mla as omla
     from tests.helpers import act_to_f64, oracle_cache
@@ -253,23 +306,30 @@ def cpu_baseline(res, budget_s):
     args = dict(q_nope=act_to_f64(case.q_nope, "bf16"), q_rope=act_to_f64(case.q_rope, "bf16"),
                 w_uk=act_to_f64(case.w_uk, "bf16"), w_uv=act_to_f64(case.w_uv, "bf16"))
     done, elapsed, tokens = 0, 0.0, 0
+    got, ref = [], []
+    o = res["o"].float().cpu().numpy()
     while elapsed < budget_s or done < 4:
         b = seqs[done % len(seqs)]
         i = int(rng.integers(case.H))
         t0 = time.perf_counter()
-        omla.decode(C, R, case.seq_start, case.lens, args["q_nope"], args["q_rope"], args["w_uk"],
-                    args["w_uv"], case.softmax_scale, case.rope_base, pairs=[(b, i)])
+        r = omla.decode(C, R, case.seq_start, case.lens, args["q_nope"], args["q_rope"], args["w_uk"],
+                        args["w_uv"], case.softmax_scale, case.rope_base, pairs=[(b, i)])
         elapsed += time.perf_counter() - t0
+        ref.append(r[0])
+        got.append(o[b, i])
         tokens += int(case.lens[b])
         done += 1
         if done >= 4000:
             break
+    # the same oracle outputs against the last timed step's (bf16) outputs
+    got, ref = np.stack(got), np.stack(ref)
+    parity = float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)))
     # per (token, head) cost, scaled to the step's tokens x heads
     per_tok_head = elapsed / tokens
     step_s = per_tok_head * float(case.lens.sum()) * case.H
     return {"value": round(res["cache_bytes"] / step_s / 1e9, 6), "unit": "GB/s", "cores": int(cores),
             "kind": "oracle", "step_seconds": round(step_s, 3), "cpu_model": cpu_model,
-            "host_cpus": os.cpu_count(), "blas": blas,
+            "host_cpus": os.cpu_count(), "blas": blas, "parity_max_err_over_rms": round(parity, 6),
             "sample": f"{done} (sequence, head) pairs of the workload ({tokens} token-heads, "
                       f"{elapsed:.1f} s of fp64 non-absorbed decode), scaled to {case.B} sequences x {case.H} heads"}
 
@@ -319,7 +379,6 @@ def main():
     gbs = res["cache_bytes"] / (res["ms_step"] * 1e-3) / 1e9
     ach = res["cache_bytes"] / (res["splitk_ms"] * 1e-3) / 1e9
     traffic = measured_traffic(res["cache_bytes"])
-    par = sampled_parity(res)
     head = workload_summary(res)
     out = {
         "metric": METRIC,
@@ -345,7 +404,6 @@ def main():
         "step_over_splitk": head["step_over_splitk"],
         "kernel_ms_p50": head["kernel_ms_p50"],
         "ms_per_step_profiled": round(res["ms_step_profiled"], 5),
-        "parity_sampled_max_err_over_rms": round(par, 6),
         "roofline": {"kernel": "splitk_decode (bf16 latent)", "bound": "hbm", "achieved": round(ach, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
@@ -363,6 +421,10 @@ def main():
                   file=sys.stderr, flush=True)
             del r
             torch.cuda.empty_cache()
+        out["workloads"]["v3_b32_ragged_merged_weights"] = run_merged(m, torch, a.steps, a.warmup)
+        print(f"# merged weights: {out['workloads']['v3_b32_ragged_merged_weights']['ms_per_step']} ms/step",
+              file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(res, a.cpu_seconds)
     print(json.dumps(out), flush=True)

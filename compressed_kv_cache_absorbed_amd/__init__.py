@@ -14,6 +14,7 @@ __all__ = [
     "dims", "cache", "mla_plan_create", "mla_append_workspace_bytes",
     "mla_decode_workspace_bytes", "mla_workspace_bytes", "mla_append", "mla_decode", "mla_append_decode",
     "mla_decode_multi", "mla_decode_multi_workspace_bytes", "mla_decode_noalloc",
+    "mla_merge_query_weight", "mla_merge_output_weight", "mla_decode_merged", "mla_decode_merged_workspace_bytes",
     "mla_workspace_init", "mla_device_error", "mla_status_str", "mla_abi_version",
     "mla_prof_begin", "mla_prof_end", "mla_calib_copy", "mla_calib_read", "EXPORTED",
     "workspace", "decode", "append", "append_decode",
@@ -30,7 +31,8 @@ EXPORTED = [
     "mla_decode_multi_workspace_bytes", "mla_decode_multi", "mla_decode_noalloc", "mla_append_decode",
     "mla_workspace_init", "mla_device_error", "mla_status_str",
     "mla_abi_version", "mla_prof_begin", "mla_prof_end", "mla_prof_kernel_name",
-    "mla_prof_num_kernels", "mla_calib_copy", "mla_calib_read",
+    "mla_prof_num_kernels", "mla_calib_copy", "mla_calib_read", "mla_merge_query_weight",
+    "mla_merge_output_weight", "mla_decode_merged", "mla_decode_merged_workspace_bytes",
 ]
 
 
@@ -92,6 +94,11 @@ def load():
         "mla_append_decode": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P,
                                              _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
                                              ctypes.c_size_t, _P]),
+        "mla_merge_query_weight": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, ctypes.c_int, _P, _P]),
+        "mla_merge_output_weight": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, ctypes.c_int, _P, _P]),
+        "mla_decode_merged": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, _P,
+                                             ctypes.c_int, _P, ctypes.c_int, _P, ctypes.c_size_t, _P]),
+        "mla_decode_merged_workspace_bytes": (ctypes.c_size_t, [_P, _P, ctypes.c_int32]),
         "mla_workspace_init": (ctypes.c_int, [_P, ctypes.c_size_t, _P]),
         "mla_device_error": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32]),
         "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -232,6 +239,26 @@ def mla_decode_noalloc(d, c, plan, q_nope, q_rope, q_pos, w_uk, w_uv, q_w_dtype,
     _check(load().mla_decode_noalloc(ctypes.byref(d), ctypes.byref(c), plan.handle, _ptr(q_nope), _ptr(q_rope),
                                      _ptr(q_pos), _ptr(w_uk), _ptr(w_uv), q_w_dtype, _ptr(o), o_dtype,
                                      _ptr(dev_status), _stream(stream)), "mla_decode_noalloc")
+
+
+def mla_merge_query_weight(d, d_x, w_q, w_uk, w_dtype, a, stream=None):
+    _check(load().mla_merge_query_weight(ctypes.byref(d), d_x, _ptr(w_q), _ptr(w_uk), w_dtype, _ptr(a),
+                                         _stream(stream)), "mla_merge_query_weight")
+
+
+def mla_merge_output_weight(d, d_out, w_o, w_uv, w_dtype, bm, stream=None):
+    _check(load().mla_merge_output_weight(ctypes.byref(d), d_out, _ptr(w_o), _ptr(w_uv), w_dtype, _ptr(bm),
+                                          _stream(stream)), "mla_merge_output_weight")
+
+
+def mla_decode_merged_workspace_bytes(d, plan, d_out):
+    return load().mla_decode_merged_workspace_bytes(ctypes.byref(d), plan.handle, d_out)
+
+
+def mla_decode_merged(d, c, plan, d_x, x, q_rope, q_pos, a, d_out, bm, w_dtype, y, y_dtype, ws, stream=None):
+    _check(load().mla_decode_merged(ctypes.byref(d), ctypes.byref(c), plan.handle, d_x, _ptr(x), _ptr(q_rope),
+                                    _ptr(q_pos), _ptr(a), d_out, _ptr(bm), w_dtype, _ptr(y), y_dtype, _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)), "mla_decode_merged")
 
 
 def mla_append_decode(d, c, plan, h, n_new, w_dkv, w_kr, q_nope, q_rope, q_pos, w_uk, w_uv,

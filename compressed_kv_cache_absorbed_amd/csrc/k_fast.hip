@@ -258,13 +258,17 @@ struct RowBatch {
     }
   }
 };
-template <int NB>
+// EMIT: no W_UV product; o^ goes to ohat as bf16 hi and lo planes
+// [B, H 512] (the precomputed-weights decode applies W_O W_UV itself).
+template <int NB, bool EMIT>
 __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr, int G, int VH, int n_items,
                                                            const SeqInfo *__restrict__ seqs,
                                                            const int32_t *__restrict__ dev_len,
                                                            const uint16_t *__restrict__ opart,
                                                            const float *__restrict__ lse,
                                                            const uint16_t *__restrict__ w_uv, void *o, int o_bf16,
+                                                           uint16_t *__restrict__ ohat_hi,
+                                                           uint16_t *__restrict__ ohat_lo,
                                                            int32_t *__restrict__ status) {
   using namespace fast;
   constexpr int NW = 8;                            // waves
@@ -288,7 +292,7 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
   const int i = (L & 7) + 8 * (slot / per_head), g = (slot % per_head) / VH, vh = slot % VH;
   const int b0 = g * NB;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const bool wact = 16 * w < DV / VH;  // this wave has weight rows
+  const bool wact = !EMIT && 16 * w < DV / VH;  // this wave has weight rows
   const int vrow = vh * (DV / VH) + 16 * w;
 
   const int bl = tid / TPB, q = tid % TPB;
@@ -412,11 +416,20 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
         hi[e] = hv;
         lo[e] = static_cast<__bf16>(acc[e0 + e] - static_cast<float>(hv));
       }
-      char *row = so + bl * OROW + 2 * (c0 + e0);
-      *reinterpret_cast<bf16x8 *>(row) = hi;
-      *reinterpret_cast<bf16x8 *>(row + 16 * OROW) = lo;
+      if constexpr (EMIT) {
+        if (b < B) {
+          const size_t off = (static_cast<size_t>(b) * H + i) * DC + c0 + e0;
+          *reinterpret_cast<bf16x8 *>(ohat_hi + off) = hi;
+          *reinterpret_cast<bf16x8 *>(ohat_lo + off) = lo;
+        }
+      } else {
+        char *row = so + bl * OROW + 2 * (c0 + e0);
+        *reinterpret_cast<bf16x8 *>(row) = hi;
+        *reinterpret_cast<bf16x8 *>(row + 16 * OROW) = lo;
+      }
     }
   }
+  if constexpr (EMIT) return;
   __syncthreads();
 
   // 3. o = W_UV,i o^
@@ -594,8 +607,32 @@ hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache
   const dim3 grid(H * G * VH);
 #define MLA_COMBINE(NBV)                                                                                      \
   case NBV:                                                                                                  \
-    return launch_kernel(combine_fast_kernel<NBV>, grid, 512, 0, s, B, H, d.n_heads, G, VH, n_items, seqs, c.seq_len, \
-                         opart, lse, w_uv, o, o_bf16, status)
+    return launch_kernel(combine_fast_kernel<NBV, false>, grid, 512, 0, s, B, H, d.n_heads, G, VH, n_items, seqs, \
+                         c.seq_len, opart, lse, w_uv, o, o_bf16, nullptr, nullptr, status)
+  switch (nb) {
+    MLA_COMBINE(1);
+    MLA_COMBINE(2);
+    MLA_COMBINE(4);
+    MLA_COMBINE(8);
+    default:
+      MLA_COMBINE(16);
+  }
+#undef MLA_COMBINE
+}
+
+hipError_t launch_combine_fast_emit(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,
+                                    const SeqInfo *seqs, const uint16_t *opart, const float *lse, uint16_t *ohat_hi,
+                                    uint16_t *ohat_lo, int32_t *status) {
+  const int B = c.batch, H = d.n_heads;
+  if (B == 0) return hipSuccess;
+  int nb = 1;
+  while (nb < 16 && static_cast<int64_t>(H) * ((B + 2 * nb - 1) / (2 * nb)) >= 256) nb *= 2;
+  const int G = (B + nb - 1) / nb;
+  const dim3 grid(H * G);
+#define MLA_COMBINE(NBV)                                                                                      \
+  case NBV:                                                                                                  \
+    return launch_kernel(combine_fast_kernel<NBV, true>, grid, 512, 0, s, B, H, d.n_heads, G, 1, n_items, seqs,  \
+                         c.seq_len, opart, lse, nullptr, nullptr, 0, ohat_hi, ohat_lo, status)
   switch (nb) {
     MLA_COMBINE(1);
     MLA_COMBINE(2);

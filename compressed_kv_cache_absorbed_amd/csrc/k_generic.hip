@@ -193,10 +193,13 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(mla_dims d, mla_cac
   if (bad && tid == 0) set_status(status, MLA_ERR_PLAN);  // a block id outside the cache: block 0 was read
 }
 
+// With ohat set, o^ is written there ([B, H, d_c] fp32) and W_UV is not
+// applied (the precomputed-weights decode applies W_O W_UV itself).
 __global__ __launch_bounds__(256) void combine_generic_kernel(mla_dims d, mla_cache c, int n_items,
                                                              const SeqInfo *seqs, const float *opart,
                                                              const float *lse, const void *w_uv,
-                                                             mla_dtype qw, void *o, mla_dtype od, int32_t *status) {
+                                                             mla_dtype qw, void *o, mla_dtype od, float *ohat,
+                                                             int32_t *status) {
   extern __shared__ float oh[];  // [d_c]
   const int b = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -223,6 +226,11 @@ __global__ __launch_bounds__(256) void combine_generic_kernel(mla_dims d, mla_ca
     for (int cc = tid; cc < d.d_c; cc += 256) oh[cc] = 0.0f;
   }
   __syncthreads();
+  if (ohat) {
+    float *dst = ohat + (static_cast<int64_t>(b) * H + i) * d.d_c;
+    for (int cc = tid; cc < d.d_c; cc += 256) dst[cc] = oh[cc];
+    return;
+  }
   const int64_t obase = (static_cast<int64_t>(b) * H + i) * d.d_v;
   for (int v = wave; v < d.d_v; v += 4) {
     const int64_t wrow = (static_cast<int64_t>(i) * d.d_v + v) * d.d_c;
@@ -329,7 +337,14 @@ hipError_t launch_combine_generic(hipStream_t s, const mla_dims &d, const mla_ca
                                   const SeqInfo *seqs, const float *opart, const float *lse,
                                   const void *w_uv, mla_dtype qw, void *o, mla_dtype od, int32_t *status) {
   return launch_kernel(combine_generic_kernel, dim3(c.batch, d.n_heads), 256, sizeof(float) * d.d_c, s, d, c, n_items,
-                       seqs, opart, lse, w_uv, qw, o, od, status);
+                       seqs, opart, lse, w_uv, qw, o, od, nullptr, status);
+}
+
+hipError_t launch_combine_generic_emit(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,
+                                       const SeqInfo *seqs, const float *opart, const float *lse, float *ohat,
+                                       int32_t *status) {
+  return launch_kernel(combine_generic_kernel, dim3(c.batch, d.n_heads), 256, sizeof(float) * d.d_c, s, d, c, n_items,
+                       seqs, opart, lse, nullptr, MLA_F32, nullptr, MLA_F32, ohat, status);
 }
 
 hipError_t launch_copy(hipStream_t s, void *dst, const void *src, size_t n16) {

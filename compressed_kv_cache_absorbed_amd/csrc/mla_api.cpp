@@ -91,7 +91,8 @@ const char *kKernelNames[K_COUNT] = {
     "init",           "append_generic", "append_gemm",    "append_finish",
     "absorb_generic", "absorb_fast",    "decode_generic", "decode_bf16",
     "decode_fp8",     "combine_generic", "combine_fast",  "copy",
-    "read"};
+    "read",           "merge_gemm",     "absorb_merged",  "out_merged",
+    "combine_emit"};
 
 #define MLA_LAUNCH(stream, kid, call)          \
   do {                                         \
@@ -606,6 +607,148 @@ mla_status mla_calib_read(const void *src, size_t n_bytes, uint32_t *sink, void 
   if (n_bytes == 0) return MLA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   MLA_LAUNCH(s, K_READ, launch_read(s, src, n_bytes / 16, sink));
+  return MLA_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------- precomputed absorbed weights
+
+namespace {
+
+struct MergedWs {
+  mla::DecodeWs dec;
+  size_t ohat = 0, part = 0, total = 0;
+};
+
+// The decode workspace, then o^ (fp32 [B, H d_c], or bf16 hi and lo planes
+// of the same total size), then the K-split partials of the output product.
+MergedWs merged_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items, int32_t d_out) {
+  MergedWs w;
+  w.dec = mla::decode_ws_layout(d, batch, n_items, 1, false);
+  const int64_t K = static_cast<int64_t>(d.n_heads) * d.d_c;
+  size_t off = w.dec.total;
+  w.ohat = off;
+  off = align_up(off + sizeof(float) * batch * K, 256);
+  w.part = off;
+  off = align_up(off + sizeof(float) * mla::merged::out_splits(K) * batch * d_out, 256);
+  w.total = off;
+  return w;
+}
+
+bool merged_fast_path(const mla_dims &d, const mla_cache &c, mla_dtype wt, int32_t d_x, int32_t d_out) {
+  // (each of the query product's four waves takes d_x / 4 inputs, an even
+  // number of 64-wide steps)
+  return mla::decode_fast_path(d, c, wt) && d_x % 512 == 0 && d_out % 128 == 0;
+}
+
+mla_status check_weight_args(const mla_dims *dims, int32_t n, const void *p0, const void *p1, mla_dtype wt,
+                             const void *out) {
+  mla_status st = check_dims(dims, false, true);
+  if (st != MLA_OK) return st;
+  if (n < 1 || !p0 || !p1 || !out) return MLA_ERR_INVALID_ARG;
+  if (wt != MLA_F32 && wt != MLA_BF16) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(p0) || !aligned16(p1) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_merge_query_weight(const mla_dims *dims, int32_t d_x, const void *w_q, const void *w_uk,
+                                  mla_dtype w_dtype, void *a, void *stream) {
+  mla_status st = check_weight_args(dims, d_x, w_q, w_uk, w_dtype, a);
+  if (st != MLA_OK) return st;
+  const mla_dims &d = *dims;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // per head: A[c][x] = sum_n W_UK[n][c] W_Q[n][x]
+  const int64_t dn = d.d_nope, dc = d.d_c, dx = d_x;
+  MLA_LAUNCH(s, K_MERGE_GEMM,
+             launch_merge_gemm(s, d.n_heads, d.d_c, d_x, d.d_nope, w_uk, dn * dc, dc, 1, w_q, dn * dx, dx, 1, w_dtype,
+                               a, dc * dx, dx, 1, w_dtype));
+  return MLA_OK;
+}
+
+mla_status mla_merge_output_weight(const mla_dims *dims, int32_t d_out, const void *w_o, const void *w_uv,
+                                   mla_dtype w_dtype, void *bm, void *stream) {
+  mla_status st = check_weight_args(dims, d_out, w_o, w_uv, w_dtype, bm);
+  if (st != MLA_OK) return st;
+  const mla_dims &d = *dims;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // per head i: Bm[o][i d_c + c] = sum_v W_O[o][i d_v + v] W_UV[i][v][c]
+  const int64_t H = d.n_heads, dv = d.d_v, dc = d.d_c;
+  MLA_LAUNCH(s, K_MERGE_GEMM,
+             launch_merge_gemm(s, d.n_heads, d_out, d.d_c, d.d_v, w_o, dv, 1, H * dv, w_uv, dv * dc, dc, 1, w_dtype,
+                               bm, dc, H * dc, 1, w_dtype));
+  return MLA_OK;
+}
+
+size_t mla_decode_merged_workspace_bytes(const mla_dims *dims, const mla_plan *plan, int32_t d_out) {
+  if (check_dims(dims, false, true) != MLA_OK || !plan || d_out < 1) return 0;
+  return merged_ws_layout(*dims, plan->batch, plan->n_items, d_out).total;
+}
+
+mla_status mla_decode_merged(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan, int32_t d_x,
+                             const void *x, const void *q_rope, const int32_t *q_pos, const void *a, int32_t d_out,
+                             const void *bm, mla_dtype w_dtype, void *y, mla_dtype y_dtype, void *ws,
+                             size_t ws_bytes, void *stream) {
+  mla_status st = check_dims(dims, false, true);
+  if (st != MLA_OK) return st;
+  st = check_cache(*dims, cache);
+  if (st != MLA_OK) return st;
+  if (!plan || plan->batch != cache->batch) return MLA_ERR_INVALID_ARG;
+  if (!x || !q_rope || !a || !bm || !y || !ws || d_x < 1 || d_out < 1) return MLA_ERR_INVALID_ARG;
+  if (w_dtype != MLA_F32 && w_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
+  if (y_dtype != MLA_F32 && y_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(q_rope) || !aligned16(a) || !aligned16(bm) || !aligned16(y) || !aligned16(ws))
+    return MLA_ERR_INVALID_ARG;
+  const mla_dims &d = *dims;
+  const MergedWs w = merged_ws_layout(d, plan->batch, plan->n_items, d_out);
+  if (ws_bytes < w.total) return MLA_ERR_WORKSPACE;
+  const bool fast = merged_fast_path(d, *cache, w_dtype, d_x, d_out);
+  if (!fast) {
+    if (d.d_c > 1024 || sizeof(float) * (static_cast<size_t>(d.d_c) + d.d_rope + 260) > 64 * 1024 ||
+        sizeof(float) * static_cast<size_t>(d_x) > 64 * 1024)
+      return MLA_ERR_UNSUPPORTED;
+  }
+  if (!plan->host_dev) return MLA_ERR_HIP;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *base = static_cast<char *>(ws);
+  int32_t *status = reinterpret_cast<int32_t *>(base + w.dec.status);
+  WorkItem *items = reinterpret_cast<WorkItem *>(base + w.dec.items);
+  SeqInfo *seqs = reinterpret_cast<SeqInfo *>(base + w.dec.seqs);
+  const PlanRef pr{plan->host_dev, items, static_cast<int32_t>(plan->host_block_bytes / 16), plan->hash};
+  float *lse = reinterpret_cast<float *>(base + w.dec.lse);
+  const int64_t K = static_cast<int64_t>(d.n_heads) * d.d_c;
+  if (fast) {
+    uint16_t *q = reinterpret_cast<uint16_t *>(base + w.dec.q);
+    uint16_t *opart = reinterpret_cast<uint16_t *>(base + w.dec.opart);
+    uint16_t *ohat_hi = reinterpret_cast<uint16_t *>(base + w.ohat);
+    uint16_t *ohat_lo = ohat_hi + static_cast<size_t>(plan->batch) * K;
+    float *part = reinterpret_cast<float *>(base + w.part);
+    MLA_LAUNCH(s, K_ABSORB_MERGED,
+               launch_absorb_merged_fast(s, d, plan->batch, d_x, x, q_rope, q_pos, a, cache->seq_len, q, pr, status));
+    MLA_LAUNCH(s, cache->latent_dtype == MLA_FP8_E4M3 ? K_DECODE_FP8 : K_DECODE_BF16,
+               launch_decode_fast(s, d, *cache, 1, plan->n_items, items, seqs, q, opart, lse, status));
+    MLA_LAUNCH(s, K_COMBINE_EMIT,
+               launch_combine_fast_emit(s, d, *cache, plan->n_items, seqs, opart, lse, ohat_hi, ohat_lo, status));
+    MLA_LAUNCH(s, K_OUT_MERGED,
+               launch_out_merged_fast(s, plan->batch, d_out, K, bm, ohat_hi, ohat_lo, part, y, y_dtype == MLA_BF16));
+  } else {
+    float *q = reinterpret_cast<float *>(base + w.dec.q);
+    float *opart = reinterpret_cast<float *>(base + w.dec.opart);
+    float *ohat = reinterpret_cast<float *>(base + w.ohat);
+    MLA_LAUNCH(s, K_ABSORB_MERGED,
+               launch_absorb_merged_generic(s, d, plan->batch, d_x, x, q_rope, q_pos, a, w_dtype, cache->seq_len, q,
+                                            pr));
+    MLA_LAUNCH(s, K_DECODE_GENERIC,
+               launch_decode_generic(s, d, *cache, plan->n_items, items, seqs, q, opart, lse, status));
+    MLA_LAUNCH(s, K_COMBINE_EMIT,
+               launch_combine_generic_emit(s, d, *cache, plan->n_items, seqs, opart, lse, ohat, status));
+    MLA_LAUNCH(s, K_OUT_MERGED, launch_out_merged_generic(s, plan->batch, d_out, K, bm, w_dtype, ohat, y, y_dtype));
+  }
   return MLA_OK;
 }
 

@@ -36,6 +36,10 @@ enum KernelId : int {
   K_COMBINE_FAST,
   K_COPY,
   K_READ,
+  K_MERGE_GEMM,
+  K_ABSORB_MERGED,
+  K_OUT_MERGED,
+  K_COMBINE_EMIT,
   K_COUNT
 };
 
@@ -154,6 +158,34 @@ hipError_t launch_combine_generic(hipStream_t s, const mla_dims &d, const mla_ca
 hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, int32_t n_items,
                                const SeqInfo *seqs, const uint16_t *opart, const float *lse, const uint16_t *w_uv,
                                void *o, int o_bf16, int32_t *status);
+
+// Decode from precomputed absorbed weights (k_merged.hip). The combine
+// kernels, given ohat, write o^ instead of applying W_UV: fp32 [B, H d_c] on
+// the generic path, bf16 hi and lo planes [B, H 512] on the matrix-core path.
+namespace merged {
+constexpr int DC = 512;
+// K splits of the matrix-core output product (each a multiple of 256 wide)
+inline int out_splits(int64_t K) { return K % (16 * 256) == 0 ? 16 : 1; }
+}  // namespace merged
+hipError_t launch_merge_gemm(hipStream_t s, int T, int M, int N, int K, const void *P, int64_t sPt, int64_t sPk,
+                             int64_t sPm, const void *Q, int64_t sQt, int64_t sQk, int64_t sQn, mla_dtype in, void *C,
+                             int64_t sCt, int64_t sCm, int64_t sCn, mla_dtype out);
+hipError_t launch_absorb_merged_fast(hipStream_t s, const mla_dims &d, int32_t batch, int32_t d_x, const void *x,
+                                     const void *q_rope, const int32_t *q_pos, const void *a,
+                                     const int32_t *seq_len, uint16_t *q_out, const PlanRef &plan, int32_t *status);
+hipError_t launch_out_merged_fast(hipStream_t s, int32_t batch, int32_t d_out, int64_t K, const void *bm,
+                                  const uint16_t *ohat_hi, const uint16_t *ohat_lo, float *part, void *y, int y_bf16);
+hipError_t launch_absorb_merged_generic(hipStream_t s, const mla_dims &d, int32_t batch, int32_t d_x, const void *x,
+                                        const void *q_rope, const int32_t *q_pos, const void *a, mla_dtype wt,
+                                        const int32_t *seq_len, float *q_out, const PlanRef &plan);
+hipError_t launch_out_merged_generic(hipStream_t s, int32_t batch, int32_t d_out, int64_t K, const void *bm,
+                                     mla_dtype wt, const float *ohat, void *y, mla_dtype yt);
+hipError_t launch_combine_generic_emit(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,
+                                       const SeqInfo *seqs, const float *opart, const float *lse, float *ohat,
+                                       int32_t *status);
+hipError_t launch_combine_fast_emit(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,
+                                    const SeqInfo *seqs, const uint16_t *opart, const float *lse, uint16_t *ohat_hi,
+                                    uint16_t *ohat_lo, int32_t *status);
 
 hipError_t launch_copy(hipStream_t s, void *dst, const void *src, size_t n16);
 // *dst = *src for one int32 (a one-thread kernel: capturable, no memcpy node)

@@ -267,6 +267,56 @@ mla_status mla_decode_multi(const mla_dims *dims, const mla_cache *cache, const 
                             size_t ws_bytes, void *stream);
 size_t mla_decode_multi_workspace_bytes(const mla_dims *dims, const mla_plan *plan, int32_t q_len);
 
+/* Precomputed absorbed weights. The up-projections can be folded into the
+ * query and output projections ahead of time, so the decode never forms
+ * per-head keys or values ("02 — Multi-Latent Attention (MLA)", "Coste de
+ * cómputo": attention rearranged with some matrix products precomputed;
+ * "Atención latente de múltiples cabezas", "Información técnica": the
+ * up-projection weights absorbed into the query and output projections;
+ * "Multi-head Latent Attention (MLA) și arhitectura DeepSeekMoE", opening
+ * paragraph). The rotary query cannot be folded (same sections: the
+ * decoupled key path exists for that) and stays an input.
+ * Layouts: W_Q [n_heads, d_nope, d_x] (head i's no-RoPE query is
+ * W_Q,i x, x the token's query input: its hidden state, or a query latent
+ * where the model compresses queries); W_O [d_out, n_heads d_v] (the layer
+ * output is W_O applied to the heads' outputs concatenated in head order).
+ *
+ * mla_merge_query_weight — a [n_heads, d_c, d_x] = W_UK,i^T W_Q,i per head.
+ * mla_merge_output_weight — bm [d_out, n_heads d_c], column block i =
+ * W_O[:, i d_v .. (i+1) d_v) W_UV,i.
+ * One-time weight preparation (fp32 accumulation, stored in w_dtype, F32 or
+ * BF16 with round-to-nearest-even); the inputs keep their W_UK and W_UV
+ * layouts of mla_decode. All pointers are device memory the caller owns,
+ * 16-byte aligned; asynchronous on the stream. MLA_ERR_INVALID_ARG for
+ * invalid dims, d_x or d_out < 1, NULL or misaligned pointers, other dtypes.
+ * Sizes: a holds n_heads d_c d_x elements, bm d_out n_heads d_c; at the
+ * DeepSeek-V3 shape with a 1536-wide query latent and d_out = 7168 that is
+ * 201 MB and 940 MB in bf16, against 16.8 MB each for W_UK and W_UV. */
+mla_status mla_merge_query_weight(const mla_dims *dims, int32_t d_x, const void *w_q, const void *w_uk,
+                                  mla_dtype w_dtype, void *a, void *stream);
+mla_status mla_merge_output_weight(const mla_dims *dims, int32_t d_out, const void *w_o, const void *w_uv,
+                                   mla_dtype w_dtype, void *bm, void *stream);
+
+/* mla_decode_merged — mla_decode from the merged weights, emitting the
+ * post-W_O output: per sequence b and head i, q~_i = A_i x_b, the same
+ * scores, softmax and latent-space output o^_i as mla_decode, and
+ * y_b = bm [o^_1; ..; o^_n_heads].
+ *   x       [batch, d_x], w_dtype
+ *   q_rope  [batch, n_heads, d_rope], w_dtype, unrotated; q_pos as mla_decode
+ *   a, bm   from the merge calls, w_dtype (F32 or BF16)
+ *   y       [batch, d_out], y_dtype (F32 or BF16)
+ *   ws      at least mla_decode_merged_workspace_bytes(dims, plan, d_out)
+ * One query token per sequence. Matrix-core path when mla_decode's fast
+ * path applies (w_dtype BF16) and d_x % 512 == 0 and d_out % 128 == 0; else
+ * the fp32 kernels (d_x up to 16384). Errors, status word and numeric domain
+ * as mla_decode (o^ enters the output product as bf16 hi + lo, about 16
+ * significant bits). */
+mla_status mla_decode_merged(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan, int32_t d_x,
+                             const void *x, const void *q_rope, const int32_t *q_pos, const void *a, int32_t d_out,
+                             const void *bm, mla_dtype w_dtype, void *y, mla_dtype y_dtype, void *ws,
+                             size_t ws_bytes, void *stream);
+size_t mla_decode_merged_workspace_bytes(const mla_dims *dims, const mla_plan *plan, int32_t d_out);
+
 /* mla_append_decode — mla_append of n_new tokens followed, in stream order,
  * by mla_decode. The plan must have been made from the lengths after the
  * append (old lengths + n_new). ws must satisfy both workspace sizes. */

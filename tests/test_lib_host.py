@@ -179,6 +179,41 @@ def test_validation_rejects_before_launch():
     assert lib.mla_workspace_init(None, 256, None) == 1
 
 
+def test_merged_weight_calls_validate_before_launch():
+    """The precomputed-weights entry points refuse bad arguments with no HIP call."""
+    lib = m.load()
+    d = d128()
+    plan = m.mla_plan_create(d, [10, 20], 4)
+    P = 4096
+    # merges: sizes >= 1, F32 or BF16, 16-byte aligned non-NULL pointers
+    for fn in (lib.mla_merge_query_weight, lib.mla_merge_output_weight):
+        assert fn(ctypes.byref(d), 0, P, P, 1, P, None) == 1
+        assert fn(ctypes.byref(d), 256, P, P, 2, P, None) == 1
+        assert fn(ctypes.byref(d), 256, None, P, 1, P, None) == 1
+        assert fn(ctypes.byref(d), 256, P, P + 2, 1, P, None) == 1
+        assert fn(ctypes.byref(m.dims(128, 512, 63, 128, 128)), 256, P, P, 1, P, None) == 1
+    need = m.mla_decode_merged_workspace_bytes(d, plan, 7168)
+    assert need > m.mla_decode_workspace_bytes(d, plan)
+    # o^ (4 bytes per latent value) and 16 splits of fp32 outputs
+    assert need >= m.mla_decode_workspace_bytes(d, plan) + 4 * 2 * 128 * 512 + 4 * 16 * 2 * 7168
+    assert m.mla_decode_merged_workspace_bytes(d, plan, 0) == 0
+
+    def dm(c, d_x=1536, d_out=7168, wt=1, yt=0, ws_bytes=need, x=P, bm=P):
+        return lib.mla_decode_merged(ctypes.byref(d), ctypes.byref(c), plan.handle, d_x, x, P, None, P, d_out, bm,
+                                     wt, P, yt, P, ws_bytes, None)
+
+    assert dm(_cache_struct(), ws_bytes=need - 1) == 5
+    assert dm(_cache_struct(), d_x=0) == 1
+    assert dm(_cache_struct(), d_out=0) == 1
+    assert dm(_cache_struct(), wt=2) == 1
+    assert dm(_cache_struct(), yt=2) == 1
+    assert dm(_cache_struct(), x=None) == 1
+    assert dm(_cache_struct(), bm=P + 8) == 1
+    assert dm(_cache_struct(batch=3)) == 1
+    # the fp32 kernels stage x in 64 KB of LDS: d_x up to 16384
+    assert dm(_cache_struct(), d_x=16385 * 2, wt=0, ws_bytes=1 << 40) == 2
+
+
 def test_tensor_calls_check_dtypes_and_shapes():
     """The tensor-level calls refuse, before touching a device, activations
     and weights of mixed dtypes or of sizes that do not match the dims and
