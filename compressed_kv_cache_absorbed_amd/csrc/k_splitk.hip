@@ -1,17 +1,20 @@
 // Split-K flash-decode over the latent cache (the hot loop of MLA decode).
 //
 // One workgroup per work item (sequence b, tokens [t0, t1)) and 128 heads,
-// four waves; wave w owns heads 32 w .. 32 w + 31 from start to end. For
-// every tile of 32 cached tokens
+// four waves; wave w computes the scores and softmax of heads 32 w .. 32 w +
+// 31. For every tile of 32 cached tokens
 //   S^T [32 tok x 32 heads]  = K [32 x 576] Q^T [576 x 32 heads]
 //   online softmax per head, base 2 (Q is pre-scaled by scale * log2 e)
-//   O^T [512 x 32 heads]    += C^T [512 x 32 tok] P^T [32 tok x 32 heads]
+//   O^T [512 x 128 heads]   += C^T [512 x 32 tok] P^T [32 tok x 128 heads]
 // where K = [c_kv | k_rope] rows and C = the c_kv part of the same rows: the
 // score is the content term plus the positional term ("DeepSeek MLA" card),
 // and both products read the one tile, shared by all 128 heads, because W_UK
 // is already folded into Q and W_UV is applied after the loop ("02 —
-// Multi-Latent Attention (MLA)", "Coste de cómputo"). P never leaves the
-// registers of the wave that computed it.
+// Multi-Latent Attention (MLA)", "Coste de cómputo"). The value product is
+// split between the waves by latent columns for bf16 latents (wave w: columns
+// 128 w .. +127 of every head; the softmax weights of all heads pass through
+// LDS) and by heads for fp8 latents (wave w: its own 32 heads, the weights
+// straight from its registers).
 //
 // Arithmetic: both products take fp16 operands with fp32 accumulation. The
 // absorbed query arrives in fp16; cached values are widened to fp16 in LDS
@@ -22,9 +25,11 @@
 // compile-time constant and every LDS address a per-lane base plus a
 // constant):
 //   score products of tile i+1, with the softmax of tile i woven between
-//   them, the copies of tile i+3 (global_load_lds_dwordx4: straight into
-//   LDS, no registers) issued under them and this wave's rows of tile i+2
-//   widened under them; then the value products of tile i; one barrier.
+//   them and the copies of tile i+3 (global_load_lds_dwordx4: straight into
+//   LDS, no registers) issued under them; then the value products of tile
+//   i, with this wave's rows of tile i+2 widened under them (bf16; fp8
+//   widens under the score products); one barrier (bf16: two, the first
+//   before the value products read the exchanged weights).
 // Each wave widens exactly the rows it copied, so it waits for its own
 // copies only; the barrier makes the widened tile visible to all.
 //
