@@ -27,7 +27,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "M
 # Every extern "C" entry point of include/mla.h.
 EXPORTED = [
     "mla_append_workspace_bytes", "mla_append", "mla_plan_create", "mla_plan_destroy",
-    "mla_plan_num_items", "mla_plan_item", "mla_decode_workspace_bytes", "mla_workspace_bytes", "mla_decode",
+    "mla_plan_num_items", "mla_plan_item", "mla_plan_num_ranges", "mla_plan_range", "mla_decode_workspace_bytes", "mla_workspace_bytes", "mla_decode",
     "mla_decode_multi_workspace_bytes", "mla_decode_multi", "mla_decode_noalloc", "mla_append_decode",
     "mla_workspace_init", "mla_device_error", "mla_status_str",
     "mla_abi_version", "mla_prof_begin", "mla_prof_end", "mla_prof_kernel_name",
@@ -82,6 +82,8 @@ def load():
         "mla_plan_destroy": (None, [_P]),
         "mla_plan_num_items": (ctypes.c_int32, [_P]),
         "mla_plan_item": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, _P]),
+        "mla_plan_num_ranges": (ctypes.c_int32, [_P]),
+        "mla_plan_range": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P]),
         "mla_decode_workspace_bytes": (ctypes.c_size_t, [_P, _P]),
         "mla_workspace_bytes": (ctypes.c_size_t, [_P, _P]),
         "mla_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
@@ -181,6 +183,16 @@ class Plan:
             _check(lib.mla_plan_item(self.handle, k, ctypes.byref(b), ctypes.byref(t0), ctypes.byref(t1)),
                    "mla_plan_item")
             out.append((b.value, t0.value, t1.value))
+        return out
+
+    def ranges(self):
+        """[(first item, end item)] of every workgroup range."""
+        lib = load()
+        k0, k1 = ctypes.c_int32(), ctypes.c_int32()
+        out = []
+        for j in range(lib.mla_plan_num_ranges(self.handle)):
+            _check(lib.mla_plan_range(self.handle, j, ctypes.byref(k0), ctypes.byref(k1)), "mla_plan_range")
+            out.append((k0.value, k1.value))
         return out
 
     def __del__(self):

@@ -1,7 +1,8 @@
 // Split-K flash-decode over the latent cache (the hot loop of MLA decode).
 //
-// One workgroup per work item (sequence b, tokens [t0, t1)) and 128 heads,
-// four waves; wave w computes the scores and softmax of heads 32 w .. 32 w +
+// One workgroup per range of work items (each a sequence b and its tokens
+// [t0, t1), run one after the other) and 128 heads, four waves; wave w
+// computes the scores and softmax of heads 32 w .. 32 w +
 // 31. For every tile of 32 cached tokens
 //   S^T [32 tok x 32 heads]  = K [32 x 576] Q^T [576 x 32 heads]
 //   online softmax per head, base 2 (Q is pre-scaled by scale * log2 e)
@@ -44,9 +45,11 @@
 // raw buffer with their scales and are widened into it (three fp16 buffers,
 // two raw ones).
 #include <cmath>
+#include <cstdlib>
 
 #include "device_util.hpp"
 #include "splitk_addr.hpp"
+#include "splitk_common.hpp"
 
 namespace mla {
 
@@ -59,9 +62,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_S16X4(p) ((__attribute__((address_space(3))) s16x4 *)(p))
-// LDS byte offset of a __shared__ array (a link-time constant when applied
-// to the array itself).
-#define LDS_OFF(arr) static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char *)(arr)))
 
 namespace sk {
 constexpr int DC = 512, D = 576;
@@ -122,12 +122,6 @@ __device__ __forceinline__ void mfma_acc_v(f32x16 &c, f16x8 a, f16x8 b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 
-// 2 bf16 (one dword) -> 2 fp16, exact for |x| < 65504 (a bf16 significand
-// fits in fp16's); round-toward-zero saturates larger magnitudes to +-65504.
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
-  const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
-  return __builtin_bit_cast(uint32_t, h);
-}
 
 // k_rope chunk swizzle: chunk c of token t's row sits at c ^ rsw(t) (the
 // copies' source chunks use the same function).
@@ -135,42 +129,8 @@ using sa::rsw;
 static_assert(sk::T == sa::T && sk::RAW_DMA_PER_WAVE == sa::RAW_DMA_PER_WAVE && sk::RAW_ROWB == sa::RAW_ROWB,
               "tile geometry shared with the copy addresses");
 
-// A copy of a thread index the compiler cannot see through, so per-tile
-// address arithmetic is recomputed in place instead of hoisted into live
-// registers.
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
 
-// vmcnt(n) with expcnt / lgkmcnt left unconstrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
-// Direct-to-LDS loads (global_load_lds_dword / _dwordx4, SGPR base + 32-bit
-// lane offset): lane i's 4 / 16 bytes from base + voff land at LDS byte
-// lds_addr + 4 i / 16 i. Issued as inline asm so the compiler's own LDS-DMA
-// tracking (which, lacking alias-scope information, would wait for every
-// outstanding copy before any LDS read) stays out of the way; the kernel waits
-// for its copies explicitly with wait_vm<>(). The instructions have no
-// register results, and VMEM operations the compiler does not see can only
-// make its own vmcnt waits stricter, never too weak.
-__device__ __forceinline__ void lds_dma16(const char *base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(lds_addr)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(const char *base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(lds_addr)
-               : "memory", "m0");
-}
 
 using sa::Item;
 using sa::RawSrc;
@@ -764,32 +724,16 @@ __device__ __forceinline__ void step(WaveState &st, f32x16 &S, const Item &it, i
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Item k of the plan, head block y (of H / 128), by one workgroup.
 template <bool FP8>
-__global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H, int Hr, int q_len, int n_items,
-                                                        const WorkItem *__restrict__ items,
-                                                        const SeqInfo *__restrict__ seqs,
-                                                        const uint16_t *__restrict__ Q,
-                                                        uint16_t *__restrict__ opart,
-                                                        float *__restrict__ lse,
-                                                        int32_t *__restrict__ status) {
+__device__ __forceinline__ void splitk_item(const mla_cache &c, int H, int Hr, int q_len, int k, int y,
+                                            const WorkItem *__restrict__ items, const SeqInfo *__restrict__ seqs,
+                                            const uint16_t *__restrict__ Q, uint16_t *__restrict__ opart,
+                                            float *__restrict__ lse, int32_t *__restrict__ status) {
   using namespace sk;
-  // item k, head block y (of Y = H / 128): workgroup L runs on XCD L % 8;
-  // the items of one sequence are consecutive, so giving each XCD a
-  // contiguous block of items lets the splits of a sequence share its
-  // absorbed query in that XCD's L2, and the head blocks of one item, next
-  // to each other there, share its cache tiles
-  const int Y = H >> 7, nfull = n_items & ~7, lfull = nfull * Y, L = blockIdx.x;
-  int k, y;
-  if (L < lfull) {
-    const int sl = L >> 3;
-    k = (L & 7) * (nfull >> 3) + sl / Y;
-    y = sl - (sl / Y) * Y;
-  } else {
-    const int r = L - lfull;
-    k = nfull + r / Y;
-    y = r - (r / Y) * Y;
-  }
-  const int tid = threadIdx.x, lane = tid & 63;
+  // (through opaque(): the lane-derived addresses are then made per item, not
+  // hoisted out of the item loop and kept live across it)
+  const int tid = opaque(static_cast<int>(threadIdx.x)), lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int head = y * 128 + 32 * w + (lane & 31);
@@ -973,19 +917,48 @@ __global__ __launch_bounds__(256, 1) void splitk_kernel(mla_cache c, int H, int 
   }
 }
 
+// One workgroup per (range, head block): range j's items one after the other.
+template <bool FP8>
+__global__ __launch_bounds__(256, 1) void splitk_kernel(SplitArgs args) {
+  int j, y;
+  range_of(static_cast<int>(blockIdx.x), args.n_ranges, args.H >> 7, j, y);
+  const int kb = args.ranges[j], ke = args.ranges[j + 1];
+  if (kb < 0 || kb > ke || ke > args.n_items) {
+    if (threadIdx.x == 0) set_status(args.status, MLA_ERR_PLAN);
+    return;
+  }
+  for (int k = kb; k < ke; ++k) {
+    // every wave has read its turned-around rows of the last item out of
+    // LDS before the next item's first copies land there
+    if (k > kb) __syncthreads();
+    const KernArgs a = kernel_args();
+    splitk_item<FP8>(cache_of(a), a->H, a->Hr, a->q_len, k, y, a->items, a->seqs, a->Q, a->opart, a->lse, a->status);
+  }
+}
+
 }  // namespace
 
+// MLA_FP8_WIDEN=1 in the environment runs fp8 caches through the widening
+// kernel (fp16 products) instead of the fp8 matrix-core one, for comparing
+// the two on the same inputs.
+static bool fp8_widen() {
+  const char *e = std::getenv("MLA_FP8_WIDEN");
+  return e && e[0] == '1';
+}
+
 hipError_t launch_decode_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, int32_t n_items,
-                              const WorkItem *items, const SeqInfo *seqs, const uint16_t *q, uint16_t *opart,
-                              float *lse, int32_t *status) {
-  if (n_items == 0) return hipSuccess;
+                              int32_t n_ranges, const int32_t *ranges, const WorkItem *items, const SeqInfo *seqs,
+                              const uint16_t *q, uint16_t *opart, float *lse, int32_t *status) {
+  if (n_items == 0 || n_ranges == 0) return hipSuccess;
   const int H = d.n_heads * q_len;
-  const dim3 grid(n_items * (H / 128));
-  if (c.latent_dtype == MLA_FP8_E4M3)
-    return launch_kernel(splitk_kernel<true>, grid, 256, 0, s, c, H, d.n_heads, q_len, n_items, items, seqs, q, opart,
-                         lse, status);
-  return launch_kernel(splitk_kernel<false>, grid, 256, 0, s, c, H, d.n_heads, q_len, n_items, items, seqs, q, opart,
-                       lse, status);
+  const dim3 grid(n_ranges * (H / 128));
+  const SplitArgs args{c, H, d.n_heads, q_len, n_items, n_ranges, ranges, items, seqs, q, opart, lse, status};
+  if (c.latent_dtype == MLA_FP8_E4M3) {
+    if (!fp8_widen())
+      return launch_decode_fast8(s, d, c, q_len, n_items, n_ranges, ranges, items, seqs, q, opart, lse, status);
+    return launch_kernel(splitk_kernel<true>, grid, 256, 0, s, args);
+  }
+  return launch_kernel(splitk_kernel<false>, grid, 256, 0, s, args);
 }
 
 }  // namespace mla

@@ -152,8 +152,9 @@ void prof_after(hipStream_t, int kernel_id) {
   p.taken = false;
 }
 
-DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items, int32_t q_len, bool fast) {
+DecodeWs decode_ws_layout(const mla_dims &d, const mla_plan &plan, int32_t q_len, bool fast) {
   DecodeWs w;
+  const int32_t batch = plan.batch, n_items = plan.n_items;
   const size_t eb = fast ? 2 : sizeof(float);  // query and partial element size
   const size_t hq = static_cast<size_t>(d.n_heads) * std::max(q_len, 1);
   const size_t ni = static_cast<size_t>(std::max(n_items, 1));
@@ -166,7 +167,8 @@ DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items, int
   off = align_up(off + sizeof(float) * ni * hq, 256);
   w.items = off;
   w.seqs = off + sizeof(WorkItem) * n_items;
-  off = align_up(w.seqs + sizeof(SeqInfo) * batch, 256);
+  w.ranges = w.seqs + sizeof(SeqInfo) * batch;
+  off = align_up(off + plan.host_block_bytes, 256);
   w.total = off;
   return w;
 }
@@ -182,6 +184,56 @@ AppendWs append_ws_layout(const mla_dims &d, int32_t batch, int32_t n_new) {
   }
   w.total = off;
   return w;
+}
+
+// ------------------------------------------------------------- planning
+// A workgroup walks a range of consecutive items; its time is about its
+// tiles plus a fixed cost per item, counted here in tiles: at an item's
+// start its first copies arrive before any product can start, and at its
+// end the last tiles' products run with no copy under them, then the 128 KB
+// partial is written. Measured per workgroup on MI355X (the time of every
+// workgroup against its tiles and items, least squares): 2.4 us per tile
+// and 11.5 us per item with a bf16 cache, 2.3 and 13.3 with an fp8 one,
+// about five to six tiles.
+constexpr int64_t kItemCostTiles = 6;
+
+struct Cut {
+  std::vector<WorkItem> items;
+  std::vector<int32_t> ranges;  // the first item of every range
+};
+
+// Walks the sequences' tiles in order and fills each range up to cost cap
+// (tiles + kItemCostTiles per item); a piece has at least min_piece tiles
+// unless its sequence has fewer left. Returns the number of ranges, or
+// stops early once it passes limit; with out, records the items and the
+// first item of every range.
+int64_t cut_ranges(const int32_t *lens, int32_t batch, int64_t cap, int64_t min_piece, int64_t limit, Cut *out) {
+  const int64_t T = kTile;
+  int64_t n = 0, rem = 0;  // ranges so far, cost left in the current one
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t tiles = (static_cast<int64_t>(lens[b]) + T - 1) / T;
+    for (int64_t t = 0; t < tiles;) {
+      const int64_t left = tiles - t;
+      int64_t take = std::min(left, rem - kItemCostTiles);
+      if (take < std::min(left, min_piece)) {
+        // a new range (cap >= kItemCostTiles + min_piece: take >= 1)
+        if (++n > limit && !out) return n;
+        if (out) out->ranges.push_back(static_cast<int32_t>(out->items.size()));
+        rem = cap;
+        take = std::min(left, rem - kItemCostTiles);
+      }
+      if (out)
+        out->items.push_back({b, static_cast<int32_t>(t * T),
+                              static_cast<int32_t>(std::min<int64_t>((t + take) * T, lens[b])), 0});
+      rem -= kItemCostTiles + take;
+      t += take;
+    }
+  }
+  return n;
+}
+
+size_t plan_block_bytes(int32_t n_items, int32_t batch, int32_t n_ranges) {
+  return sizeof(WorkItem) * n_items + sizeof(SeqInfo) * batch + align_up(sizeof(int32_t) * (n_ranges + 1), 16);
 }
 
 }  // namespace mla
@@ -219,74 +271,48 @@ mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32
     maxlen = std::max<int64_t>(maxlen, host_lens[b]);
     nonempty += host_lens[b] > 0;
   }
-  int64_t min_tiles = 1;
+  int64_t min_piece = 1;
   if (n_workers == 0) {
-    min_tiles = 2;
+    min_piece = 2;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       return MLA_ERR_HIP;
     n_workers = cus;
   }
+  (void)maxlen;
 
-  // Smallest chunk C (a multiple of the tile) whose item count fits the
-  // workers; with more non-empty sequences than workers, aim for whole waves.
-  const int64_t T = kTile;
-  auto count = [&](int64_t C) {
-    int64_t n = 0;
-    for (int32_t b = 0; b < batch; ++b) n += (host_lens[b] + C - 1) / C;
-    return n;
-  };
-  int64_t target = n_workers;
-  if (nonempty > target) target = (nonempty + n_workers - 1) / n_workers * n_workers;
-  int64_t C = T;
+  // The smallest range cost whose cut needs at most n_workers ranges (the
+  // cut is monotone in the cost: a larger one never needs more ranges).
+  Cut cut;
   if (total > 0) {
-    int64_t lo = 1, hi = (maxlen + T - 1) / T;  // in tiles
+    const int64_t T = kTile;
+    int64_t lo = kItemCostTiles + min_piece;
+    int64_t hi = (total + T * nonempty) / T + kItemCostTiles * nonempty + min_piece;  // one range holds it all
     while (lo < hi) {
-      const int64_t mid = (lo + hi) / 2;
-      if (count(mid * T) <= target) hi = mid; else lo = mid + 1;
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (cut_ranges(host_lens, batch, mid, min_piece, n_workers, nullptr) <= n_workers) hi = mid; else lo = mid + 1;
     }
-    C = std::max(lo, min_tiles) * T;
+    cut_ranges(host_lens, batch, lo, min_piece, n_workers, &cut);
   }
+  cut.ranges.push_back(static_cast<int32_t>(cut.items.size()));  // the end of the last range
+  const int32_t n_ranges = static_cast<int32_t>(cut.ranges.size()) - 1;
 
-  std::vector<WorkItem> items;
   std::vector<SeqInfo> seqs(batch);
-  for (int32_t b = 0; b < batch; ++b) {
-    const int64_t L = host_lens[b];
-    const int64_t n = (L + C - 1) / C;
-    seqs[b].item_begin = static_cast<int32_t>(items.size());
-    seqs[b].item_count = static_cast<int32_t>(n);
-    seqs[b].len = static_cast<int32_t>(L);
-    seqs[b].pad = 0;
-    if (n == 0) continue;
-    // n nearly equal chunks, boundaries on tile multiples
-    const int64_t per = ((L + n - 1) / n + T - 1) / T * T;
-    for (int64_t k = 0, t0 = 0; k < n; ++k) {
-      const int64_t t1 = (k == n - 1) ? L : std::min(L, t0 + per);
-      items.push_back({b, static_cast<int32_t>(t0), static_cast<int32_t>(t1), 0});
-      t0 = t1;
-    }
-  }
-  // Dropping trailing empty chunks can happen when per * n > L; remove them.
-  std::vector<WorkItem> kept;
-  for (int32_t b = 0; b < batch; ++b) {
-    const int32_t begin = static_cast<int32_t>(kept.size());
-    for (int32_t k = 0; k < seqs[b].item_count; ++k) {
-      const WorkItem &it = items[seqs[b].item_begin + k];
-      if (it.t1 > it.t0) kept.push_back(it);
-    }
-    seqs[b].item_begin = begin;
-    seqs[b].item_count = static_cast<int32_t>(kept.size()) - begin;
+  for (int32_t b = 0; b < batch; ++b) seqs[b] = {0, 0, host_lens[b], 0};
+  for (size_t k = 0; k < cut.items.size(); ++k) {
+    SeqInfo &si = seqs[cut.items[k].b];
+    if (si.item_count++ == 0) si.item_begin = static_cast<int32_t>(k);
   }
 
   mla_plan *p = new (std::nothrow) mla_plan();
   if (!p) return MLA_ERR_INVALID_ARG;
   p->batch = batch;
-  p->n_items = static_cast<int32_t>(kept.size());
-  p->chunk = static_cast<int32_t>(C);
+  p->n_items = static_cast<int32_t>(cut.items.size());
+  p->n_ranges = n_ranges;
   p->n_workers = n_workers;
   p->lens.assign(host_lens, host_lens + batch);
-  p->host_block_bytes = sizeof(WorkItem) * kept.size() + sizeof(SeqInfo) * batch;
+  p->host_block_bytes = plan_block_bytes(p->n_items, batch, n_ranges);
   // pinned and mapped: the first kernel of a decode reads it directly when
   // the workspace's copy does not match. Without a device (host-side
   // planning, inspection) the block is ordinary memory and decodes refuse
@@ -305,8 +331,11 @@ mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32
   }
   p->host_block = blk;
   p->host_dev = dev;
-  std::memcpy(blk, kept.data(), sizeof(WorkItem) * kept.size());
-  std::memcpy(static_cast<char *>(blk) + sizeof(WorkItem) * kept.size(), seqs.data(), sizeof(SeqInfo) * batch);
+  std::memset(blk, 0, p->host_block_bytes);
+  std::memcpy(blk, cut.items.data(), sizeof(WorkItem) * cut.items.size());
+  std::memcpy(static_cast<char *>(blk) + sizeof(WorkItem) * cut.items.size(), seqs.data(), sizeof(SeqInfo) * batch);
+  std::memcpy(static_cast<char *>(blk) + sizeof(WorkItem) * cut.items.size() + sizeof(SeqInfo) * batch,
+              cut.ranges.data(), sizeof(int32_t) * (n_ranges + 1));
   const uint32_t *words = static_cast<const uint32_t *>(blk);
   uint64_t h = 0;
   for (size_t i = 0; i < p->host_block_bytes / 16; ++i)
@@ -326,6 +355,16 @@ void mla_plan_destroy(mla_plan *plan) {
 
 int32_t mla_plan_num_items(const mla_plan *plan) { return plan ? plan->n_items : -1; }
 
+int32_t mla_plan_num_ranges(const mla_plan *plan) { return plan ? plan->n_ranges : -1; }
+
+mla_status mla_plan_range(const mla_plan *plan, int32_t j, int32_t *item_begin, int32_t *item_end) {
+  if (!plan || !item_begin || !item_end || j < 0 || j >= plan->n_ranges) return MLA_ERR_INVALID_ARG;
+  const int32_t *r = reinterpret_cast<const int32_t *>(plan->seqs() + plan->batch);
+  *item_begin = r[j];
+  *item_end = r[j + 1];
+  return MLA_OK;
+}
+
 mla_status mla_plan_item(const mla_plan *plan, int32_t k, int32_t *b, int32_t *t0, int32_t *t1) {
   if (!plan || !b || !t0 || !t1 || k < 0 || k >= plan->n_items) return MLA_ERR_INVALID_ARG;
   const WorkItem &it = plan->items()[k];
@@ -344,7 +383,7 @@ size_t mla_append_workspace_bytes(const mla_dims *dims, int32_t batch, int32_t n
 size_t mla_decode_workspace_bytes(const mla_dims *dims, const mla_plan *plan) {
   if (check_dims(dims, false, true) != MLA_OK || !plan) return 0;
   // sized for the generic path's fp32 arrays, so one size serves either path
-  return decode_ws_layout(*dims, plan->batch, plan->n_items, 1, false).total;
+  return decode_ws_layout(*dims, *plan, 1, false).total;
 }
 
 size_t mla_workspace_bytes(const mla_dims *dims, const mla_plan *plan) {
@@ -356,7 +395,7 @@ size_t mla_workspace_bytes(const mla_dims *dims, const mla_plan *plan) {
 
 size_t mla_decode_multi_workspace_bytes(const mla_dims *dims, const mla_plan *plan, int32_t q_len) {
   if (check_dims(dims, false, true) != MLA_OK || !plan || q_len < 1 || q_len > kMaxQueryTokens) return 0;
-  return decode_ws_layout(*dims, plan->batch, plan->n_items, q_len, false).total;
+  return decode_ws_layout(*dims, *plan, q_len, false).total;
 }
 
 }  // extern "C"
@@ -448,7 +487,7 @@ mla_status decode_check_args(const mla_dims *dims, const mla_cache *cache, const
       !aligned16(o) || !aligned16(ws))
     return MLA_ERR_INVALID_ARG;
   if (q_len < 1 || q_len > kMaxQueryTokens) return MLA_ERR_INVALID_ARG;
-  if (ws_bytes < decode_ws_layout(*dims, plan->batch, plan->n_items, q_len, false).total) return MLA_ERR_WORKSPACE;
+  if (ws_bytes < decode_ws_layout(*dims, *plan, q_len, false).total) return MLA_ERR_WORKSPACE;
   if (!decode_fast_path(*dims, *cache, qw)) {
     if (q_len > 1) return MLA_ERR_UNSUPPORTED;
     if (dims->d_c > 1024) return MLA_ERR_UNSUPPORTED;
@@ -461,7 +500,7 @@ mla_status decode_check_args(const mla_dims *dims, const mla_cache *cache, const
 }
 
 size_t decode_compact_bytes(const mla_dims &d, const mla_cache &c, const mla_plan &plan, mla_dtype qw) {
-  return decode_ws_layout(d, plan.batch, plan.n_items, 1, decode_fast_path(d, c, qw)).total;
+  return decode_ws_layout(d, plan, 1, decode_fast_path(d, c, qw)).total;
 }
 
 mla_status decode_launch(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan, const void *q_nope,
@@ -469,11 +508,12 @@ mla_status decode_launch(const mla_dims *dims, const mla_cache *cache, const mla
                          void *o, mla_dtype od, void *ws, hipStream_t s, int32_t q_len, bool compact,
                          bool clear_status) {
   const bool fast = decode_fast_path(*dims, *cache, qw);
-  const DecodeWs w = decode_ws_layout(*dims, plan->batch, plan->n_items, q_len, compact && fast);
+  const DecodeWs w = decode_ws_layout(*dims, *plan, q_len, compact && fast);
   char *base = static_cast<char *>(ws);
   int32_t *status = reinterpret_cast<int32_t *>(base + w.status);
   WorkItem *items = reinterpret_cast<WorkItem *>(base + w.items);
   SeqInfo *seqs = reinterpret_cast<SeqInfo *>(base + w.seqs);
+  const int32_t *ranges = reinterpret_cast<const int32_t *>(base + w.ranges);
   // the absorb kernel checks this copy against the plan (and refetches it)
   // before the kernels after it read it
   const PlanRef pr{plan->host_dev, items, static_cast<int32_t>(plan->host_block_bytes / 16), plan->hash};
@@ -487,7 +527,8 @@ mla_status decode_launch(const mla_dims *dims, const mla_cache *cache, const mla
                launch_absorb_fast(s, *dims, plan->batch, q_len, q_nope, q_rope, q_pos, w_uk, cache->seq_len, q, pr,
                                   status));
     MLA_LAUNCH(s, cache->latent_dtype == MLA_FP8_E4M3 ? K_DECODE_FP8 : K_DECODE_BF16,
-               launch_decode_fast(s, *dims, *cache, q_len, plan->n_items, items, seqs, q, opart16, lse, status));
+               launch_decode_fast(s, *dims, *cache, q_len, plan->n_items, plan->n_ranges, ranges, items, seqs, q, opart16, lse,
+                                  status));
     MLA_LAUNCH(s, K_COMBINE_FAST,
                launch_combine_fast(s, *dims, *cache, q_len, plan->n_items, seqs, opart16, lse,
                                    static_cast<const uint16_t *>(w_uv), o, od, status));
@@ -623,9 +664,10 @@ struct MergedWs {
 
 // The decode workspace, then o^ (fp32 [B, H d_c], or bf16 hi and lo planes
 // of the same total size), then the K-split partials of the output product.
-MergedWs merged_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items, int32_t d_out) {
+MergedWs merged_ws_layout(const mla_dims &d, const mla_plan &plan, int32_t d_out) {
   MergedWs w;
-  w.dec = mla::decode_ws_layout(d, batch, n_items, 1, false);
+  const int32_t batch = plan.batch;
+  w.dec = mla::decode_ws_layout(d, plan, 1, false);
   const int64_t K = static_cast<int64_t>(d.n_heads) * d.d_c;
   size_t off = w.dec.total;
   w.ohat = off;
@@ -686,7 +728,7 @@ mla_status mla_merge_output_weight(const mla_dims *dims, int32_t d_out, const vo
 
 size_t mla_decode_merged_workspace_bytes(const mla_dims *dims, const mla_plan *plan, int32_t d_out) {
   if (check_dims(dims, false, true) != MLA_OK || !plan || d_out < 1) return 0;
-  return merged_ws_layout(*dims, plan->batch, plan->n_items, d_out).total;
+  return merged_ws_layout(*dims, *plan, d_out).total;
 }
 
 mla_status mla_decode_merged(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan, int32_t d_x,
@@ -704,7 +746,7 @@ mla_status mla_decode_merged(const mla_dims *dims, const mla_cache *cache, const
   if (!aligned16(x) || !aligned16(q_rope) || !aligned16(a) || !aligned16(bm) || !aligned16(y) || !aligned16(ws))
     return MLA_ERR_INVALID_ARG;
   const mla_dims &d = *dims;
-  const MergedWs w = merged_ws_layout(d, plan->batch, plan->n_items, d_out);
+  const MergedWs w = merged_ws_layout(d, *plan, d_out);
   if (ws_bytes < w.total) return MLA_ERR_WORKSPACE;
   const bool fast = merged_fast_path(d, *cache, w_dtype, d_x, d_out);
   if (!fast) {
@@ -719,6 +761,7 @@ mla_status mla_decode_merged(const mla_dims *dims, const mla_cache *cache, const
   int32_t *status = reinterpret_cast<int32_t *>(base + w.dec.status);
   WorkItem *items = reinterpret_cast<WorkItem *>(base + w.dec.items);
   SeqInfo *seqs = reinterpret_cast<SeqInfo *>(base + w.dec.seqs);
+  const int32_t *ranges = reinterpret_cast<const int32_t *>(base + w.dec.ranges);
   const PlanRef pr{plan->host_dev, items, static_cast<int32_t>(plan->host_block_bytes / 16), plan->hash};
   float *lse = reinterpret_cast<float *>(base + w.dec.lse);
   const int64_t K = static_cast<int64_t>(d.n_heads) * d.d_c;
@@ -731,7 +774,7 @@ mla_status mla_decode_merged(const mla_dims *dims, const mla_cache *cache, const
     MLA_LAUNCH(s, K_ABSORB_MERGED,
                launch_absorb_merged_fast(s, d, plan->batch, d_x, x, q_rope, q_pos, a, cache->seq_len, q, pr, status));
     MLA_LAUNCH(s, cache->latent_dtype == MLA_FP8_E4M3 ? K_DECODE_FP8 : K_DECODE_BF16,
-               launch_decode_fast(s, d, *cache, 1, plan->n_items, items, seqs, q, opart, lse, status));
+               launch_decode_fast(s, d, *cache, 1, plan->n_items, plan->n_ranges, ranges, items, seqs, q, opart, lse, status));
     MLA_LAUNCH(s, K_COMBINE_EMIT,
                launch_combine_fast_emit(s, d, *cache, plan->n_items, seqs, opart, lse, ohat_hi, ohat_lo, status));
     MLA_LAUNCH(s, K_OUT_MERGED,

@@ -64,9 +64,11 @@ struct alignas(16) SeqInfo {
 struct mla_plan {
   int32_t batch = 0;
   int32_t n_items = 0;
-  int32_t chunk = 0;
+  int32_t n_ranges = 0;            // workgroup ranges: range j runs items ranges[j] .. ranges[j + 1] - 1
   int32_t n_workers = 0;
-  void *host_block = nullptr;      // [n_items WorkItem][batch SeqInfo], pinned when a device is there
+  // [n_items WorkItem][batch SeqInfo][n_ranges + 1 int32, padded to 16
+  // bytes], pinned when a device is there
+  void *host_block = nullptr;
   const void *host_dev = nullptr;  // the same block's device address (nullptr: not pinned)
   bool pinned = false;
   size_t host_block_bytes = 0;
@@ -91,12 +93,15 @@ struct DecodeWs {
   size_t opart = 0;   // normalised split partials [n_items, H, d_c]: fp16 (matrix-core path) or f32
   size_t lse = 0;     // f32 [n_items, H]
   size_t items = 0;   // WorkItem[n_items]
-  size_t seqs = 0;    // SeqInfo[batch] (directly after the items: one copy of the plan's block)
+  size_t seqs = 0;    // SeqInfo[batch]
+  size_t ranges = 0;  // int32[n_ranges + 1] (items, seqs, ranges: one copy of the plan's block)
   size_t total = 0;
 };
 // q_len new query tokens per sequence multiply every per-head array; fast
 // selects the matrix-core path's 2-byte query and partials.
-DecodeWs decode_ws_layout(const mla_dims &d, int32_t batch, int32_t n_items, int32_t q_len, bool fast);
+DecodeWs decode_ws_layout(const mla_dims &d, const mla_plan &plan, int32_t q_len, bool fast);
+// Bytes of a plan's block: its items, sequence records and range starts.
+size_t plan_block_bytes(int32_t n_items, int32_t batch, int32_t n_ranges);
 
 struct AppendWs {
   size_t status = 0;
@@ -148,9 +153,16 @@ hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, i
 hipError_t launch_decode_generic(hipStream_t s, const mla_dims &d, const mla_cache &c,
                                  int32_t n_items, const WorkItem *items, const SeqInfo *seqs,
                                  const float *q, float *opart, float *lse, int32_t *status);
+// fp8 latents on the fp8 matrix cores (k_splitk8.hip); launch_decode_fast
+// sends fp8 caches there.
+// The matrix-core split-K kernels run one workgroup per (range, head block
+// of 128): it walks the range's items one after the other.
+hipError_t launch_decode_fast8(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, int32_t n_items,
+                               int32_t n_ranges, const int32_t *ranges, const WorkItem *items, const SeqInfo *seqs,
+                               const uint16_t *q, uint16_t *opart, float *lse, int32_t *status);
 hipError_t launch_decode_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len,
-                              int32_t n_items, const WorkItem *items, const SeqInfo *seqs,
-                              const uint16_t *q, uint16_t *opart, float *lse, int32_t *status);
+                              int32_t n_items, int32_t n_ranges, const int32_t *ranges, const WorkItem *items,
+                              const SeqInfo *seqs, const uint16_t *q, uint16_t *opart, float *lse, int32_t *status);
 
 hipError_t launch_combine_generic(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_items,
                                   const SeqInfo *seqs, const float *opart, const float *lse,

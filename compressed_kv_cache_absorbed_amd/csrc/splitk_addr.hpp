@@ -129,6 +129,27 @@ __host__ __device__ inline uint32_t raw_piece_off(const RawSrc &rs, int w, int l
   return static_cast<uint32_t>(imin(t, rs.tmax) - rs.t0) * static_cast<uint32_t>(rs.stride) +
          static_cast<uint32_t>(16 * ch);
 }
+// The fp8 matrix-core kernel keeps the raw rows at the same 640-byte stride
+// but permutes each row's 16-byte chunks: slot p of token t's row holds
+// chunk p ^ rsw8(t) (an XOR of the low three bits: a chunk stays in its
+// aligned group of eight, so the 32 code chunks and the 8 k_rope chunks keep
+// their places). The permutation spreads the rows over the LDS banks both
+// for reads of two chunks of one row per lane and for the transposed 8-byte
+// reads of 8 rows at once.
+__host__ __device__ inline int rsw8(int t) { return ((t >> 2) & 1) | (((t >> 1) & 1) << 1) | (((t >> 3) & 1) << 2); }
+// Raw copy x (< 5) of wave w, lane ln, into that permuted layout: slot
+// P = 64 (5 w + x) + ln of the tile (token P / 40, slot P % 40) receives
+// chunk (P % 40) ^ rsw8(token) of the token's row. Offset from rs.base.
+// (P / 40 as (P 1639) >> 16, exact for the tile's 1280 slots: it keeps the
+// division off the copies' issue path)
+__host__ __device__ inline uint32_t raw_piece_off_sw(const RawSrc &rs, int w, int ln, int x) {
+  const int q = RAW_DMA_PER_WAVE * w + x;
+  const uint32_t P = static_cast<uint32_t>(64 * q + ln);
+  const int t = static_cast<int>((P * 1639u) >> 16);
+  const int ch = (static_cast<int>(P) - 40 * t) ^ rsw8(t);
+  return static_cast<uint32_t>(imin(t, rs.tmax) - rs.t0) * static_cast<uint32_t>(rs.stride) +
+         static_cast<uint32_t>(16 * ch);
+}
 // The scale copy: lane ln reads the scale of token ln % 32 (clamped), as an
 // offset from rs.sbase.
 __host__ __device__ inline uint32_t raw_scale_off(const RawSrc &rs, int ln) {

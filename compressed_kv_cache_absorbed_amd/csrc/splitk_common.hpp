@@ -1,0 +1,125 @@
+// Helpers shared by the split-K kernels (bf16 / fp16-widened and fp8
+// matrix-core forms): bf16 -> fp16 conversion, wait counters, direct-to-LDS
+// copies.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+// LDS byte offset of a __shared__ array (a link-time constant when applied
+// to the array itself).
+#define LDS_OFF(arr) static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char *)(arr)))
+
+namespace mla {
+namespace {
+
+// 2 bf16 (one dword) -> 2 fp16, exact for |x| < 65504 (a bf16 significand
+// fits in fp16's); round-toward-zero saturates larger magnitudes to +-65504.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// A copy of a thread index the compiler cannot see through, so per-tile
+// address arithmetic is recomputed in place instead of hoisted into live
+// registers.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// vmcnt(n) with expcnt / lgkmcnt left unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// Direct-to-LDS loads (global_load_lds_dword / _dwordx4, SGPR base + 32-bit
+// lane offset): lane i's 4 / 16 bytes from base + voff land at LDS byte
+// lds_addr + 4 i / 16 i. Issued as inline asm so the compiler's own LDS-DMA
+// tracking (which, lacking alias-scope information, would wait for every
+// outstanding copy before any LDS read) stays out of the way; the kernel waits
+// for its copies explicitly with wait_vm<>(). The instructions have no
+// register results, and VMEM operations the compiler does not see can only
+// make its own vmcnt waits stricter, never too weak.
+__device__ __forceinline__ void lds_dma16(const char *base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const char *base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// A split-K launch's arguments, passed as the kernel's only argument.
+struct SplitArgs {
+  mla_cache c;
+  int H, Hr, q_len, n_items, n_ranges;
+  const int32_t *ranges;
+  const WorkItem *items;
+  const SeqInfo *seqs;
+  const uint16_t *Q;
+  uint16_t *opart;
+  float *lse;
+  int32_t *status;
+};
+static_assert(sizeof(SplitArgs) % 4 == 0, "SplitArgs is read as 32-bit words");
+
+typedef const __attribute__((address_space(4))) SplitArgs *KernArgs;
+
+// The arguments, read again from the kernel-argument segment (scalar loads
+// through an address the compiler cannot follow, each where it is used): a
+// workgroup that walks several items reads them afresh for each, so none of
+// them stays live in registers across the item loop.
+__device__ __forceinline__ KernArgs kernel_args() {
+  KernArgs p = (KernArgs)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return p;
+}
+// (field by field: a struct in that address space does not bind to a
+// reference)
+__device__ __forceinline__ mla_cache cache_of(KernArgs a) {
+  mla_cache c;
+  c.latent_dtype = a->c.latent_dtype;
+  c.rope_dtype = a->c.rope_dtype;
+  c.rows = a->c.rows;
+  c.row_stride = a->c.row_stride;
+  c.scale = a->c.scale;
+  c.n_rows = a->c.n_rows;
+  c.batch = a->c.batch;
+  c.seq_start = a->c.seq_start;
+  c.seq_cap = a->c.seq_cap;
+  c.seq_len = a->c.seq_len;
+  c.block_table = a->c.block_table;
+  c.block_tokens = a->c.block_tokens;
+  c.max_blocks = a->c.max_blocks;
+  return c;
+}
+
+// Workgroup L of a split-K launch over R ranges and Y head blocks of 128:
+// range j, head block y. Workgroup L runs on XCD L % 8, so each XCD takes a
+// contiguous block of ranges: a sequence's items are consecutive, and the
+// splits of a sequence then share its absorbed query in that XCD's L2; the
+// head blocks of one range, next to each other there, share its cache tiles.
+__device__ __forceinline__ void range_of(int L, int R, int Y, int &j, int &y) {
+  const int nfull = R & ~7, lfull = nfull * Y;
+  if (L < lfull) {
+    const int sl = L >> 3;
+    j = (L & 7) * (nfull >> 3) + sl / Y;
+    y = sl - (sl / Y) * Y;
+  } else {
+    const int r = L - lfull;
+    j = nfull + r / Y;
+    y = r - (r / Y) * Y;
+  }
+}
+
+}  // namespace
+}  // namespace mla

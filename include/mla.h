@@ -156,17 +156,20 @@ mla_status mla_append(const mla_dims *dims, const mla_cache *cache, const void *
 
 /* -------------------------------------------------------------------- plan
  * mla_plan_create — split the decode work of a batch with cached lengths
- * host_lens[batch] (host) into work items (b, t0, t1) of about equal token
- * counts, so that one launch fills the GPU even for a few long sequences.
- * Split-K over the sequence is not on the pages; it is exact by the
- * log-sum-exp identity (the combine step). n_workers is the number of
- * concurrent work items to aim for; 0 means "derive from the current HIP
- * device" (one per compute unit), and then no item is made shorter than
- * 64 tokens unless its sequence is (an item's fixed cost, its first copies
- * and its partial result, outweighs a one-tile item's work; a 4K-token
- * sequence alone runs fastest in 64 items of two tiles).
- * With an explicit n_workers the chunks are as short as that count needs
- * (one 32-token tile at the least). The plan is deterministic in its inputs
+ * host_lens[batch] (host) into work items (b, t0, t1), pieces of one
+ * sequence on 32-token tile boundaries, listed in sequence order, and cut
+ * that list into at most n_workers ranges of consecutive items, one
+ * workgroup (per 128 heads) each, so that one launch fills the GPU and its
+ * workgroups finish together whatever the mix of lengths. The ranges are
+ * balanced on tiles plus a fixed cost of six tiles per item (an item's
+ * pipeline fill and drain and its 128 KB partial result): the concatenated
+ * tiles of all sequences are cut at about equal cost, so a range may end
+ * one sequence and begin the next. Split-K over the sequence is not on the
+ * pages; it is exact by the log-sum-exp identity (the combine step).
+ * n_workers 0 means "derive from the current HIP device" (one range per
+ * compute unit), and then no item is made shorter than 64 tokens unless its
+ * sequence (or what a range leaves of it) is; with an explicit n_workers
+ * items may be a single 32-token tile. The plan is deterministic in its inputs
  * and reusable across layers and calls with the same lengths. Its work list
  * lives in pinned host memory mapped for the current device, which the
  * decode's first kernel reads when a workspace's copy of it does not match;
@@ -177,9 +180,13 @@ mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32
                            int32_t n_workers, mla_plan **out);
 void mla_plan_destroy(mla_plan *plan);
 /* Plan inspection (host): number of work items, and item k's
- * (sequence, first token, end token). */
+ * (sequence, first token, end token); number of workgroup ranges, and range
+ * j's items [item_begin, item_end). MLA_ERR_INVALID_ARG for an index out
+ * of range or a null pointer (the counts return -1 for a null plan). */
 int32_t mla_plan_num_items(const mla_plan *plan);
 mla_status mla_plan_item(const mla_plan *plan, int32_t k, int32_t *b, int32_t *t0, int32_t *t1);
+int32_t mla_plan_num_ranges(const mla_plan *plan);
+mla_status mla_plan_range(const mla_plan *plan, int32_t j, int32_t *item_begin, int32_t *item_end);
 
 /* ------------------------------------------------------------------ decode
  * mla_decode — one query token per sequence attends over its cached rows.

@@ -141,6 +141,25 @@ void check_tile(const Layout &L, int cap, int t0, int n, int tile, bool fp8) {
           const int P = 64 * (RAW_DMA_PER_WAVE * w + x) + lane;
           if (tok != ts + imin(P / 40, src.tmax) || byte != 16 * (P % 40))
             fail("raw piece of the wrong token or chunk", n, t0, tile, w, lane, x);
+          // the permuted layout of the fp8 matrix-core kernel: the same
+          // token, chunk (P % 40) ^ rsw8(P / 40), still one of the row's 40
+          locate(rs.base + raw_piece_off_sw(rs, w, lane, x), 16, "permuted raw piece out of the item", w, lane, x,
+                 &tok, &byte);
+          if (tok != ts + imin(P / 40, src.tmax) || byte != 16 * ((P % 40) ^ rsw8(P / 40)) || byte + 16 > 640)
+            fail("permuted raw piece of the wrong token or chunk", n, t0, tile, w, lane, x);
+        }
+      }
+      // the multiply that stands for the division by 40 is exact on every slot
+      for (int P = 0; P < 32 * 40; ++P)
+        if (static_cast<int>((static_cast<uint32_t>(P) * 1639u) >> 16) != P / 40) fail("slot row", n, t0, tile, w, 0, P);
+      // the permutation is one within every row: each of a token's 40 slots
+      // receives a different chunk
+      for (int t = 8 * w; t < 8 * w + 8; ++t) {
+        bool seen[40] = {};
+        for (int p = 0; p < 40; ++p) {
+          const int c = p ^ rsw8(t);
+          if (c < 0 || c >= 40 || seen[c]) fail("raw chunk permutation", n, t0, tile, w, 0, t);
+          seen[c] = true;
         }
       }
       for (int lane = 0; lane < 64; ++lane) {

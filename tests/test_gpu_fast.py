@@ -87,8 +87,8 @@ def test_fast_256_heads(gpu, latent):
 def test_fast_combine_group_sizes(gpu, B, max_len, splits):
     """The combine kernel groups 1, 2, 4, 8 or 16 sequences per workgroup
     (by batch size); every grouping, with a partial last group, and more
-    splits per sequence than one batch of row loads holds (B = 1 with 188
-    splits, B = 20 with up to 38)."""
+    splits per sequence than one batch of row loads holds (B = 1 with 182
+    splits, 128 a batch; B = 20 with up to 18, 12 a batch)."""
     rng = np.random.default_rng(1000 + B + max_len)
     lens = [int(x) for x in rng.integers(max_len // 2 if max_len > 1000 else 1, max_len, size=B)]
     case = v3_case(lens, seed=60 + B)

@@ -69,25 +69,72 @@ def test_plan_covers_every_token_once(lens, workers):
         # boundaries on tile multiples
         for t0, t1 in segs:
             assert t0 % 32 == 0
-    nonempty = sum(1 for L in lens if L)
-    if nonempty <= workers:
-        assert len(items) <= max(workers, nonempty)
+    # the ranges cut the item list in order into at most `workers` non-empty runs
+    ranges = p.ranges()
+    assert len(ranges) <= workers
+    assert [k for r in ranges for k in range(*r)] == list(range(len(items)))
+    assert all(k1 > k0 for k0, k1 in ranges)
+    assert (len(ranges) == 0) == (sum(lens) == 0)
+
+
+ITEM_COST = 6  # the planner's fixed cost of an item, in tiles
+
+
+def range_costs(p):
+    """Tiles plus ITEM_COST per item, the planner's cost, of every range."""
+    items = p.items()
+    return [sum((items[k][2] - items[k][1] + 31) // 32 + ITEM_COST for k in range(k0, k1)) for k0, k1 in p.ranges()]
 
 
 def test_plan_balances_equal_sequences():
     p = m.mla_plan_create(d128(), [8192] * 32, 256)
     sizes = [t1 - t0 for _, t0, t1 in p.items()]
     assert len(sizes) == 256 and max(sizes) == min(sizes) == 1024
+    assert p.ranges() == [(k, k + 1) for k in range(256)]
 
 
-def test_plan_ragged_makespan_near_ideal():
-    rng = np.random.default_rng(2)
-    lens = rng.integers(4096, 8192, 32, endpoint=True).tolist()
+@pytest.mark.parametrize("lens,workers", [
+    (np.random.default_rng(2).integers(4096, 8192, 32, endpoint=True).tolist(), 256),
+    (np.exp(np.random.default_rng(3).uniform(np.log(1024), np.log(32768), 128)).astype(int).tolist(), 256),
+    ([100000, 10, 10, 5000] + [64] * 40, 256), ([33] * 1000, 256), ([65536], 100),
+])
+def test_plan_ranges_balanced(lens, workers):
+    """Each range costs at most the average cost, counting one more item per
+    sequence and per range (the splits), plus one piece of slack."""
+    p = m.mla_plan_create(d128(), lens, workers)
+    tiles = sum((L + 31) // 32 for L in lens)
+    nonempty = sum(1 for L in lens if L)
+    costs = range_costs(p)
+    assert max(costs) <= (tiles + ITEM_COST * (nonempty + workers)) / workers + ITEM_COST + 2
+    # the longest range's tiles within 6 % + 3 tiles of the balanced share
+    items = p.items()
+    rt = [sum((items[k][2] - items[k][1] + 31) // 32 for k in range(*r)) for r in p.ranges()]
+    assert max(rt) <= 1.06 * tiles / workers + 3 or len(lens) > workers
+
+
+def test_plan_lognormal_lengths_beat_per_sequence_chunks():
+    """Log-uniform lengths 1K..32K over 128 sequences: no range holds more
+    than 2 % over the balanced share of tiles (one common chunk size per
+    sequence would leave the longest chunk about a third over it)."""
+    lens = np.exp(np.random.default_rng(4).uniform(np.log(1024), np.log(32768), 128)).astype(int).tolist()
     p = m.mla_plan_create(d128(), lens, 256)
-    sizes = [t1 - t0 for _, t0, t1 in p.items()]
-    assert len(sizes) <= 256
-    ideal = sum(lens) / 256
-    assert max(sizes) <= 1.25 * ideal + 32
+    items = p.items()
+    rt = [sum((items[k][2] - items[k][1] + 31) // 32 for k in range(*r)) for r in p.ranges()]
+    share = sum((L + 31) // 32 for L in lens) / 256
+    assert max(rt) <= 1.02 * share + 2
+
+
+def test_plan_inspection_rejects_bad_index():
+    p = m.mla_plan_create(d128(), [100, 5000], 8)
+    lib = m.load()
+    k0, k1 = ctypes.c_int32(), ctypes.c_int32()
+    n = lib.mla_plan_num_ranges(p.handle)
+    assert 1 <= n <= 8
+    assert lib.mla_plan_range(p.handle, n - 1, ctypes.byref(k0), ctypes.byref(k1)) == 0 and k1.value == p.n_items
+    for j in (-1, n):
+        assert lib.mla_plan_range(p.handle, j, ctypes.byref(k0), ctypes.byref(k1)) == 1
+    assert lib.mla_plan_range(p.handle, 0, None, ctypes.byref(k1)) == 1
+    assert lib.mla_plan_num_ranges(None) == -1
 
 
 def test_plan_rejects_bad_input():
