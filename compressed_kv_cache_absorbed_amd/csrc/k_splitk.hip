@@ -588,6 +588,10 @@ __device__ __forceinline__ void pv_cols(WaveState &st, bool fresh, Hide &hide, f
 // i+3 may still fly), and converted and stored two products later. The
 // latent copy's source row pointer advances by the stride per row (no
 // multiply), and stops at the item's last row.
+// (kBf16CopiesUnderValues: the copies of tile i+3 go under the value
+// products instead, after value products 1, 4, .., 22 and the k_rope part
+// after 25, once every earlier copy has landed.)
+constexpr bool kBf16CopiesUnderValues = true;
 template <int DMA_BUF, int WIDEN_BUF>
 struct HideBf16 {
   const char *row;        // latent source of the next copy
@@ -597,21 +601,28 @@ struct HideBf16 {
   uint32_t rope_voff;     // this lane's k_rope source offset from rope_base
   int w, lane, tid;
   u32x4 v[2];
-  __device__ __forceinline__ void score_step(int kk) {
+  __device__ __forceinline__ void copy(int x) {
     using M = sk::Map<false>;
-    if (kk % 4 == 0 && kk / 4 < 8) {
-      const int x = kk / 4;
+    if (x < 8) {
       lds_dma16(row, static_cast<uint32_t>(16 * lane), LDS_OFF(g_lds) + M::lat(DMA_BUF) + sk::LROW * (8 * w + x));
       row = sa::latent_row_next(row, stride, lim, x);
+    } else {
+      lds_dma16(rope_base, rope_voff, LDS_OFF(g_lds) + M::rope(DMA_BUF) + 1024 * w);
     }
-    if (kk == 32) lds_dma16(rope_base, rope_voff, LDS_OFF(g_lds) + M::rope(DMA_BUF) + 1024 * w);
+  }
+  __device__ __forceinline__ void score_step(int kk) {
+    if (kBf16CopiesUnderValues) return;
+    if (kk % 4 == 0 && kk / 4 < 8) copy(kk / 4);
+    if (kk == 32) copy(8);
   }
   // after value product m (0 .. 31)
   __device__ __forceinline__ void value_step(int m) {
     if (m == 0) {
-      wait_vm<9>();
+      if (kBf16CopiesUnderValues) wait_vm<0>();
+      else wait_vm<9>();
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (kBf16CopiesUnderValues && m % 3 == 1 && m / 3 < 9) copy(m / 3);
     if (m % 3 == 2 && (m - 2) / 3 < 9) {
       const int x = (m - 2) / 3;
       widen_bf16_store<WIDEN_BUF>(tid, x, v[x & 1]);
