@@ -111,7 +111,7 @@ def run_workload(m, torch, name, steps, warmup, q_len=1, repeats=10):
     lat, rope = DT[case.latent_dtype], DT[case.rope_dtype]
     caches = [m.cache(rows[j], case.row_stride, lat, rope, t["seq_start"], t["seq_cap"], t["seq_len"],
                       None if scale is None else scale[j]) for j in range(ncopy)]
-    plan = m.mla_plan_create(d, lens.tolist(), 0)
+    plan = m.mla_plan_create(d, lens.tolist(), 0) if q_len == 1 else m.mla_plan_create_multi(d, lens.tolist(), q_len)
     nbytes = m.mla_decode_workspace_bytes(d, plan)
     if q_len > 1:
         qn, qr = mla_synth.multi_queries(case, q_len, seed=17)

@@ -11,7 +11,7 @@ import os
 
 __all__ = [
     "F32", "BF16", "FP8_E4M3", "MLAError", "MlaDims", "MlaCache", "Plan", "load", "lib_path",
-    "dims", "cache", "mla_plan_create", "mla_append_workspace_bytes",
+    "dims", "cache", "mla_plan_create", "mla_plan_create_multi", "mla_append_workspace_bytes",
     "mla_decode_workspace_bytes", "mla_workspace_bytes", "mla_append", "mla_decode", "mla_append_decode",
     "mla_decode_multi", "mla_decode_multi_workspace_bytes", "mla_decode_noalloc",
     "mla_merge_query_weight", "mla_merge_output_weight", "mla_decode_merged", "mla_decode_merged_workspace_bytes",
@@ -26,7 +26,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "M
 
 # Every extern "C" entry point of include/mla.h.
 EXPORTED = [
-    "mla_append_workspace_bytes", "mla_append", "mla_plan_create", "mla_plan_destroy",
+    "mla_append_workspace_bytes", "mla_append", "mla_plan_create", "mla_plan_create_multi", "mla_plan_destroy",
     "mla_plan_num_items", "mla_plan_item", "mla_plan_num_ranges", "mla_plan_range", "mla_decode_workspace_bytes", "mla_workspace_bytes", "mla_decode",
     "mla_decode_multi_workspace_bytes", "mla_decode_multi", "mla_decode_noalloc", "mla_append_decode",
     "mla_workspace_init", "mla_device_error", "mla_status_str",
@@ -79,6 +79,7 @@ def load():
         "mla_append": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_int, _P,
                                       ctypes.c_size_t, _P]),
         "mla_plan_create": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, _P]),
+        "mla_plan_create_multi": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]),
         "mla_plan_destroy": (None, [_P]),
         "mla_plan_num_items": (ctypes.c_int32, [_P]),
         "mla_plan_item": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, _P]),
@@ -207,6 +208,15 @@ def mla_plan_create(d, host_lens, n_workers=0):
     h = ctypes.c_void_p()
     _check(load().mla_plan_create(ctypes.byref(d), arr, len(lens), n_workers, ctypes.byref(h)),
            "mla_plan_create")
+    return Plan(h, len(lens))
+
+
+def mla_plan_create_multi(d, host_lens, q_len, n_workers=0):
+    lens = [int(x) for x in host_lens]
+    arr = (ctypes.c_int32 * len(lens))(*lens)
+    h = ctypes.c_void_p()
+    _check(load().mla_plan_create_multi(ctypes.byref(d), arr, len(lens), q_len, n_workers, ctypes.byref(h)),
+           "mla_plan_create_multi")
     return Plan(h, len(lens))
 
 

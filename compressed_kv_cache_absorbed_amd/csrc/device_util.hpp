@@ -158,7 +158,12 @@ __device__ __forceinline__ void plan_verify(const PlanRef &p) {
     const u32x4_ v = dev[x];
     h += plan_chunk_hash(static_cast<uint32_t>(x), v[0], v[1], v[2], v[3]);
   }
-  atomicAdd(&sum, static_cast<unsigned long long>(h));
+  // the wave's sum first (one LDS atomic per wave, not per thread)
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(h), off), hi = __shfl_xor(static_cast<uint32_t>(h >> 32), off);
+    h += (static_cast<uint64_t>(hi) << 32) | lo;
+  }
+  if ((threadIdx.x & 63) == 0) atomicAdd(&sum, static_cast<unsigned long long>(h));
   __syncthreads();
   if (sum != p.hash) {
     const u32x4_ *host = static_cast<const u32x4_ *>(p.host);

@@ -131,6 +131,10 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
     const int q = tid + 256 * x, n = q >> 4, ch = q & 15;
     wv[x] = *reinterpret_cast<const u32x4 *>(W + n * DC + 8 * ch);
   }
+  // the plan copy the split-K and combine kernels read, checked while this
+  // workgroup's loads are in flight (after its own work it lengthened the
+  // launch by its full latency)
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) plan_verify(plan);
 
   // RoPE of pair rp of sequence rb, while the weights land
   if (rb < B) {
@@ -187,8 +191,6 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
     }
     if (!(amax < kF16Max)) set_status(status, MLA_ERR_RANGE);
   }
-  // the plan copy the split-K and combine kernels read
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) plan_verify(plan);
 }
 
 // ---------------------------------------------------------------- combine
@@ -198,8 +200,8 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
 // (G = ceil(B / NB) groups of NB sequences), 512 threads (8 waves).
 // Workgroup L runs on XCD L % 8 and all groups of one head get the same
 // L % 8, so W_UV,i is fetched from HBM once and from that XCD's L2 by the
-// other groups. Every byte a workgroup reads arrives in whole rows: 1 KB
-// per load instruction.
+// other groups. The partial rows arrive whole (1 KB per load
+// instruction), the W_UV rows as 64-byte pieces of 16 rows.
 //   1. For each sequence b of the group: M_b = max_s lse_s and
 //      den_b = sum_s 2^(lse_s - M_b), by an online max-and-sum of its
 //      TPB = 512 / NB threads over splits p, p + TPB, .., combined by
@@ -216,8 +218,8 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
 //      v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16, k = 8(l/16) ..
 //      +7; B: column l%16, same k; D: lane l, register r holds row
 //      4(l/16) + r, column l%16). Wave w owns values 16 w .. 16 w + 15; it
-//      loads their rows whole at the start and turns them into the A
-//      layout through LDS (half of k at a time) once the merge is done.
+//      loads their rows straight into the A layout at the start (staging
+//      them through LDS instead took 3.6 us of a 12 us workgroup).
 // A sequence with no splits, or whose length no longer matches the plan,
 // gets o = 0.
 __device__ __forceinline__ void lse_combine(float &m, float &d, float m2, float d2) {
@@ -278,9 +280,7 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
   constexpr int NL = CPT / 8;                      // 16-byte loads per split
   constexpr int SB = NL == 1 ? 16 : 12;            // splits per batch (rows in flight per thread)
   constexpr int OROW = 1040;                       // LDS bytes per o^ row (conflict-free B reads)
-  constexpr int WROW = 528;                        // LDS bytes per staged W half-row
   __shared__ __attribute__((aligned(16))) char so[2 * 16 * OROW];
-  __shared__ __attribute__((aligned(16))) char sw[NW * 16 * WROW];
   __shared__ float red_m[NW], red_d[NW];
   __shared__ __attribute__((aligned(16))) float red_acc[R > 1 ? NW : 1][DC];
   // workgroup L: head i (on XCD L % 8, with every group of that head),
@@ -321,12 +321,15 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
   RowBatch<NL, SB, R> rb;
   if (r < S) rb.issue(r, S, src, stride, lcol, H);
 
-  // rows vrow .. vrow + 15 of W_UV,i, whole: lane l holds columns 8 l .. 8 l + 7
-  u32x4 wr[16];
+  // rows vrow .. vrow + 15 of W_UV,i straight into the A layout of the
+  // products: k-step kk, lane l takes row l % 16, columns 32 kk + 8 (l / 16)
+  // .. +7 (each load reads 64 contiguous bytes of 16 rows; two consecutive
+  // k-steps cover a 128-byte line)
+  bf16x8 wa[DC / 32];
   if (wact) {
-    const uint16_t *wrow = w_uv + (static_cast<size_t>(i % Hr) * DV + vrow) * DC + 8 * lane;
+    const uint16_t *wrow = w_uv + (static_cast<size_t>(i % Hr) * DV + vrow + (lane & 15)) * DC + 8 * (lane >> 4);
 #pragma unroll
-    for (int x = 0; x < 16; ++x) wr[x] = *reinterpret_cast<const u32x4 *>(wrow + x * DC);
+    for (int kk = 0; kk < DC / 32; ++kk) wa[kk] = *reinterpret_cast<const bf16x8 *>(wrow + 32 * kk);
   }
 
   // 1. M_b and den_b
@@ -367,27 +370,6 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
     for (int s0 = r + R * SB; s0 < S; s0 += R * SB) {
       rb.issue(s0, S, src, stride, lcol, H);
       rb.consume(acc, s0, S, M, inv);
-    }
-  }
-
-  // W_UV rows into the A layout: k-half h, k-step kk = 8 h + t: lane l
-  // takes row l%16, columns 256 h + 32 t + 8(l/16) .. +7
-  bf16x8 wa[DC / 32];
-  if (wact) {
-    char *sww = sw + w * 16 * WROW;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // lanes exchange data through LDS: wave-scope fences keep the compiler
-      // from reusing the first pass's loads or moving the stores across them
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      if ((lane >> 5) == h) {
-#pragma unroll
-        for (int x = 0; x < 16; ++x) *reinterpret_cast<u32x4 *>(sww + x * WROW + 16 * (lane & 31)) = wr[x];
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        wa[8 * h + t] = *reinterpret_cast<const bf16x8 *>(sww + (lane & 15) * WROW + 64 * t + 16 * (lane >> 4));
     }
   }
 

@@ -260,9 +260,18 @@ const char *mla_status_str(mla_status s) {
 // ------------------------------------------------------------------ plan
 mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32_t batch,
                            int32_t n_workers, mla_plan **out) {
+  return mla_plan_create_multi(dims, host_lens, batch, 1, n_workers, out);
+}
+
+mla_status mla_plan_create_multi(const mla_dims *dims, const int32_t *host_lens, int32_t batch, int32_t q_len,
+                                 int32_t n_workers, mla_plan **out) {
   if (!out) return MLA_ERR_INVALID_ARG;
   *out = nullptr;
   if (!dims || !host_lens || batch < 1 || n_workers < 0) return MLA_ERR_INVALID_ARG;
+  if (q_len < 1 || q_len > kMaxQueryTokens || dims->n_heads < 1) return MLA_ERR_INVALID_ARG;
+  // each range runs as one workgroup per 128 of the q_len * H (token, head)
+  // pairs (the matrix-core kernels' head blocks)
+  const int32_t blocks = static_cast<int32_t>((static_cast<int64_t>(q_len) * dims->n_heads + 127) / 128);
   int64_t total = 0, maxlen = 0;
   int32_t nonempty = 0;
   for (int32_t b = 0; b < batch; ++b) {
@@ -281,6 +290,7 @@ mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32
     n_workers = cus;
   }
   (void)maxlen;
+  n_workers = std::max(1, n_workers / blocks);
 
   // The smallest range cost whose cut needs at most n_workers ranges (the
   // cut is monotone in the cost: a larger one never needs more ranges).

@@ -178,6 +178,20 @@ mla_status mla_append(const mla_dims *dims, const mla_cache *cache, const void *
  * MLA_ERR_INVALID_ARG for batch < 1, a negative length or a null pointer. */
 mla_status mla_plan_create(const mla_dims *dims, const int32_t *host_lens, int32_t batch,
                            int32_t n_workers, mla_plan **out);
+/* mla_plan_create_multi — the same for mla_decode_multi with q_len new
+ * query tokens per sequence ("Multi-head Latent Attention (MLA) și
+ * arhitectura DeepSeekMoE", "Concepte cheie și caracteristici": several
+ * tokens per step for speculative decoding). Each range then runs as
+ * ceil(q_len * n_heads / 128) workgroups, one per head block of the
+ * (token, head) pairs, so the ranges are cut for n_workers divided by that
+ * count (at least one): every compute unit still gets one workgroup, and an
+ * item's fixed cost is paid once per compute unit rather than once per head
+ * block. n_workers 0 means the compute units of the current HIP device.
+ * mla_plan_create(...) is mla_plan_create_multi(..., q_len = 1, ...); a plan
+ * from either serves every decode call with the same lengths.
+ * MLA_ERR_INVALID_ARG as mla_plan_create, and for q_len outside 1..16. */
+mla_status mla_plan_create_multi(const mla_dims *dims, const int32_t *host_lens, int32_t batch, int32_t q_len,
+                                 int32_t n_workers, mla_plan **out);
 void mla_plan_destroy(mla_plan *plan);
 /* Plan inspection (host): number of work items, and item k's
  * (sequence, first token, end token); number of workgroup ranges, and range

@@ -79,7 +79,9 @@ def test_multi_ragged_batch_sampled(gpu):
     q_len = 4
     qn, qr = mla_synth.multi_queries(case, q_len, seed=5)
     run = DeviceRun(gpu, case)
-    o = to_np(run.decode_multi(q_len, qn, qr))
+    # the plan the benchmark uses: ranges cut for four head blocks each
+    plan = run.m.mla_plan_create_multi(run.d, (case.lens + case.n_new).tolist(), q_len)
+    o = to_np(run.decode_multi(q_len, qn, qr, plan=plan))
     assert run.status() == 0
     rng = np.random.default_rng(7)
     tri = [(int(rng.integers(32)), int(rng.integers(q_len)), int(rng.integers(128))) for _ in range(12)]
@@ -89,3 +91,21 @@ def test_multi_ragged_batch_sampled(gpu):
     ref = oracle_decode_multi(case, qn, qr, triples=tri, C=C, R=R)
     got = np.stack([o[b, j, i] for b, j, i in tri])
     assert rel_rms_err(got, ref) <= TOL_BF16_REL
+
+
+@pytest.mark.parametrize("latent,q_len,workers", [("bf16", 4, 24), ("fp8", 3, 24), ("bf16", 2, 0), ("bf16", 16, 40)])
+def test_multi_plan_for_tokens(gpu, latent, q_len, workers):
+    """A plan from mla_plan_create_multi (ranges cut for the head blocks of
+    q_len tokens: fewer, longer ranges) against the oracle, over the edge
+    lengths."""
+    lens = [1, 2, 3, 31, 33, 100, 700, 0, 64, 15]
+    case = v3_case(lens, latent, seed=83)
+    qn, qr = mla_synth.multi_queries(case, q_len, seed=95 + q_len)
+    run = DeviceRun(gpu, case)
+    plan = run.m.mla_plan_create_multi(run.d, lens, q_len, workers)
+    blocks = (q_len * 128 + 127) // 128
+    assert len(plan.ranges()) <= max(1, (workers or 256) // blocks)
+    o = to_np(run.decode_multi(q_len, qn, qr, plan=plan))
+    assert run.status() == 0
+    tol = TOL_FP8_REL if latent == "fp8" else TOL_BF16_REL
+    assert rel_rms_err(o, oracle_decode_multi(case, qn, qr)) <= tol

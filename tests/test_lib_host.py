@@ -124,6 +124,30 @@ def test_plan_lognormal_lengths_beat_per_sequence_chunks():
     assert max(rt) <= 1.02 * share + 2
 
 
+@pytest.mark.parametrize("q_len,workers", [(1, 256), (2, 256), (4, 256), (16, 256), (3, 7), (4, 2)])
+def test_plan_multi_ranges_per_head_blocks(q_len, workers):
+    """mla_plan_create_multi cuts at most n_workers / ceil(q_len H / 128)
+    ranges (at least one), covering every token once, balanced like a
+    one-token plan of that many workers; q_len 1 is mla_plan_create."""
+    lens = np.random.default_rng(q_len).integers(1, 9000, 40).tolist()
+    p = m.mla_plan_create_multi(d128(), lens, q_len, workers)
+    blocks = q_len  # H = 128: one head block per token
+    W = max(1, workers // blocks)
+    assert len(p.ranges()) <= W
+    assert sorted((b, t0, t1) for b, t0, t1 in p.items()) == sorted(m.mla_plan_create(d128(), lens, W).items())
+    if q_len == 1:
+        assert p.items() == m.mla_plan_create(d128(), lens, workers).items()
+
+
+def test_plan_multi_rejects_bad_q_len():
+    h = ctypes.c_void_p()
+    lib = m.load()
+    d = d128()
+    good = (ctypes.c_int32 * 2)(10, 20)
+    for q in (0, 17, -1):
+        assert lib.mla_plan_create_multi(ctypes.byref(d), good, 2, q, 4, ctypes.byref(h)) == 1
+
+
 def test_plan_inspection_rejects_bad_index():
     p = m.mla_plan_create(d128(), [100, 5000], 8)
     lib = m.load()
