@@ -60,8 +60,11 @@ def parse():
 
 
 def kernel_source_hash():
+    """Hash of the sources that decide the split-K kernels' traffic: the
+    kernels, their headers and the planner (which items they run)."""
     h = hashlib.sha256()
-    for f in ("k_splitk.hip", "device_util.hpp", "mla_internal.hpp", "splitk_addr.hpp", "plan_hash.hpp"):
+    for f in ("k_splitk.hip", "k_splitk8.hip", "splitk_common.hpp", "device_util.hpp", "mla_internal.hpp",
+              "splitk_addr.hpp", "plan_hash.hpp", "mla_api.cpp"):
         with open(os.path.join(ROOT, "compressed_kv_cache_absorbed_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -67,6 +67,29 @@ def test_fast_matches_generic_path(gpu, latent, monkeypatch):
     assert rel_rms_err(fast, gen) <= tol
 
 
+@pytest.mark.parametrize("workers", [16, 5])
+def test_fp8_matrix_cores_and_widening_kernel(gpu, monkeypatch, workers):
+    """An fp8 cache runs on the fp8 matrix cores by default (e4m3 codes
+    straight from the tile, q~ and P as hi + lo e4m3 pairs); MLA_FP8_WIDEN=1
+    selects the kernel that widens the codes to fp16 first. Both against the
+    oracle over the edge lengths (with ranges of several items at 5
+    workers), and against each other, within the bf16 tolerance: the fp8
+    products' own error is far inside the fp8 one (the emulation of exactly
+    this arithmetic gives 3.2e-3), and the widened codes are exact in fp16."""
+    case = v3_case(EDGE_LENS, "fp8", seed=57, gap_rows=2)
+    run = DeviceRun(gpu, case)
+    o8 = to_np(run.decode(n_workers=workers))
+    monkeypatch.setenv("MLA_FP8_WIDEN", "1")
+    o16 = to_np(run.decode(n_workers=workers))
+    monkeypatch.delenv("MLA_FP8_WIDEN")
+    assert run.status() == 0
+    ref = oracle_decode(case, absorbed=True)
+    e8, e16, e816 = rel_rms_err(o8, ref), rel_rms_err(o16, ref), rel_rms_err(o8, o16)
+    print(f"fp8 matrix cores {e8:.2e}, widening kernel {e16:.2e}, between them {e816:.2e}")
+    assert max(e8, e16, e816) <= TOL_BF16_REL
+    assert np.all(o8[EDGE_LENS.index(0)] == 0) and np.all(o16[EDGE_LENS.index(0)] == 0)
+
+
 @pytest.mark.parametrize("latent", ["bf16", "fp8"])
 def test_fast_256_heads(gpu, latent):
     """Two 128-head blocks per work item (split-K grid of two rows of
