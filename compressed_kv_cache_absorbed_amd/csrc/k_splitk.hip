@@ -793,8 +793,6 @@ __device__ __forceinline__ void splitk_item(const mla_cache &c, int H, int Hr, i
     dma_raw<1>(it, 1, w, lane);
   } else {
     dma_bf16<0>(it, 0, w, lane);
-    dma_bf16<1>(it, 1, w, lane);
-    dma_bf16<2>(it, 2, w, lane);
   }
 
   WaveState st;
@@ -805,6 +803,13 @@ __device__ __forceinline__ void splitk_item(const mla_cache &c, int H, int Hr, i
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) st.qf[kk] = *reinterpret_cast<const f16x8 *>(qrow + 16 * kk);
   }
+  // bf16: tiles 1 and 2 after Q, so that the first scores wait for tile 0
+  // and Q only (with every workgroup loading at once, each kilobyte waited
+  // for delays the first product)
+  if (!FP8) {
+    dma_bf16<1>(it, 1, w, lane);
+    dma_bf16<2>(it, 2, w, lane);
+  }
 #pragma unroll
   for (int db = 0; db < DC / 32; ++db) {
     st.O[db] = f32x16{};
@@ -814,9 +819,10 @@ __device__ __forceinline__ void splitk_item(const mla_cache &c, int H, int Hr, i
   st.m = -INFINITY;
   st.l = 0.0f;
 
-  // this wave's rows of tiles 0 and 1 landed and widened (fp8: then raw
-  // buffer 0 takes tile 2, only this wave's rows, which only it read); then
-  // the scores of tile 0 alone
+  // fp8: this wave's rows of tiles 0 and 1 landed and widened, then raw
+  // buffer 0 takes tile 2 (only this wave's rows, which only it read); bf16:
+  // tile 0 widened. Then the scores of tile 0 alone (bf16: and tile 1
+  // widened after them)
   if (FP8) {
     wait_vm<0>();
     __builtin_amdgcn_sched_barrier(0);
@@ -825,10 +831,9 @@ __device__ __forceinline__ void splitk_item(const mla_cache &c, int H, int Hr, i
     wait_lds();
     dma_raw<0>(it, 2, w, lane);
   } else {
-    wait_vm<9>();  // only Q's loads, issued last, may still fly
+    wait_vm<18>();  // tile 0 and Q landed; tiles 1 and 2 may still fly
     __builtin_amdgcn_sched_barrier(0);
     widen_bf16_inplace<0>(tid);
-    widen_bf16_inplace<1>(tid);
     wait_lds();
   }
   __builtin_amdgcn_s_barrier();
@@ -837,6 +842,15 @@ __device__ __forceinline__ void splitk_item(const mla_cache &c, int H, int Hr, i
     NoHide nh;
     Softmax sm;
     score_chain<FP8, 0, false>(st, S, S, sm, nh);
+  }
+  if (!FP8) {
+    // tile 1 (this wave's rows) landed while tile 0 was scored
+    wait_vm<9>();
+    __builtin_amdgcn_sched_barrier(0);
+    widen_bf16_inplace<1>(tid);
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (FP8) {
     for (int i = 0; i < it.ntiles; i += 6) {
