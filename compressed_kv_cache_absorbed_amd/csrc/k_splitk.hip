@@ -757,9 +757,8 @@ __device__ __forceinline__ void splitk_item(const mla_cache &c, int H, int Hr, i
   uint16_t *ob = opart + (static_cast<size_t>(k) * H + y * 128) * DC;
 
   // (the item must name a sequence of the batch before anything is indexed by it)
-  const bool ok = wi.b >= 0 && wi.b < c.batch && c.seq_len[wi.b] == seqs[wi.b].len && wi.t0 >= 0 && wi.t0 < wi.t1 &&
-                  seq_range_ok(c, wi.b, wi.t1);
-  if (!ok) {
+  const ItemSeq sq = item_seq(c, seqs, wi);
+  if (!sq.ok) {
     if (tid == 0 && y == 0) set_status(status, MLA_ERR_PLAN);
     for (int x = tid; x < 128 * DC / 8; x += 256) reinterpret_cast<u32x4 *>(ob)[x] = u32x4{0, 0, 0, 0};
     if (half == 0) lse[static_cast<size_t>(k) * H + head] = -INFINITY;
@@ -769,7 +768,7 @@ __device__ __forceinline__ void splitk_item(const mla_cache &c, int H, int Hr, i
   it.rows = static_cast<const char *>(c.rows);
   it.scale = c.scale;
   it.stride = c.row_stride;
-  it.row0 = c.block_table == nullptr ? c.seq_start[wi.b] : 0;
+  it.row0 = sq.row0;
   it.blocks = c.block_table == nullptr ? nullptr : c.block_table + static_cast<int64_t>(wi.b) * c.max_blocks;
   it.block_tokens = c.block_tokens;
   it.n_blocks = c.block_table == nullptr ? 0 : static_cast<int>(c.n_rows / c.block_tokens);
@@ -784,7 +783,7 @@ __device__ __forceinline__ void splitk_item(const mla_cache &c, int H, int Hr, i
   it.t0 = wi.t0;
   it.t1 = wi.t1;
   it.ntiles = (wi.t1 - wi.t0 + T - 1) / T;
-  it.tvis = min(wi.t1, seqs[wi.b].len - (q_len - 1 - jq));
+  it.tvis = min(wi.t1, sq.len - (q_len - 1 - jq));
 
   // prologue copies first, so they overlap the Q fetch (tiles past the end
   // re-read the item's last tile, like the steps)

@@ -103,6 +103,40 @@ __device__ __forceinline__ mla_cache cache_of(KernArgs a) {
   return c;
 }
 
+// An item's sequence checked and its data read, every load issued at once:
+// the sequence index is checked first (nothing is indexed by an index
+// outside the batch), then the device length, the plan's length, the
+// reserved tokens and the start row are read together and the checks are
+// combined without short-circuit evaluation, which would chain the loads one
+// memory round trip after another (eight of them stood before an item's
+// first copy). ok: the item's tokens lie in its sequence's range, the
+// device length equals the plan's, and the item is non-empty.
+struct ItemSeq {
+  bool ok;
+  int len;       // the plan's length of the sequence
+  int64_t row0;  // the sequence's first row (contiguous cache), else 0
+};
+__device__ __forceinline__ ItemSeq item_seq(const mla_cache &c, const SeqInfo *seqs, const WorkItem &wi) {
+  const bool b_ok = (wi.b >= 0) & (wi.b < c.batch);
+  const int b = b_ok ? wi.b : 0;
+  const bool paged = c.block_table != nullptr;
+  const int dev_len = c.seq_len[b];
+  const int plan_len = seqs[b].len;
+  const int64_t cap = c.seq_cap[b];
+  // (a pointer chosen without a branch, so this load issues with the others:
+  // a paged cache may have no seq_start, and reads seq_len there instead)
+  const int32_t *sp = paged ? c.seq_len : c.seq_start;
+  const int64_t start = paged ? 0 : static_cast<int64_t>(sp[b]);
+  const int64_t t1 = wi.t1;
+  const bool in_rows = paged ? t1 <= static_cast<int64_t>(c.max_blocks) * c.block_tokens
+                             : (start >= 0) & (start + t1 <= c.n_rows);
+  ItemSeq r;
+  r.ok = b_ok & (dev_len == plan_len) & (wi.t0 >= 0) & (wi.t0 < wi.t1) & (t1 <= cap) & in_rows;
+  r.len = plan_len;
+  r.row0 = start;
+  return r;
+}
+
 // Workgroup L of a split-K launch over R ranges and Y head blocks of 128:
 // range j, head block y. Workgroup L runs on XCD L % 8, so each XCD takes a
 // contiguous block of ranges: a sequence's items are consecutive, and the
