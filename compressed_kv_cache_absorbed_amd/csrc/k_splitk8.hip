@@ -168,6 +168,19 @@ __device__ __forceinline__ void dma8_piece(const RawSrc &rs, int w, int lane, in
     lds_dma4(rs.sbase, sa::raw_scale_off(rs, ln), __builtin_amdgcn_readfirstlane(lds0 + s8::scl(R, 0) + 256u * w));
   }
 }
+// The same copy with the per-lane constants of the item (sa::RawLane),
+// offset from the tile's first row tbase: the form the steps issue.
+template <int R>
+__device__ __forceinline__ void dma8_piece_lane(const RawSrc &rs, const char *tbase, const sa::RawLane &rl, int w,
+                                                int lane, int x) {
+  if (x < sa::RAW_DMA_PER_WAVE) {
+    const int q = sa::RAW_DMA_PER_WAVE * w + x;
+    lds_dma16(tbase, sa::raw_piece_off_lane(rl, x, rs.tmax, rs.stride),
+              __builtin_amdgcn_readfirstlane(LDS_OFF(g_lds8) + s8::raw(R) + 1024u * q));
+  } else {
+    dma8_piece<R>(rs, w, lane, x);
+  }
+}
 template <int R>
 __device__ __forceinline__ void dma8(const Item &it, int tile, int w, int lane) {
   const RawSrc rs = raw_src(tile_src(it, tile), w);
@@ -181,6 +194,7 @@ __device__ __forceinline__ void dma8(const Item &it, int tile, int w, int lane) 
 // accumulator O^T [512 x 32 heads] as 16 column blocks, and the running max
 // and denominator of the lane's head.
 struct State8 {
+  sa::RawLane rl;  // this lane's copy constants for the item's row stride
   i32x8 qh[8], ql[8];
   f16x8 qr[4];
   int sq_hi, sq_lo;
@@ -285,12 +299,15 @@ constexpr bool kCopiesUnderValues = true;
 template <int DMA_RAW>
 struct Hide8 {
   RawSrc rs;
+  const char *tbase;  // the tile's first row
+  const sa::RawLane *rl;
   int w, lane;
   __device__ __forceinline__ void step(int n) {
-    if (!kCopiesUnderValues && n <= sa::RAW_DMA_PER_WAVE) dma8_piece<DMA_RAW>(rs, w, lane, n);
+    if (!kCopiesUnderValues && n <= sa::RAW_DMA_PER_WAVE) dma8_piece_lane<DMA_RAW>(rs, tbase, *rl, w, lane, n);
   }
   __device__ __forceinline__ void value_step(int cb) {
-    if (kCopiesUnderValues && cb >= 1 && cb - 1 <= sa::RAW_DMA_PER_WAVE) dma8_piece<DMA_RAW>(rs, w, lane, cb - 1);
+    if (kCopiesUnderValues && cb >= 1 && cb - 1 <= sa::RAW_DMA_PER_WAVE)
+      dma8_piece_lane<DMA_RAW>(rs, tbase, *rl, w, lane, cb - 1);
   }
 };
 template <int B, bool SOFTMAX, class Hide>
@@ -444,7 +461,12 @@ template <int I>
 __device__ __forceinline__ void step8(State8 &st, f32x16 &S, const Item &it, int i, int w, int lane) {
   using namespace s8;
   Hide8<(I + 3) % NBUF> hd;
-  hd.rs = raw_src(tile_src(it, i + 3), w);
+  {
+    const sa::TileSrc src = tile_src(it, i + 3);
+    hd.rs = raw_src(src, w);
+    hd.tbase = src.base;
+  }
+  hd.rl = &st.rl;
   hd.w = w;
   hd.lane = lane;
   // (the last score product is asm: cover its result latency before the
@@ -537,6 +559,7 @@ __device__ __forceinline__ void splitk8_item(const mla_cache &c, int H, int Hr, 
   State8 st;
   st.w = w;
   st.lane = lane;
+  st.rl = sa::raw_lane(w, opaque(lane), it.stride);
   {
     const uint16_t *qrow = Q + (static_cast<size_t>(wi.b) * H + head) * D;
     float amax = 0.0f;

@@ -150,6 +150,33 @@ __host__ __device__ inline uint32_t raw_piece_off_sw(const RawSrc &rs, int w, in
   return static_cast<uint32_t>(imin(t, rs.tmax) - rs.t0) * static_cast<uint32_t>(rs.stride) +
          static_cast<uint32_t>(16 * ch);
 }
+// The same copies with their per-lane constants made once per item: copy x
+// of wave w, lane ln fills slot P = 64 (5 w + x) + ln, which holds token
+// t[x] = P / 40 and, when no token is clamped, reads t[x] stride + 16 chunk
+// bytes past the tile's first row (off[x]). A tile whose last valid token
+// is tmax < t[x] reads row tmax instead: off[x] - (t[x] - tmax) stride. The
+// result equals rs.base + raw_piece_off_sw(rs, w, ln, x) as an address
+// (tests/c/splitk_addr_check.cpp checks every case); three instructions per
+// copy instead of the division and the multiplies.
+struct RawLane {
+  int t[RAW_DMA_PER_WAVE];
+  uint32_t off[RAW_DMA_PER_WAVE];
+};
+__host__ __device__ inline RawLane raw_lane(int w, int ln, int64_t stride) {
+  RawLane r;
+  for (int x = 0; x < RAW_DMA_PER_WAVE; ++x) {
+    const int P = 64 * (RAW_DMA_PER_WAVE * w + x) + ln;
+    const int t = P / 40;
+    r.t[x] = t;
+    r.off[x] = static_cast<uint32_t>(t) * static_cast<uint32_t>(stride) + static_cast<uint32_t>(16 * ((P - 40 * t) ^ rsw8(t)));
+  }
+  return r;
+}
+// Offset of copy x from the tile's first row (TileSrc::base).
+__host__ __device__ inline uint32_t raw_piece_off_lane(const RawLane &rl, int x, int tmax, int64_t stride) {
+  const int d = rl.t[x] - tmax;
+  return rl.off[x] - static_cast<uint32_t>(d > 0 ? d : 0) * static_cast<uint32_t>(stride);
+}
 // The scale copy: lane ln reads the scale of token ln % 32 (clamped), as an
 // offset from rs.sbase.
 __host__ __device__ inline uint32_t raw_scale_off(const RawSrc &rs, int ln) {

@@ -147,6 +147,11 @@ void check_tile(const Layout &L, int cap, int t0, int n, int tile, bool fp8) {
                  &tok, &byte);
           if (tok != ts + imin(P / 40, src.tmax) || byte != 16 * ((P % 40) ^ rsw8(P / 40)) || byte + 16 > 640)
             fail("permuted raw piece of the wrong token or chunk", n, t0, tile, w, lane, x);
+          // the same address from the per-lane constants, offset from the
+          // tile's first row
+          const RawLane rl = raw_lane(w, lane, src.stride);
+          if (src.base + raw_piece_off_lane(rl, x, src.tmax, src.stride) != rs.base + raw_piece_off_sw(rs, w, lane, x))
+            fail("per-lane raw piece address", n, t0, tile, w, lane, x);
         }
       }
       // the multiply that stands for the division by 40 is exact on every slot
