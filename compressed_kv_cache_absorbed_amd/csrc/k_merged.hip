@@ -41,7 +41,7 @@ namespace {
 __global__ __launch_bounds__(256) void merge_gemm_kernel(int M, int N, int K, const void *P, int64_t sPt, int64_t sPk,
                                                          int64_t sPm, const void *Q, int64_t sQt, int64_t sQk,
                                                          int64_t sQn, mla_dtype in, void *C, int64_t sCt,
-                                                         int64_t sCm, int64_t sCn, mla_dtype out) {
+                                                         int64_t sCm, int64_t sCn, mla_dtype out, int64_t tileK) {
   __shared__ float ps[16][65], qs[16][65];
   const int t = blockIdx.z, m0 = 64 * blockIdx.y, n0 = 64 * blockIdx.x;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
@@ -70,7 +70,8 @@ __global__ __launch_bounds__(256) void merge_gemm_kernel(int M, int N, int K, co
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + 4 * tx + j;
       if (n >= N) continue;
-      const int64_t off = t * sCt + m * sCm + n * sCn;
+      int64_t off = t * sCt + m * sCm + n * sCn;
+      if (tileK > 0) off = merged::weight_off(off / tileK, off % tileK, tileK, true);
       if (out == MLA_BF16)
         static_cast<uint16_t *>(C)[off] = f32_to_bf16_bits(acc[i][j]);
       else
@@ -137,9 +138,12 @@ __global__ __launch_bounds__(256) void wstream_kernel(int R, int K, int B, int k
   const bool bval = bcol < B;
   const int kw = kchunk / 4, kbeg = ks * kchunk + w * kw;
 
+  // the weight is fragment-tiled (merged::weight_off): row block r, step s
+  // is 2048 contiguous elements, product f of it 512, this lane's 8 at 8 lane
   const uint16_t *wp[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) wp[r] = W + static_cast<size_t>(row0 + 32 * r + (lane & 31)) * K + kbeg + 32 * h;
+  for (int r = 0; r < NR; ++r)
+    wp[r] = W + (static_cast<size_t>(row0 / 32 + r) * (K / 64) + kbeg / 64) * 2048 + 8 * lane;
   // columns past B read column b0's data (in bounds) and are zeroed by a select
   const size_t xrow = static_cast<size_t>(bval ? bcol : b0) * K + kbeg + 32 * h;
   const uint16_t *xh = Xhi + xrow;
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(256) void wstream_kernel(int R, int K, int B, int k
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
-      for (int f = 0; f < 4; ++f) a[r][f] = *reinterpret_cast<const u32x4 *>(wp[r] + 64 * s + 8 * f);
+      for (int f = 0; f < 4; ++f) a[r][f] = *reinterpret_cast<const u32x4 *>(wp[r] + 2048 * s + 512 * f);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       xv[f] = *reinterpret_cast<const u32x4 *>(xh + 64 * s + 8 * f);
@@ -298,10 +302,11 @@ __global__ __launch_bounds__(256) void absorb_merged_generic_kernel(mla_dims d, 
   __syncthreads();
   const float qs = d.softmax_scale * kLog2e;
   float *out = q_out + (static_cast<int64_t>(b) * H + i) * D;
+  const bool tl = merged::tiled(static_cast<int64_t>(H) * d.d_c, d_x);
   for (int c = wave; c < d.d_c; c += 4) {
-    const int64_t row = (static_cast<int64_t>(i) * d.d_c + c) * d_x;
+    const int64_t row = static_cast<int64_t>(i) * d.d_c + c;
     float acc = 0.0f;
-    for (int k = lane; k < d_x; k += 64) acc = fmaf(load_elem(a, row + k, wt), xs[k], acc);
+    for (int k = lane; k < d_x; k += 64) acc = fmaf(load_elem(a, merged::weight_off(row, k, d_x, tl), wt), xs[k], acc);
     acc = wave_sum(acc);
     if (lane == 0) out[c] = acc * qs;
   }
@@ -325,8 +330,9 @@ __global__ __launch_bounds__(256) void out_generic_kernel(int d_out, int64_t K, 
   const int b = blockIdx.y, r = 4 * blockIdx.x + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (r >= d_out) return;
   const float *o = ohat + static_cast<int64_t>(b) * K;
+  const bool tl = merged::tiled(d_out, K);
   float acc = 0.0f;
-  for (int64_t k = lane; k < K; k += 64) acc = fmaf(load_elem(bm, r * K + k, wt), o[k], acc);
+  for (int64_t k = lane; k < K; k += 64) acc = fmaf(load_elem(bm, merged::weight_off(r, k, K, tl), wt), o[k], acc);
   acc = wave_sum(acc);
   if (lane == 0) {
     const int64_t off = static_cast<int64_t>(b) * d_out + r;
@@ -343,10 +349,10 @@ __global__ __launch_bounds__(256) void out_generic_kernel(int d_out, int64_t K, 
 
 hipError_t launch_merge_gemm(hipStream_t s, int T, int M, int N, int K, const void *P, int64_t sPt, int64_t sPk,
                              int64_t sPm, const void *Q, int64_t sQt, int64_t sQk, int64_t sQn, mla_dtype in, void *C,
-                             int64_t sCt, int64_t sCm, int64_t sCn, mla_dtype out) {
+                             int64_t sCt, int64_t sCm, int64_t sCn, mla_dtype out, int64_t tileK) {
   if (T == 0 || M == 0 || N == 0) return hipSuccess;
   return launch_kernel(merge_gemm_kernel, dim3((N + 63) / 64, (M + 63) / 64, T), 256, 0, s, M, N, K, P, sPt, sPk, sPm,
-                       Q, sQt, sQk, sQn, in, C, sCt, sCm, sCn, out);
+                       Q, sQt, sQk, sQn, in, C, sCt, sCm, sCn, out, tileK);
 }
 
 hipError_t launch_absorb_merged_fast(hipStream_t s, const mla_dims &d, int32_t batch, int32_t d_x, const void *x,

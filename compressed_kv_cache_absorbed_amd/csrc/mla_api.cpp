@@ -714,11 +714,13 @@ mla_status mla_merge_query_weight(const mla_dims *dims, int32_t d_x, const void 
   if (st != MLA_OK) return st;
   const mla_dims &d = *dims;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // per head: A[c][x] = sum_n W_UK[n][c] W_Q[n][x]
+  // per head: A[c][x] = sum_n W_UK[n][c] W_Q[n][x] (A as a weight of H d_c
+  // rows and d_x columns: fragment-tiled when the shape allows)
   const int64_t dn = d.d_nope, dc = d.d_c, dx = d_x;
+  const int64_t tk = merged::tiled(static_cast<int64_t>(d.n_heads) * dc, dx) ? dx : 0;
   MLA_LAUNCH(s, K_MERGE_GEMM,
              launch_merge_gemm(s, d.n_heads, d.d_c, d_x, d.d_nope, w_uk, dn * dc, dc, 1, w_q, dn * dx, dx, 1, w_dtype,
-                               a, dc * dx, dx, 1, w_dtype));
+                               a, dc * dx, dx, 1, w_dtype, tk));
   return MLA_OK;
 }
 
@@ -729,10 +731,12 @@ mla_status mla_merge_output_weight(const mla_dims *dims, int32_t d_out, const vo
   const mla_dims &d = *dims;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // per head i: Bm[o][i d_c + c] = sum_v W_O[o][i d_v + v] W_UV[i][v][c]
+  // (fragment-tiled when the shape allows)
   const int64_t H = d.n_heads, dv = d.d_v, dc = d.d_c;
+  const int64_t tk = merged::tiled(d_out, H * dc) ? H * dc : 0;
   MLA_LAUNCH(s, K_MERGE_GEMM,
              launch_merge_gemm(s, d.n_heads, d_out, d.d_c, d.d_v, w_o, dv, 1, H * dv, w_uv, dv * dc, dc, 1, w_dtype,
-                               bm, dc, H * dc, 1, w_dtype));
+                               bm, dc, H * dc, 1, w_dtype, tk));
   return MLA_OK;
 }
 

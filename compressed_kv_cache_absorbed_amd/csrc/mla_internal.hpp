@@ -178,10 +178,26 @@ namespace merged {
 constexpr int DC = 512;
 // K splits of the matrix-core output product (each a multiple of 256 wide)
 inline int out_splits(int64_t K) { return K % (16 * 256) == 0 ? 16 : 1; }
+// Layout of a merged weight [R rows x K columns]: when R % 32 == 0 and
+// K % 64 == 0, fragment-tiled, so that every load of the weight-streaming
+// kernel reads 1 KB contiguous: tile (r / 32, k / 64) of 2048 elements at
+// ((r / 32) (K / 64) + k / 64) 2048, and inside it element (r, k) at
+// ((k % 32) / 8) 512 + (r % 32 + 32 ((k % 64) / 32)) 8 + k % 8 (the order
+// in which the lanes of a wave take the A operand of four 32x32x16
+// products). Otherwise row-major, r K + k.
+__host__ __device__ inline bool tiled(int64_t R, int64_t K) { return R % 32 == 0 && K % 64 == 0; }
+__host__ __device__ inline int64_t weight_off(int64_t r, int64_t k, int64_t K, bool tl) {
+  if (!tl) return r * K + k;
+  return ((r >> 5) * (K >> 6) + (k >> 6)) * 2048 + ((k & 31) >> 3) * 512 + ((r & 31) + 32 * ((k & 63) >> 5)) * 8 +
+         (k & 7);
+}
 }  // namespace merged
+// C[t] = P[t]^T Q[t]; element (t, m, n) goes to the row-major offset
+// t sCt + m sCm + n sCn, or, with tileK > 0, to that offset's place in the
+// fragment-tiled layout of a weight whose rows are tileK long.
 hipError_t launch_merge_gemm(hipStream_t s, int T, int M, int N, int K, const void *P, int64_t sPt, int64_t sPk,
                              int64_t sPm, const void *Q, int64_t sQt, int64_t sQk, int64_t sQn, mla_dtype in, void *C,
-                             int64_t sCt, int64_t sCm, int64_t sCn, mla_dtype out);
+                             int64_t sCt, int64_t sCm, int64_t sCn, mla_dtype out, int64_t tileK);
 hipError_t launch_absorb_merged_fast(hipStream_t s, const mla_dims &d, int32_t batch, int32_t d_x, const void *x,
                                      const void *q_rope, const int32_t *q_pos, const void *a,
                                      const int32_t *seq_len, uint16_t *q_out, const PlanRef &plan, int32_t *status);

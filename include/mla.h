@@ -302,9 +302,16 @@ size_t mla_decode_multi_workspace_bytes(const mla_dims *dims, const mla_plan *pl
  * where the model compresses queries); W_O [d_out, n_heads d_v] (the layer
  * output is W_O applied to the heads' outputs concatenated in head order).
  *
- * mla_merge_query_weight — a [n_heads, d_c, d_x] = W_UK,i^T W_Q,i per head.
+ * mla_merge_query_weight — a [n_heads, d_c, d_x] = W_UK,i^T W_Q,i per head,
+ * as a weight of R = n_heads d_c rows and K = d_x columns (row h d_c + c).
  * mla_merge_output_weight — bm [d_out, n_heads d_c], column block i =
- * W_O[:, i d_v .. (i+1) d_v) W_UV,i.
+ * W_O[:, i d_v .. (i+1) d_v) W_UV,i: R = d_out rows, K = n_heads d_c.
+ * Storage of such a weight: when R % 32 == 0 and K % 64 == 0,
+ * fragment-tiled, so that the decode streams it in contiguous 1 KB loads:
+ * element (r, k) at ((r / 32) (K / 64) + k / 64) 2048 + ((k % 32) / 8) 512 +
+ * (r % 32 + 32 ((k % 64) / 32)) 8 + k % 8; otherwise row-major, r K + k.
+ * The buffers are meant for mla_decode_merged with the same dims, d_x and
+ * d_out (which reads them in that storage).
  * One-time weight preparation (fp32 accumulation, stored in w_dtype, F32 or
  * BF16 with round-to-nearest-even); the inputs keep their W_UK and W_UV
  * layouts of mla_decode. All pointers are device memory the caller owns,

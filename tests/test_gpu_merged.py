@@ -1,9 +1,10 @@
 """GPU parity of the decode from precomputed absorbed weights (C ABI through
 the binding) against oracle.merged:
 
-* the one-time merges (W_UK,i^T W_Q,i and W_O,i W_UV,i) element by element:
-  fp32 within 1e-5 of the largest value; bf16 within one bf16 ulp of the
-  exact product (fp32 sums rounded once);
+* the one-time merges (W_UK,i^T W_Q,i and W_O,i W_UV,i) element by element,
+  read through the documented storage (row-major, or fragment-tiled when the
+  shape allows): fp32 within 1e-5 of the largest value; bf16 within one
+  bf16 ulp of the exact product (fp32 sums rounded once);
 * mla_decode_merged end to end (the GPU's own merged weights, the oracle's
   fp64 ones): fp32 kernels within 1e-4 (max |err| / rms), the matrix-core
   path within the bf16 tolerance 2e-2, over ragged lengths with an empty
@@ -75,6 +76,31 @@ class Merged:
                                 c.softmax_scale, c.rope_base)
 
 
+def untile(w, R, K):
+    """A merged weight as the header documents its storage: fragment-tiled
+    when R % 32 == 0 and K % 64 == 0 (element (r, k) at ((r / 32) (K / 64) +
+    k / 64) 2048 + ((k % 32) / 8) 512 + (r % 32 + 32 ((k % 64) / 32)) 8 +
+    k % 8), else row-major; returned as [R, K]."""
+    flat = np.asarray(w).reshape(-1)
+    if R % 32 or K % 64:
+        return flat.reshape(R, K)
+    # [tile row, tile k, f (k % 32 / 8), h (k % 64 / 32), r % 32, k % 8]
+    t = flat.reshape(R // 32, K // 64, 4, 2, 32, 8)
+    return t.transpose(0, 4, 1, 3, 2, 5).reshape(R, K)
+
+
+def test_untile_reads_the_documented_offsets():
+    R, K = 64, 128
+    rng = np.random.default_rng(0)
+    dense = rng.standard_normal((R, K))
+    flat = np.empty(R * K)
+    for r in range(R):
+        for k in range(K):
+            off = ((r // 32) * (K // 64) + k // 64) * 2048 + ((k % 32) // 8) * 512 + (r % 32 + 32 * ((k % 64) // 32)) * 8 + k % 8
+            flat[off] = dense[r, k]
+    assert np.array_equal(untile(flat, R, K), dense)
+
+
 def tiny_f32(seed):
     return make(B=4, H=4, d_c=32, d_rope=8, d_nope=16, d_v=16, lens=("list", [5, 0, 70, 33]), latent_dtype="f32",
                 rope_dtype="f32", act_dtype="f32", seed=seed)
@@ -86,16 +112,23 @@ def v3_case(seed, latent="bf16"):
 
 
 def test_merges_f32_match_oracle(gpu):
+    """Shapes that keep the row-major storage (d_x = 24, d_out = 20)."""
     mg = Merged(gpu, tiny_f32(200), d_x=24, d_out=20, seed=201)
     a, bm = mg.oracle_weights()
-    assert np.max(np.abs(to_np(mg.a) - a)) <= 1e-5 * np.max(np.abs(a))
-    assert np.max(np.abs(to_np(mg.bm) - bm)) <= 1e-5 * np.max(np.abs(bm))
+    c = mg.case
+    assert np.max(np.abs(untile(to_np(mg.a), c.H * c.d_c, 24) - a.reshape(c.H * c.d_c, 24))) <= 1e-5 * np.max(np.abs(a))
+    assert np.max(np.abs(untile(to_np(mg.bm), 20, c.H * c.d_c) - bm)) <= 1e-5 * np.max(np.abs(bm))
 
 
-def test_merges_bf16_within_one_ulp(gpu):
-    mg = Merged(gpu, v3_case(202), d_x=512, d_out=256, seed=203)
-    for got, exact in zip((mg.a, mg.bm), mg.oracle_weights()):
-        g = to_np(got)
+@pytest.mark.parametrize("d_x,d_out", [(512, 256), (1024, 384)])
+def test_merges_bf16_within_one_ulp(gpu, d_x, d_out):
+    """The fragment-tiled storage (both weights' shapes allow it)."""
+    mg = Merged(gpu, v3_case(202), d_x=d_x, d_out=d_out, seed=203)
+    c = mg.case
+    shapes = ((c.H * c.d_c, d_x), (d_out, c.H * c.d_c))
+    for got, exact, (R, K) in zip((mg.a, mg.bm), mg.oracle_weights(), shapes):
+        g = untile(to_np(got), R, K)
+        exact = exact.reshape(R, K)
         ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 1e-30))) - 7)
         assert np.all(np.abs(g - exact) <= ulp + 1e-6 * np.max(np.abs(exact)))
 
