@@ -67,6 +67,25 @@ def test_fast_matches_generic_path(gpu, latent, monkeypatch):
     assert rel_rms_err(fast, gen) <= tol
 
 
+@pytest.mark.parametrize("latent", ["bf16", "fp8"])
+def test_ranges_of_many_items(gpu, latent):
+    """Three workgroups over nine sequences: each walks several items one
+    after the other, ranges begin and end inside sequences, and an empty and
+    a one-token sequence sit between them. All outputs against the oracle."""
+    lens = [33, 1, 700, 64, 5, 2000, 31, 0, 129]
+    case = v3_case(lens, latent, seed=58)
+    run = DeviceRun(gpu, case)
+    plan = run.plan(n_workers=3)
+    ranges = plan.ranges()
+    assert len(ranges) == 3 and max(k1 - k0 for k0, k1 in ranges) >= 3
+    items = plan.items()
+    assert any(items[k0][0] == items[k0 - 1][0] for k0, _ in ranges[1:])  # a sequence split between ranges
+    o = to_np(run.decode(plan=plan))
+    assert run.status() == 0
+    check(case, o, TOL_FP8_REL if latent == "fp8" else TOL_BF16_REL)
+    assert np.all(o[lens.index(0)] == 0)
+
+
 @pytest.mark.parametrize("workers", [16, 5])
 def test_fp8_matrix_cores_and_widening_kernel(gpu, monkeypatch, workers):
     """An fp8 cache runs on the fp8 matrix cores by default (e4m3 codes
