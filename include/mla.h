@@ -280,8 +280,11 @@ mla_status mla_decode(const mla_dims *dims, const mla_cache *cache, const mla_pl
  * 1 <= q_len <= 16 (MLA_ERR_INVALID_ARG otherwise). Matrix-core path only:
  * arguments the fast path does not take (see mla_decode) return
  * MLA_ERR_UNSUPPORTED when q_len > 1. q_len = 1 is mla_decode, bit for bit.
- * The cache is read once for all q_len queries: the work per cached byte
- * grows q_len times. */
+ * Each range of the plan runs as one workgroup per 128 (token, head) pairs;
+ * the workgroups of one range sit on one XCD, so the cache comes from HBM
+ * about once for all q_len queries while the work per cached byte grows
+ * q_len times. A plan from mla_plan_create_multi with the same q_len keeps
+ * one workgroup per compute unit (any plan for these lengths is valid). */
 mla_status mla_decode_multi(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan, int32_t q_len,
                             const void *q_nope, const void *q_rope, const int32_t *q_pos, const void *w_uk,
                             const void *w_uv, mla_dtype q_w_dtype, void *o, mla_dtype o_dtype, void *ws,
