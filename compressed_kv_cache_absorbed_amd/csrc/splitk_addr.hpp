@@ -183,5 +183,23 @@ __host__ __device__ inline uint32_t raw_scale_off(const RawSrc &rs, int ln) {
   return static_cast<uint32_t>(imin(ln & 31, rs.tmax) - rs.s0) * 4u;
 }
 
+// Workgroup L of a split-K launch over R ranges and Y head blocks of 128:
+// range j, head block y. Workgroup L runs on XCD L % 8, so each XCD takes a
+// contiguous block of ranges: a sequence's items are consecutive, and the
+// splits of a sequence then share its absorbed query in that XCD's L2; the
+// head blocks of one range, next to each other there, share its cache tiles.
+__host__ __device__ __forceinline__ void range_of(int L, int R, int Y, int &j, int &y) {
+  const int nfull = R & ~7, lfull = nfull * Y;
+  if (L < lfull) {
+    const int sl = L >> 3;
+    j = (L & 7) * (nfull >> 3) + sl / Y;
+    y = sl - (sl / Y) * Y;
+  } else {
+    const int r = L - lfull;
+    j = nfull + r / Y;
+    y = r - (r / Y) * Y;
+  }
+}
+
 }  // namespace sa
 }  // namespace mla

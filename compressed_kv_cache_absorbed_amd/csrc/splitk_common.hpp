@@ -137,23 +137,9 @@ __device__ __forceinline__ ItemSeq item_seq(const mla_cache &c, const SeqInfo *s
   return r;
 }
 
-// Workgroup L of a split-K launch over R ranges and Y head blocks of 128:
-// range j, head block y. Workgroup L runs on XCD L % 8, so each XCD takes a
-// contiguous block of ranges: a sequence's items are consecutive, and the
-// splits of a sequence then share its absorbed query in that XCD's L2; the
-// head blocks of one range, next to each other there, share its cache tiles.
-__device__ __forceinline__ void range_of(int L, int R, int Y, int &j, int &y) {
-  const int nfull = R & ~7, lfull = nfull * Y;
-  if (L < lfull) {
-    const int sl = L >> 3;
-    j = (L & 7) * (nfull >> 3) + sl / Y;
-    y = sl - (sl / Y) * Y;
-  } else {
-    const int r = L - lfull;
-    j = nfull + r / Y;
-    y = r - (r / Y) * Y;
-  }
-}
+// (range_of, the workgroup -> (range, head block) map, sits with the copy
+// addresses in splitk_addr.hpp, where a CPU test checks it)
+using sa::range_of;
 
 }  // namespace
 }  // namespace mla

@@ -10,7 +10,9 @@
 //     chunk the LDS layout expects (the last valid token repeats past the
 //     tile's end);
 //   * the incremental row walk of the pipelined steps gives the same rows as
-//     the direct form.
+//     the direct form;
+//   * range_of maps a launch's workgroups onto every (range, head block)
+//     exactly once, each XCD taking a contiguous block of ranges.
 // Built host-only by __graft_entry__.build(); prints "ok <checks>" and exits
 // 0, or prints the first failure and exits 1.
 #include <cstdio>
@@ -195,6 +197,28 @@ int main() {
             const int ntiles = (n + T - 1) / T;
             for (int tile = 0; tile < ntiles + 4; ++tile) check_tile(L, cap, t0, n, tile, fp8 != 0);
           }
+        }
+      }
+    }
+  }
+  // range_of: the R Y workgroups of a launch take every (range, head block)
+  // exactly once, and XCD x (workgroups L % 8 == x) takes a contiguous block
+  // of the first R - R % 8 ranges, the last R % 8 spread over all XCDs
+  for (int Y = 1; Y <= 4; ++Y) {
+    for (int R = 0; R <= 300; ++R) {
+      std::vector<int> seen(static_cast<size_t>(R) * Y, 0);
+      const int nfull = R & ~7;
+      for (int L = 0; L < R * Y; ++L) {
+        int j = -1, y = -1;
+        range_of(L, R, Y, j, y);
+        ++g_checks;
+        if (j < 0 || j >= R || y < 0 || y >= Y || seen[static_cast<size_t>(j) * Y + y]++ != 0) {
+          std::printf("FAIL range_of: L %d of R %d Y %d gives range %d block %d\n", L, R, Y, j, y);
+          return 1;
+        }
+        if (L < nfull * Y && (j < (L % 8) * (nfull / 8) || j >= (L % 8 + 1) * (nfull / 8))) {
+          std::printf("FAIL range_of: L %d of R %d Y %d gives range %d outside its XCD's block\n", L, R, Y, j);
+          return 1;
         }
       }
     }
