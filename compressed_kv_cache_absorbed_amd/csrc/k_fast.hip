@@ -196,12 +196,17 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
 // ---------------------------------------------------------------- combine
 // The log-sum-exp merge of the split partials (base 2) and the W_UV product
 // ("02 — Multi-Latent Attention (MLA)", "Coste de cómputo": W_UV is applied
-// to the latent-space output) in one kernel. 1-D grid of H G workgroups
-// (G = ceil(B / NB) groups of NB sequences), 512 threads (8 waves).
-// Workgroup L runs on XCD L % 8 and all groups of one head get the same
+// to the latent-space output) in one kernel. 1-D grid of H GW workgroups,
+// 512 threads (8 waves); the G = ceil(B / NB) groups of NB sequences of a
+// head are dealt to its GW workgroups, each of which loads its W_UV rows once
+// and then runs steps 1-3 below for each of its groups in turn (GW is set so
+// that every workgroup of the launch is resident at once: with one
+// workgroup per group, 128 sequences gave 1024 workgroups, four rounds of
+// one per compute unit, each loading its head's weight rows again).
+// Workgroup L runs on XCD L % 8 and all workgroups of one head get the same
 // L % 8, so W_UV,i is fetched from HBM once and from that XCD's L2 by the
-// other groups. The partial rows arrive whole (1 KB per load
-// instruction), the W_UV rows as 64-byte pieces of 16 rows.
+// others. The partial rows arrive whole (1 KB per load instruction), the
+// W_UV rows as 64-byte pieces of 16 rows.
 //   1. For each sequence b of the group: M_b = max_s lse_s and
 //      den_b = sum_s 2^(lse_s - M_b), by an online max-and-sum of its
 //      TPB = 512 / NB threads over splits p, p + TPB, .., combined by
@@ -263,7 +268,7 @@ struct RowBatch {
 // EMIT: no W_UV product; o^ goes to ohat as bf16 hi and lo planes
 // [B, H 512] (the precomputed-weights decode applies W_O W_UV itself).
 template <int NB, bool EMIT>
-__global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr, int G, int VH, int n_items,
+__global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr, int G, int GW, int VH, int n_items,
                                                            const SeqInfo *__restrict__ seqs,
                                                            const int32_t *__restrict__ dev_len,
                                                            const uint16_t *__restrict__ opart,
@@ -283,43 +288,18 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
   __shared__ __attribute__((aligned(16))) char so[2 * 16 * OROW];
   __shared__ float red_m[NW], red_d[NW];
   __shared__ __attribute__((aligned(16))) float red_acc[R > 1 ? NW : 1][DC];
-  // workgroup L: head i (on XCD L % 8, with every group of that head),
-  // sequences b0 .. b0 + NB - 1, output rows vh * DV / VH .. +DV / VH - 1
-  // (VH = 2 only when a workgroup per (head, group) leaves compute units
-  // idle: the weight rows are then split between two workgroups, and wave
-  // w < 8 / VH takes rows 16 w .. 16 w + 15 of that half)
-  const int L = blockIdx.x, slot = L >> 3, per_head = G * VH;
-  const int i = (L & 7) + 8 * (slot / per_head), g = (slot % per_head) / VH, vh = slot % VH;
-  const int b0 = g * NB;
+  // workgroup L: head i (on XCD L % 8, with every workgroup of that head),
+  // groups gs, gs + GW, .. < G of NB sequences each, output rows
+  // vh * DV / VH .. +DV / VH - 1 (VH = 2 only when a workgroup per head and
+  // group leaves compute units idle: the weight rows are then split between
+  // two workgroups, and wave w < 8 / VH takes rows 16 w .. 16 w + 15 of that
+  // half). The weight rows are loaded once for all of the workgroup's groups.
+  const int L = blockIdx.x, slot = L >> 3, per_head = GW * VH;
+  const int i = (L & 7) + 8 * (slot / per_head), gs = (slot % per_head) / VH, vh = slot % VH;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const bool wact = !EMIT && 16 * w < DV / VH;  // this wave has weight rows
   const int vrow = vh * (DV / VH) + 16 * w;
-
   const int bl = tid / TPB, q = tid % TPB;
-  const int b = b0 + bl;
-  int S = 0, ib = 0;
-  if (b < B) {
-    const SeqInfo si = seqs[b];
-    // (a sequence's items must lie in the item list; the plan copy was
-    // checked, so this only guards the reads below)
-    const bool in_list = si.item_begin >= 0 && si.item_count >= 0 && si.item_begin <= n_items - si.item_count;
-    if (!in_list && q == 0 && i == 0) set_status(status, MLA_ERR_PLAN);
-    if (in_list && si.item_count > 0 && dev_len[b] == si.len) {
-      S = si.item_count;
-      ib = si.item_begin;
-    }
-  }
-  const float *lcol = lse + static_cast<size_t>(ib) * H + i;
-  // loads in the order they are needed: this thread's first lse for step 1,
-  // the first batch of partial rows for step 2 (they need no weight yet),
-  // then the weight rows for step 3
-  const float l0 = q < S ? lcol[static_cast<size_t>(q) * H] : -INFINITY;
-  const int r = TPB >= 64 ? q / 64 : 0;
-  const int c0 = TPB >= 64 ? 8 * (q % 64) : CPT * q;
-  const uint16_t *src = opart + (static_cast<size_t>(ib) * H + i) * DC + c0;
-  const size_t stride = static_cast<size_t>(H) * DC;
-  RowBatch<NL, SB, R> rb;
-  if (r < S) rb.issue(r, S, src, stride, lcol, H);
 
   // rows vrow .. vrow + 15 of W_UV,i straight into the A layout of the
   // products: k-step kk, lane l takes row l % 16, columns 32 kk + 8 (l / 16)
@@ -331,29 +311,7 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
 #pragma unroll
     for (int kk = 0; kk < DC / 32; ++kk) wa[kk] = *reinterpret_cast<const bf16x8 *>(wrow + 32 * kk);
   }
-
-  // 1. M_b and den_b
-  float M = -INFINITY, den = 0.0f;
-  lse_combine(M, den, l0, 1.0f);
-  for (int s = q + TPB; s < S; s += TPB) lse_combine(M, den, lcol[static_cast<size_t>(s) * H], 1.0f);
-#pragma unroll
-  for (int off = 1; off < (TPB < 64 ? TPB : 64); off <<= 1) {
-    const float m2 = __shfl_xor(M, off), d2 = __shfl_xor(den, off);
-    lse_combine(M, den, m2, d2);  // symmetric: every lane ends with the same value
-  }
-  if (TPB > 64) {
-    if (lane == 0) {
-      red_m[w] = M;
-      red_d[w] = den;
-    }
-    __syncthreads();
-    M = red_m[bl * R];
-    den = red_d[bl * R];
-#pragma unroll
-    for (int x = 1; x < R; ++x) lse_combine(M, den, red_m[bl * R + x], red_d[bl * R + x]);
-  }
-
-  // 2. o^[b]; rows NB .. 15 of the B operand are zero
+  // rows NB .. 15 of the B operand are zero (no group writes them)
   if (NB < 16) {
     constexpr int ZR = NB < 16 ? 16 - NB : 1;
     for (int x = tid; x < 2 * ZR * 64; x += 64 * NW) {
@@ -361,79 +319,131 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
       *reinterpret_cast<u32x4 *>(so + (pl * 16 + row) * OROW + 16 * (x % 64)) = u32x4{0, 0, 0, 0};
     }
   }
-  float acc[CPT];
-#pragma unroll
-  for (int e = 0; e < CPT; ++e) acc[e] = 0.0f;
-  if (M != -INFINITY && r < S) {
-    const float inv = 1.0f / den;
-    rb.consume(acc, r, S, M, inv);
-    for (int s0 = r + R * SB; s0 < S; s0 += R * SB) {
-      rb.issue(s0, S, src, stride, lcol, H);
-      rb.consume(acc, s0, S, M, inv);
-    }
-  }
 
-  if (R > 1) {
-    if (r > 0) {
-#pragma unroll
-      for (int e = 0; e < CPT; e += 4)
-        *reinterpret_cast<float4 *>(&red_acc[w][c0 + e]) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  for (int g = gs; g < G; g += GW) {
+    // every wave's products of the previous group have read o^ out of LDS
+    if (g != gs) __syncthreads();
+    const int b0 = g * NB;
+    const int b = b0 + bl;
+    int S = 0, ib = 0;
+    if (b < B) {
+      const SeqInfo si = seqs[b];
+      // (a sequence's items must lie in the item list; the plan copy was
+      // checked, so this only guards the reads below)
+      const bool in_list = si.item_begin >= 0 && si.item_count >= 0 && si.item_begin <= n_items - si.item_count;
+      if (!in_list && q == 0 && i == 0) set_status(status, MLA_ERR_PLAN);
+      if (in_list && si.item_count > 0 && dev_len[b] == si.len) {
+        S = si.item_count;
+        ib = si.item_begin;
+      }
     }
-    __syncthreads();
+    const float *lcol = lse + static_cast<size_t>(ib) * H + i;
+    // loads in the order they are needed: this thread's first lse for step 1,
+    // then the first batch of partial rows for step 2 (they need no weight yet)
+    const float l0 = q < S ? lcol[static_cast<size_t>(q) * H] : -INFINITY;
+    const int r = TPB >= 64 ? q / 64 : 0;
+    const int c0 = TPB >= 64 ? 8 * (q % 64) : CPT * q;
+    const uint16_t *src = opart + (static_cast<size_t>(ib) * H + i) * DC + c0;
+    const size_t stride = static_cast<size_t>(H) * DC;
+    RowBatch<NL, SB, R> rb;
+    if (r < S) rb.issue(r, S, src, stride, lcol, H);
+
+    // 1. M_b and den_b
+    float M = -INFINITY, den = 0.0f;
+    lse_combine(M, den, l0, 1.0f);
+    for (int s = q + TPB; s < S; s += TPB) lse_combine(M, den, lcol[static_cast<size_t>(s) * H], 1.0f);
+#pragma unroll
+    for (int off = 1; off < (TPB < 64 ? TPB : 64); off <<= 1) {
+      const float m2 = __shfl_xor(M, off), d2 = __shfl_xor(den, off);
+      lse_combine(M, den, m2, d2);  // symmetric: every lane ends with the same value
+    }
+    if (TPB > 64) {
+      if (lane == 0) {
+        red_m[w] = M;
+        red_d[w] = den;
+      }
+      __syncthreads();
+      M = red_m[bl * R];
+      den = red_d[bl * R];
+#pragma unroll
+      for (int x = 1; x < R; ++x) lse_combine(M, den, red_m[bl * R + x], red_d[bl * R + x]);
+    }
+
+    // 2. o^[b]
+    float acc[CPT];
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) acc[e] = 0.0f;
+    if (M != -INFINITY && r < S) {
+      const float inv = 1.0f / den;
+      rb.consume(acc, r, S, M, inv);
+      for (int s0 = r + R * SB; s0 < S; s0 += R * SB) {
+        rb.issue(s0, S, src, stride, lcol, H);
+        rb.consume(acc, s0, S, M, inv);
+      }
+    }
+
+    if (R > 1) {
+      if (r > 0) {
+#pragma unroll
+        for (int e = 0; e < CPT; e += 4)
+          *reinterpret_cast<float4 *>(&red_acc[w][c0 + e]) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+      }
+      __syncthreads();
+      if (r == 0) {
+#pragma unroll
+        for (int x = 1; x < R; ++x) {
+#pragma unroll
+          for (int e = 0; e < CPT; ++e) acc[e] += red_acc[w + x][c0 + e];
+        }
+      }
+    }
     if (r == 0) {
 #pragma unroll
-      for (int x = 1; x < R; ++x) {
+      for (int e0 = 0; e0 < CPT; e0 += 8) {
+        bf16x8 hi, lo;
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) acc[e] += red_acc[w + x][c0 + e];
-      }
-    }
-  }
-  if (r == 0) {
-#pragma unroll
-    for (int e0 = 0; e0 < CPT; e0 += 8) {
-      bf16x8 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 hv = static_cast<__bf16>(acc[e0 + e]);
-        hi[e] = hv;
-        lo[e] = static_cast<__bf16>(acc[e0 + e] - static_cast<float>(hv));
-      }
-      if constexpr (EMIT) {
-        if (b < B) {
-          const size_t off = (static_cast<size_t>(b) * H + i) * DC + c0 + e0;
-          *reinterpret_cast<bf16x8 *>(ohat_hi + off) = hi;
-          *reinterpret_cast<bf16x8 *>(ohat_lo + off) = lo;
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 hv = static_cast<__bf16>(acc[e0 + e]);
+          hi[e] = hv;
+          lo[e] = static_cast<__bf16>(acc[e0 + e] - static_cast<float>(hv));
         }
-      } else {
-        char *row = so + bl * OROW + 2 * (c0 + e0);
-        *reinterpret_cast<bf16x8 *>(row) = hi;
-        *reinterpret_cast<bf16x8 *>(row + 16 * OROW) = lo;
+        if constexpr (EMIT) {
+          if (b < B) {
+            const size_t off = (static_cast<size_t>(b) * H + i) * DC + c0 + e0;
+            *reinterpret_cast<bf16x8 *>(ohat_hi + off) = hi;
+            *reinterpret_cast<bf16x8 *>(ohat_lo + off) = lo;
+          }
+        } else {
+          char *row = so + bl * OROW + 2 * (c0 + e0);
+          *reinterpret_cast<bf16x8 *>(row) = hi;
+          *reinterpret_cast<bf16x8 *>(row + 16 * OROW) = lo;
+        }
       }
     }
-  }
-  if constexpr (EMIT) return;
-  __syncthreads();
+    if constexpr (EMIT) continue;
+    __syncthreads();
 
-  // 3. o = W_UV,i o^
-  f32x4 d = {};
-  if (wact) {
-    const char *bp = so + (lane & 15) * OROW + 16 * (lane >> 4);
+    // 3. o = W_UV,i o^
+    f32x4 d = {};
+    if (wact) {
+      const char *bp = so + (lane & 15) * OROW + 16 * (lane >> 4);
 #pragma unroll
-    for (int kk = 0; kk < DC / 32; ++kk) {
-      d = mfma16(wa[kk], *reinterpret_cast<const bf16x8 *>(bp + 64 * kk), d);
-      d = mfma16(wa[kk], *reinterpret_cast<const bf16x8 *>(bp + 64 * kk + 16 * OROW), d);
+      for (int kk = 0; kk < DC / 32; ++kk) {
+        d = mfma16(wa[kk], *reinterpret_cast<const bf16x8 *>(bp + 64 * kk), d);
+        d = mfma16(wa[kk], *reinterpret_cast<const bf16x8 *>(bp + 64 * kk + 16 * OROW), d);
+      }
     }
-  }
-  const int bo = b0 + (lane & 15);
-  if (wact && (lane & 15) < NB && bo < B) {
-    const size_t base = (static_cast<size_t>(bo) * H + i) * DV + vrow + 4 * (lane >> 4);
-    if (o_bf16) {
-      bf16x4 v;
+    const int bo = b0 + (lane & 15);
+    if (wact && (lane & 15) < NB && bo < B) {
+      const size_t base = (static_cast<size_t>(bo) * H + i) * DV + vrow + 4 * (lane >> 4);
+      if (o_bf16) {
+        bf16x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(d[e]);
-      *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(o) + base) = v;
-    } else {
-      *reinterpret_cast<float4 *>(static_cast<float *>(o) + base) = make_float4(d[0], d[1], d[2], d[3]);
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(d[e]);
+        *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(o) + base) = v;
+      } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(o) + base) = make_float4(d[0], d[1], d[2], d[3]);
+      }
     }
   }
 }
@@ -573,6 +583,15 @@ hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, i
                        static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seq_len, q_out, plan, status);
 }
 
+// Workgroups per head (and weight half) of the combine: G groups dealt to at
+// most one workgroup per compute unit over the launch (its 8 waves of ~250
+// registers fill a unit), so that all of them are resident at once.
+static int combine_workgroups_per_head(int heads, int G) {
+  constexpr int kSlots = 256;
+  const int per_head = kSlots / heads > 1 ? kSlots / heads : 1;
+  return G < per_head ? G : per_head;
+}
+
 hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t q_len, int32_t n_items,
                                const SeqInfo *seqs, const uint16_t *opart, const float *lse, const uint16_t *w_uv,
                                void *o, int o_bf16, int32_t *status) {
@@ -586,11 +605,12 @@ hipError_t launch_combine_fast(hipStream_t s, const mla_dims &d, const mla_cache
   // still fewer workgroups than compute units (one sequence): split each
   // head's weight rows over two workgroups
   const int VH = static_cast<int64_t>(H) * G < 256 ? 2 : 1;
-  const dim3 grid(H * G * VH);
-#define MLA_COMBINE(NBV)                                                                                      \
-  case NBV:                                                                                                  \
-    return launch_kernel(combine_fast_kernel<NBV, false>, grid, 512, 0, s, B, H, d.n_heads, G, VH, n_items, seqs, \
-                         c.seq_len, opart, lse, w_uv, o, o_bf16, nullptr, nullptr, status)
+  const int GW = combine_workgroups_per_head(H * VH, G);
+  const dim3 grid(H * GW * VH);
+#define MLA_COMBINE(NBV)                                                                                          \
+  case NBV:                                                                                                      \
+    return launch_kernel(combine_fast_kernel<NBV, false>, grid, 512, 0, s, B, H, d.n_heads, G, GW, VH, n_items, \
+                         seqs, c.seq_len, opart, lse, w_uv, o, o_bf16, nullptr, nullptr, status)
   switch (nb) {
     MLA_COMBINE(1);
     MLA_COMBINE(2);
@@ -610,11 +630,12 @@ hipError_t launch_combine_fast_emit(hipStream_t s, const mla_dims &d, const mla_
   int nb = 1;
   while (nb < 16 && static_cast<int64_t>(H) * ((B + 2 * nb - 1) / (2 * nb)) >= 256) nb *= 2;
   const int G = (B + nb - 1) / nb;
-  const dim3 grid(H * G);
-#define MLA_COMBINE(NBV)                                                                                      \
-  case NBV:                                                                                                  \
-    return launch_kernel(combine_fast_kernel<NBV, true>, grid, 512, 0, s, B, H, d.n_heads, G, 1, n_items, seqs,  \
-                         c.seq_len, opart, lse, nullptr, nullptr, 0, ohat_hi, ohat_lo, status)
+  const int GW = combine_workgroups_per_head(H, G);
+  const dim3 grid(H * GW);
+#define MLA_COMBINE(NBV)                                                                                          \
+  case NBV:                                                                                                      \
+    return launch_kernel(combine_fast_kernel<NBV, true>, grid, 512, 0, s, B, H, d.n_heads, G, GW, 1, n_items,   \
+                         seqs, c.seq_len, opart, lse, nullptr, nullptr, 0, ohat_hi, ohat_lo, status)
   switch (nb) {
     MLA_COMBINE(1);
     MLA_COMBINE(2);
