@@ -55,8 +55,13 @@ __device__ __forceinline__ int elem_bytes(mla_dtype t) {
 // reduced to [-pi, pi] by a - k 2 pi with 2 pi split into two doubles (the
 // fused multiply-add keeps k * hi exact; accurate to ~1e-15 for |k| < 2^30),
 // so the sine and cosine only ever see a small argument.
-__device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, int d, float base, float *c, float *s) {
-  const double theta = pow(static_cast<double>(base), -2.0 * j / d);
+
+// The rotation frequency of RoPE pair j of d dimensions, base^(-2j/d).
+__device__ __forceinline__ double rope_theta(int j, int d, float base) {
+  return pow(static_cast<double>(base), -2.0 * j / d);
+}
+// cos and sin of the angle pos * theta, reduced by 2 pi in fp64.
+__device__ __forceinline__ void rope_cos_sin_theta(int64_t pos, double theta, float *c, float *s) {
   const double a = static_cast<double>(pos) * theta;
   const double k = rint(a * 0.15915494309189535);  // 1 / (2 pi)
   double r = fma(-k, 6.283185307179586, a);          // 2 pi, high part
@@ -65,6 +70,9 @@ __device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, int d, float ba
   sincos(r, &sd, &cd);
   *c = static_cast<float>(cd);
   *s = static_cast<float>(sd);
+}
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, int d, float base, float *c, float *s) {
+  rope_cos_sin_theta(pos, rope_theta(j, d, base), c, s);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

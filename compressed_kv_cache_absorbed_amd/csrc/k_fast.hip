@@ -81,12 +81,68 @@ bool decode_fast_path(const mla_dims &d, const mla_cache &c, mla_dtype q_w_dtype
 namespace {
 
 // ----------------------------------------------------------------- absorb
-// Grid (H, 4, ceil(B/32)), 256 threads: head i, latent quarter cq (columns
-// 128 cq .. +127), 32 sequences. The quarter of W_UK,i [128 n x 128 c] is
-// staged in LDS with a 288-byte row stride (rows 32 bytes apart in the banks,
-// so the transposed reads below are conflict-free) and read transposed as the
-// A operand of q~^T = W_UK,i^T q_nope^T; wave w owns columns 32 w of the
-// quarter. The quarter also rotates RoPE pairs 8 cq .. 8 cq + 7 of q_rope.
+// Grid (Hr, 4), 256 threads: weight head iw, latent quarter cq (columns
+// 128 cq .. +127). The quarter of W_UK,iw [128 n x 128 c] is staged in LDS
+// once, with a 288-byte row stride (rows 32 bytes apart in the banks, so the
+// transposed reads below are conflict-free), and serves every unit that uses
+// it: the q_len query heads i = j Hr + iw (new token j) times the blocks of
+// 32 sequences. Per unit it is read transposed as the A operand of
+// q~^T = W_UK,iw^T q_nope^T; wave w owns columns 32 w of the quarter. The
+// unit also rotates RoPE pairs 8 cq .. 8 cq + 7 of q_rope. A unit's inputs
+// are loaded while the previous unit runs, and its RoPE is computed from
+// them then. (One workgroup per unit instead made 2048 workgroups at 128
+// sequences or four query tokens, each loading its 32 KB quarter again.)
+struct AbsorbIn {
+  int64_t P;     // RoPE position of this thread's pair
+  uint32_t xr;   // its two q_rope values (bf16)
+  bf16x8 qb[fast::DNOPE / 16];  // B operand: q_nope^T [16 n x 32 b], lane holds sequence b0 + l%32
+};
+__device__ __forceinline__ void absorb_load(AbsorbIn &in, int B, int H, int Hr, int q_len, int u, int nzb, int iw,
+                                            int cq, int tid, const uint16_t *__restrict__ q_nope,
+                                            const uint16_t *__restrict__ q_rope, const int32_t *__restrict__ q_pos,
+                                            const int32_t *__restrict__ dev_len) {
+  using namespace fast;
+  const int j = u / nzb, b0 = (u - j * nzb) * 32;
+  const int i = j * Hr + iw, back = q_len - 1 - j;
+  const int lane = tid & 63;
+  const int rb = b0 + (tid >> 3), rp = 8 * cq + (tid & 7);  // RoPE: sequence, pair
+  in.P = 0;
+  in.xr = 0;
+  if (rb < B) {
+    in.P = (q_pos ? q_pos[rb] : static_cast<int64_t>(dev_len[rb]) - 1) - back;
+    in.xr = *reinterpret_cast<const uint32_t *>(q_rope + (static_cast<size_t>(rb) * H + i) * DR + 2 * rp);
+  }
+  const int bb = b0 + (lane & 31);
+#pragma unroll
+  for (int kk = 0; kk < DNOPE / 16; ++kk) {
+    if (bb < B) {
+      in.qb[kk] = *reinterpret_cast<const bf16x8 *>(q_nope + (static_cast<size_t>(bb) * H + i) * DNOPE +
+                                                    16 * kk + 8 * (lane >> 5));
+    } else {
+      in.qb[kk] = bf16x8{};
+    }
+  }
+}
+// RoPE of pair rp = 8 cq + tid % 8 of sequence b0 + tid / 8 for query head i
+// of a unit, from its loaded inputs and the pair's frequency theta.
+__device__ __forceinline__ void absorb_rope(const AbsorbIn &in, int B, int H, int i, int b0, int cq, int tid,
+                                            double theta, float qscale, uint16_t *__restrict__ Q,
+                                            int32_t *__restrict__ status) {
+  using namespace fast;
+  const int rb = b0 + (tid >> 3), rp = 8 * cq + (tid & 7);
+  if (rb < B) {
+    float cs, sn;
+    rope_cos_sin_theta(in.P, theta, &cs, &sn);
+    const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(in.xr & 0xffffu));
+    const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(in.xr >> 16));
+    f16x2 r;
+    const float r0 = (x0 * cs - x1 * sn) * qscale, r1 = (x0 * sn + x1 * cs) * qscale;
+    if (!(fmaxf(fabsf(r0), fabsf(r1)) < kF16Max)) set_status(status, MLA_ERR_RANGE);
+    r[0] = static_cast<_Float16>(r0);
+    r[1] = static_cast<_Float16>(r1);
+    *reinterpret_cast<f16x2 *>(Q + (static_cast<size_t>(rb) * H + i) * D + DC + 2 * rp) = r;
+  }
+}
 __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, int q_len, float qscale, float rope_base,
                                                           const uint16_t *__restrict__ q_nope,
                                                           const uint16_t *__restrict__ q_rope,
@@ -98,32 +154,13 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
   using namespace fast;
   constexpr int WROW = 288;  // LDS bytes per W row (128 columns = 256 bytes + 32)
   __shared__ __attribute__((aligned(16))) char smem[DNOPE * WROW];
-  // head i of H = q_len * Hr: (new token j, head i % Hr), token-major
-  const int i = blockIdx.x, cq = blockIdx.y, b0 = blockIdx.z * 32;
-  const int iw = i % Hr, back = q_len - 1 - i / Hr;
+  const int iw = blockIdx.x, cq = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // every global load first, in the order of use: the RoPE inputs, the
-  // q_nope fragments, the weight quarter (32 KB: 128 rows x 16 chunks of
-  // 16 bytes, 8 per thread)
-  const int rb = b0 + (tid >> 3), rp = 8 * cq + (tid & 7);  // RoPE: sequence, pair
-  int64_t P = 0;
-  uint32_t xr = 0;
-  if (rb < B) {
-    P = (q_pos ? q_pos[rb] : static_cast<int64_t>(dev_len[rb]) - 1) - back;
-    xr = *reinterpret_cast<const uint32_t *>(q_rope + (static_cast<size_t>(rb) * H + i) * DR + 2 * rp);
-  }
-  // B operand: q_nope^T [16 n x 32 b]: lane holds sequence b0 + l%32, n = 16 kk + 8(l/32) .. +7
-  const int bb = b0 + (lane & 31);
-  bf16x8 qb[DNOPE / 16];
-#pragma unroll
-  for (int kk = 0; kk < DNOPE / 16; ++kk) {
-    if (bb < B) {
-      qb[kk] = *reinterpret_cast<const bf16x8 *>(q_nope + (static_cast<size_t>(bb) * H + i) * DNOPE +
-                                                 16 * kk + 8 * (lane >> 5));
-    } else {
-      qb[kk] = bf16x8{};
-    }
-  }
+  const int nzb = (B + 31) / 32, units = q_len * nzb;
+  // the first unit's inputs, then the weight quarter (32 KB: 128 rows x 16
+  // chunks of 16 bytes, 8 per thread)
+  AbsorbIn in;
+  absorb_load(in, B, H, Hr, q_len, 0, nzb, iw, cq, tid, q_nope, q_rope, q_pos, dev_len);
   const uint16_t *W = w_uk + static_cast<size_t>(iw) * DNOPE * DC + 128 * cq;
   u32x4 wv[8];
 #pragma unroll
@@ -134,62 +171,62 @@ __global__ __launch_bounds__(256) void absorb_fast_kernel(int B, int H, int Hr, 
   // the plan copy the split-K and combine kernels read, checked while this
   // workgroup's loads are in flight (after its own work it lengthened the
   // launch by its full latency)
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) plan_verify(plan);
-
-  // RoPE of pair rp of sequence rb, while the weights land
-  if (rb < B) {
-    float cs, sn;
-    rope_cos_sin(P, rp, DR, rope_base, &cs, &sn);
-    const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(xr & 0xffffu));
-    const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(xr >> 16));
-    f16x2 r;
-    const float r0 = (x0 * cs - x1 * sn) * qscale, r1 = (x0 * sn + x1 * cs) * qscale;
-    if (!(fmaxf(fabsf(r0), fabsf(r1)) < kF16Max)) set_status(status, MLA_ERR_RANGE);
-    r[0] = static_cast<_Float16>(r0);
-    r[1] = static_cast<_Float16>(r1);
-    *reinterpret_cast<f16x2 *>(Q + (static_cast<size_t>(rb) * H + i) * D + DC + 2 * rp) = r;
-  }
+  if (blockIdx.x == 0 && blockIdx.y == 0) plan_verify(plan);
+  // the first unit's RoPE while the weights land (this thread's pair, hence
+  // its frequency, is the same in every unit)
+  const double theta = rope_theta(8 * cq + (tid & 7), DR, rope_base);
+  absorb_rope(in, B, H, iw, 0, cq, tid, theta, qscale, Q, status);
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
     const int q = tid + 256 * x, n = q >> 4, ch = q & 15;
     *reinterpret_cast<u32x4 *>(smem + n * WROW + 16 * ch) = wv[x];
   }
   __syncthreads();
+
   // A operand: W^T [32 c x 16 n] via transposed LDS reads of W [n][c], with
   // the same contiguous k order as the B operand: in 16-lane group g the
   // lanes take c = c0 + 16(g%2) + i and n = 16 kk + 8(g/2) + e, e = 0..3 from
   // the first read and 4..7 from the second; source lane j points at
   // W[16 kk + 8(g/2) + j/4 (+4)][c0 + 16(g%2) + 4(j%4)].
-  const int g = (lane >> 4) & 3, j = lane & 15;
+  const int g = (lane >> 4) & 3, jl = lane & 15;
   const int c0 = 32 * w;
-  f32x16 acc = {};
+  for (int u = 0; u < units; ++u) {
+    const AbsorbIn cur = in;
+    if (u + 1 < units) absorb_load(in, B, H, Hr, q_len, u + 1, nzb, iw, cq, tid, q_nope, q_rope, q_pos, dev_len);
+    const int j = u / nzb, b0 = (u - j * nzb) * 32;
+    const int i = j * Hr + iw;
+    // (from inputs loaded one unit earlier; the first unit's ran above)
+    if (u > 0) absorb_rope(cur, B, H, i, b0, cq, tid, theta, qscale, Q, status);
+    f32x16 acc = {};
 #pragma unroll
-  for (int kk = 0; kk < DNOPE / 16; ++kk) {
-    const int n0 = 16 * kk + 8 * (g >> 1) + (j >> 2);
-    const int cc = c0 + 16 * (g & 1) + 4 * (j & 3);
-    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, smem + n0 * WROW + cc * 2));
-    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, smem + (n0 + 4) * WROW + cc * 2));
-    bf16x8 a;
-    a.lo = __builtin_bit_cast(bf16x4, lo);
-    a.hi = __builtin_bit_cast(bf16x4, hi);
-    acc = mfma32(a, qb[kk], acc);
-  }
-  // D [32 c x 32 b]: lane holds sequence b0 + l%32, c = c0 + 8(r/4) + 4(l/32) + r%4
-  if (bb < B) {
-    uint16_t *dst = Q + (static_cast<size_t>(bb) * H + i) * D + 128 * cq + c0 + 4 * (lane >> 5);
-    float amax = 0.0f;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      f16x4 v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = acc[4 * g4 + r] * qscale;
-        amax = fmaxf(amax, fabsf(x));
-        v[r] = static_cast<_Float16>(x);
-      }
-      *reinterpret_cast<f16x4 *>(dst + 8 * g4) = v;
+    for (int kk = 0; kk < DNOPE / 16; ++kk) {
+      const int n0 = 16 * kk + 8 * (g >> 1) + (jl >> 2);
+      const int cc = c0 + 16 * (g & 1) + 4 * (jl & 3);
+      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, smem + n0 * WROW + cc * 2));
+      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, smem + (n0 + 4) * WROW + cc * 2));
+      bf16x8 a;
+      a.lo = __builtin_bit_cast(bf16x4, lo);
+      a.hi = __builtin_bit_cast(bf16x4, hi);
+      acc = mfma32(a, cur.qb[kk], acc);
     }
-    if (!(amax < kF16Max)) set_status(status, MLA_ERR_RANGE);
+    // D [32 c x 32 b]: lane holds sequence b0 + l%32, c = c0 + 8(r/4) + 4(l/32) + r%4
+    const int bb = b0 + (lane & 31);
+    if (bb < B) {
+      uint16_t *dst = Q + (static_cast<size_t>(bb) * H + i) * D + 128 * cq + c0 + 4 * (lane >> 5);
+      float amax = 0.0f;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = acc[4 * g4 + r] * qscale;
+          amax = fmaxf(amax, fabsf(x));
+          v[r] = static_cast<_Float16>(x);
+        }
+        *reinterpret_cast<f16x4 *>(dst + 8 * g4) = v;
+      }
+      if (!(amax < kF16Max)) set_status(status, MLA_ERR_RANGE);
+    }
   }
 }
 
@@ -578,7 +615,7 @@ hipError_t launch_absorb_fast(hipStream_t s, const mla_dims &d, int32_t batch, i
                               const int32_t *seq_len, uint16_t *q_out, const PlanRef &plan,
                               int32_t *status) {
   const int H = d.n_heads * q_len;
-  return launch_kernel(absorb_fast_kernel, dim3(H, fast::DC / 128, (batch + 31) / 32), 256, 0, s, batch, H,
+  return launch_kernel(absorb_fast_kernel, dim3(d.n_heads, fast::DC / 128), 256, 0, s, batch, H,
                        d.n_heads, q_len, d.softmax_scale * kLog2e, d.rope_base, static_cast<const uint16_t *>(q_nope),
                        static_cast<const uint16_t *>(q_rope), q_pos, static_cast<const uint16_t *>(w_uk), seq_len, q_out, plan, status);
 }
