@@ -301,6 +301,21 @@ def test_streams_and_separate_workspaces(gpu):
             assert torch.equal(o, ref)
 
 
+@pytest.mark.parametrize("latent", ["bf16", "fp8"])
+def test_fast_many_groups_per_workgroup(gpu, latent):
+    """70 sequences: the combine deals a head's 5 groups of 16 sequences (the
+    last of 6) to its 2 workgroups, 3 and 2 groups each, which keep their
+    W_UV rows across them; each absorb workgroup runs its weight quarter over
+    3 blocks of 32 sequences (the last of 6) one after the other."""
+    rng = np.random.default_rng(1070)
+    lens = [int(x) for x in rng.integers(1, 600, size=70)]
+    case = v3_case(lens, latent, seed=61)
+    run = DeviceRun(gpu, case)
+    o = to_np(run.decode())
+    assert run.status() == 0
+    check(case, o, TOL_FP8_REL if latent == "fp8" else TOL_BF16_REL)
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
 def test_fast_random_shapes(gpu, seed):
     """Seeded random batches: 1-12 sequences of 0-3000 tokens, a random worker

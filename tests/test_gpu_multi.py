@@ -93,6 +93,22 @@ def test_multi_ragged_batch_sampled(gpu):
     assert rel_rms_err(got, ref) <= TOL_BF16_REL
 
 
+def test_multi_many_units_and_groups(gpu):
+    """40 sequences, 2 new tokens each (256 query heads): each absorb
+    workgroup runs its weight quarter over 2 tokens x 2 blocks of 32
+    sequences (the second block of 8), and each combine workgroup of a head
+    loops over its 3 groups of 16 sequences (the last of 8)."""
+    rng = np.random.default_rng(1040)
+    lens = [int(x) for x in rng.integers(0, 500, size=40)]
+    lens[3] = 1
+    case = v3_case(lens, "bf16", seed=84)
+    qn, qr = mla_synth.multi_queries(case, 2, seed=97)
+    run = DeviceRun(gpu, case)
+    o = to_np(run.decode_multi(2, qn, qr))
+    assert run.status() == 0
+    assert rel_rms_err(o, oracle_decode_multi(case, qn, qr)) <= TOL_BF16_REL
+
+
 @pytest.mark.parametrize("latent,q_len,workers", [("bf16", 4, 24), ("fp8", 3, 24), ("bf16", 2, 0), ("bf16", 16, 40)])
 def test_multi_plan_for_tokens(gpu, latent, q_len, workers):
     """A plan from mla_plan_create_multi (ranges cut for the head blocks of
