@@ -357,33 +357,60 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
     }
   }
 
+  const int r = TPB >= 64 ? q / 64 : 0;
+  const int c0 = TPB >= 64 ? 8 * (q % 64) : CPT * q;
+  const size_t stride = static_cast<size_t>(H) * DC;
+  // Group g's sequence for this thread: its plan entry and device length
+  // (loaded from an index clamped into the batch), then its split count S
+  // and first item ib (S = 0 past the batch, or when the entry is unusable).
+  struct GroupSeq {
+    SeqInfo si;
+    int32_t len;
+  };
+  auto group_seq = [&](int g) {
+    const int bc = min(g * NB + bl, B - 1);
+    return GroupSeq{seqs[bc], dev_len[bc]};
+  };
+  auto group_splits = [&](int g, const GroupSeq &x, int &S, int &ib) {
+    S = 0;
+    ib = 0;
+    if (g * NB + bl < B) {
+      // (a sequence's items must lie in the item list; the plan copy was
+      // checked, so this only guards the reads below)
+      const SeqInfo &si = x.si;
+      const bool in_list = si.item_begin >= 0 && si.item_count >= 0 && si.item_begin <= n_items - si.item_count;
+      if (!in_list && q == 0 && i == 0) set_status(status, MLA_ERR_PLAN);
+      if (in_list && si.item_count > 0 && x.len == si.len) {
+        S = si.item_count;
+        ib = si.item_begin;
+      }
+    }
+  };
+  // a group's first loads, in the order they are needed: this thread's first
+  // lse for step 1, then the first batch of partial rows for step 2
+  RowBatch<NL, SB, R> rb;
+  auto group_issue = [&](int S, int ib, float &l0) {
+    const float *lcol = lse + static_cast<size_t>(ib) * H + i;
+    l0 = q < S ? lcol[static_cast<size_t>(q) * H] : -INFINITY;
+    if (r < S) rb.issue(r, S, opart + (static_cast<size_t>(ib) * H + i) * DC + c0, stride, lcol, H);
+  };
+  int S, ib;
+  float l0;
+  group_splits(gs, group_seq(gs), S, ib);
+  group_issue(S, ib, l0);
+
   for (int g = gs; g < G; g += GW) {
     // every wave's products of the previous group have read o^ out of LDS
     if (g != gs) __syncthreads();
     const int b0 = g * NB;
     const int b = b0 + bl;
-    int S = 0, ib = 0;
-    if (b < B) {
-      const SeqInfo si = seqs[b];
-      // (a sequence's items must lie in the item list; the plan copy was
-      // checked, so this only guards the reads below)
-      const bool in_list = si.item_begin >= 0 && si.item_count >= 0 && si.item_begin <= n_items - si.item_count;
-      if (!in_list && q == 0 && i == 0) set_status(status, MLA_ERR_PLAN);
-      if (in_list && si.item_count > 0 && dev_len[b] == si.len) {
-        S = si.item_count;
-        ib = si.item_begin;
-      }
-    }
+    // the next group's sequence, read now and used once this group's rows
+    // are summed, when its first loads go out under this group's products
+    const int gn = g + GW;
+    GroupSeq nx;
+    if (gn < G) nx = group_seq(gn);
     const float *lcol = lse + static_cast<size_t>(ib) * H + i;
-    // loads in the order they are needed: this thread's first lse for step 1,
-    // then the first batch of partial rows for step 2 (they need no weight yet)
-    const float l0 = q < S ? lcol[static_cast<size_t>(q) * H] : -INFINITY;
-    const int r = TPB >= 64 ? q / 64 : 0;
-    const int c0 = TPB >= 64 ? 8 * (q % 64) : CPT * q;
     const uint16_t *src = opart + (static_cast<size_t>(ib) * H + i) * DC + c0;
-    const size_t stride = static_cast<size_t>(H) * DC;
-    RowBatch<NL, SB, R> rb;
-    if (r < S) rb.issue(r, S, src, stride, lcol, H);
 
     // 1. M_b and den_b
     float M = -INFINITY, den = 0.0f;
@@ -417,6 +444,11 @@ __global__ __launch_bounds__(512) void combine_fast_kernel(int B, int H, int Hr,
         rb.issue(s0, S, src, stride, lcol, H);
         rb.consume(acc, s0, S, M, inv);
       }
+    }
+    // (S, ib and l0 are not read again for this group)
+    if (gn < G) {
+      group_splits(gn, nx, S, ib);
+      group_issue(S, ib, l0);
     }
 
     if (R > 1) {
