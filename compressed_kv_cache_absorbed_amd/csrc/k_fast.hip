@@ -570,7 +570,10 @@ __global__ __launch_bounds__(64) void append_gemm_kernel(int T, int d_c, int d_m
 // partials, rotates the k_r part at that position, rounds to the storage
 // dtypes and writes the row; a sequence without room for all n_new tokens
 // is left untouched and reported (MLA_ERR_CAPACITY), as on the generic path.
-__global__ __launch_bounds__(256) void append_finish_kernel(mla_dims d, mla_cache c, int32_t n_new, int ksplit,
+// With one new token per sequence (advance) the sequence's only workgroup
+// also adds it to seq_len once the row is written (no other workgroup reads
+// that length); with several, advance_len_kernel does it afterwards.
+__global__ __launch_bounds__(256) void append_finish_kernel(mla_dims d, mla_cache c, int32_t n_new, int ksplit, bool advance,
                                                             const float *__restrict__ partial,
                                                             int32_t *__restrict__ status) {
   using namespace fast;
@@ -612,6 +615,7 @@ __global__ __launch_bounds__(256) void append_finish_kernel(mla_dims d, mla_cach
   }
   __syncthreads();
   store_appended_row(d, c, row, outv, red, status);
+  if (advance && tid == 0) c.seq_len[b] = len + 1;
 }
 
 }  // namespace
@@ -621,6 +625,8 @@ bool append_fast_shape(const mla_dims &d, int32_t tokens) {
   return tokens > 0 && n % 32 == 0 && n <= fast::APPEND_NMAX && d.d_model >= fast::APPEND_KS &&
          d.d_model % fast::APPEND_KS == 0;
 }
+
+int append_fast_ksplit(const mla_dims &d) { return d.d_model / fast::APPEND_KS; }
 
 bool append_fast_path(const mla_dims &d, int32_t tokens, mla_dtype act) {
   return !force_generic() && act == MLA_BF16 && append_fast_shape(d, tokens);
@@ -637,8 +643,10 @@ hipError_t launch_append_fast(hipStream_t s, const mla_dims &d, const mla_cache 
 
 hipError_t launch_append_finish(hipStream_t s, const mla_dims &d, const mla_cache &c, int32_t n_new,
                                 const float *partial, int ksplit, int32_t *status) {
-  hipError_t e = launch_kernel(append_finish_kernel, c.batch * n_new, 256, 0, s, d, c, n_new, ksplit, partial, status);
-  if (e != hipSuccess) return e;
+  const bool advance = n_new == 1;
+  hipError_t e =
+      launch_kernel(append_finish_kernel, c.batch * n_new, 256, 0, s, d, c, n_new, ksplit, advance, partial, status);
+  if (e != hipSuccess || advance) return e;
   return launch_advance_len(s, c, n_new);
 }
 

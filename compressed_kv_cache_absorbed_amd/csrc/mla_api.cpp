@@ -179,7 +179,7 @@ AppendWs append_ws_layout(const mla_dims &d, int32_t batch, int32_t n_new) {
   w.partial = off;
   const int64_t tokens = static_cast<int64_t>(batch) * n_new;
   if (append_fast_shape(d, static_cast<int32_t>(std::min<int64_t>(tokens, INT32_MAX)))) {
-    w.ksplit = std::max(1, d.d_model / 512);
+    w.ksplit = append_fast_ksplit(d);
     off = align_up(off + sizeof(float) * w.ksplit * tokens * (d.d_c + d.d_rope), 256);
   }
   w.total = off;

@@ -117,6 +117,9 @@ bool append_fast_path(const mla_dims &d, int32_t tokens, mla_dtype act_w_dtype);
 // The shapes the matrix-core append handles (the workspace is sized for it
 // whenever the shape qualifies, whatever the dtype or environment).
 bool append_fast_shape(const mla_dims &d, int32_t tokens);
+// K-splits of the matrix-core append's down-projection (d_model inputs per
+// split fixed by the kernel), when append_fast_shape holds.
+int append_fast_ksplit(const mla_dims &d);
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error. All take the stream first.
