@@ -62,7 +62,9 @@ _P = ctypes.c_void_p
 
 
 def lib_path():
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+    """The in-tree libmla.so, or the build MLA_LIBRARY names (e.g. a host-only
+    AddressSanitizer build from build.build_host_asan)."""
+    return os.environ.get("MLA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 
 
 def load():

@@ -50,7 +50,13 @@ def d128():
     ([2**30] * 3, 256), ([2**31 - 1, 5, 2**31 - 33], 1024),
 ])
 def test_plan_covers_every_token_once(lens, workers):
-    p = m.mla_plan_create(d128(), lens, workers)
+    check_plan(m.mla_plan_create(d128(), lens, workers), lens, workers)
+
+
+def check_plan(p, lens, workers):
+    """Every token of every sequence in exactly one item, a sequence's items
+    contiguous and in order on tile boundaries, the ranges cutting the item
+    list in order into at most `workers` non-empty runs."""
     items = p.items()
     cover = {b: [] for b in range(len(lens))}
     for b, t0, t1 in items:
@@ -75,6 +81,36 @@ def test_plan_covers_every_token_once(lens, workers):
     assert [k for r in ranges for k in range(*r)] == list(range(len(items)))
     assert all(k1 > k0 for k0, k1 in ranges)
     assert (len(ranges) == 0) == (sum(lens) == 0)
+
+
+def test_plan_invariants_on_seeded_random_batches():
+    """Both planners on 400 seeded random batches (uniform, log-uniform, tiny
+    and edge lengths; 1-2000 workers; 1-16 query tokens for the multi plan),
+    against the same invariants; the multi plan's ranges are also bounded by
+    the workers per head block and its items equal the one-token plan's at
+    that worker count."""
+    rng = np.random.default_rng(7)
+    for it in range(400):
+        B = int(rng.integers(1, 300))
+        kind = it % 4
+        if kind == 0:
+            lens = rng.integers(0, 70000, size=B)
+        elif kind == 1:
+            lens = np.exp(rng.uniform(0, 12, size=B)).astype(np.int64)
+        elif kind == 2:
+            lens = rng.integers(0, 40, size=B)
+        else:
+            lens = rng.choice([0, 1, 31, 32, 33, 4096, 131072], size=B)
+        lens = [int(x) for x in lens]
+        workers = int(rng.integers(1, 2000))
+        if it % 2 == 0:
+            check_plan(m.mla_plan_create(d128(), lens, workers), lens, workers)
+        else:
+            q_len = int(rng.integers(1, 17))
+            p = m.mla_plan_create_multi(d128(), lens, q_len, workers)
+            per_block = max(1, workers // q_len)
+            check_plan(p, lens, per_block)
+            assert p.items() == m.mla_plan_create(d128(), lens, per_block).items()
 
 
 ITEM_COST = 6  # the planner's fixed cost of an item, in tiles
