@@ -416,7 +416,16 @@ __device__ __forceinline__ i32x4 value_frag8(const VBase &vb, int cb) {
   const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(p + 16 * s8::ROWB));
   return i32x4{r0[0], r0[1], r1[0], r1[1]};
 }
-__device__ __forceinline__ i32x8 dup8(i32x4 v) { return i32x8{v[0], v[1], v[2], v[3], v[0], v[1], v[2], v[3]}; }
+// The same fragment read twice, straight into both halves of the 64-wide
+// operand (the lo block of P multiplies the same codes): two more LDS reads
+// instead of four register copies, and no vector-ALU write before the product.
+// (vb2 holds the same bases as vb in other registers, so the compiler cannot
+// merge the two reads back into one and copy its result)
+__device__ __forceinline__ i32x8 value_frag8x2(const VBase &vb, const VBase &vb2, int cb) {
+  const i32x4 a = value_frag8(vb, cb), b = value_frag8(vb2, cb);
+  return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+constexpr int VPF2 = 2;  // doubled fragments read ahead of their product
 
 // Value products of tile buffer B for this wave's heads, after the rescale
 // (if the running max moved): O^T block cb += codes^T P^T with P as hi / lo
@@ -425,9 +434,12 @@ template <int B, class Hide>
 __device__ __forceinline__ void pv8(State8 &st, const Soft8 &sm, bool fresh, Hide &hide) {
   using namespace s8;
   const VBase vb = value_bases8<B>(st.lane);
-  i32x4 va[VPF + 1];
+  VBase vb2;
 #pragma unroll
-  for (int n = 0; n < VPF; ++n) va[n] = value_frag8(vb, n);
+  for (int q = 0; q < 4; ++q) vb2.b[q] = opaque(vb.b[q]);
+  i32x8 va[VPF2 + 1];
+#pragma unroll
+  for (int n = 0; n < VPF2; ++n) va[n] = value_frag8x2(vb, vb2, n);
   if (!fresh && __any(sm.alpha != 1.0f)) {
 #pragma unroll
     for (int x = 0; x < DC / 32; ++x) {
@@ -443,10 +455,10 @@ __device__ __forceinline__ void pv8(State8 &st, const Soft8 &sm, bool fresh, Hid
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int cb = 0; cb < DC / 32; ++cb) {
-    if (cb + VPF < DC / 32) va[(cb + VPF) % (VPF + 1)] = value_frag8(vb, cb + VPF);
+    if (cb + VPF2 < DC / 32) va[(cb + VPF2) % (VPF2 + 1)] = value_frag8x2(vb, vb2, cb + VPF2);
     __builtin_amdgcn_sched_barrier(0);
-    if (cb == VBLK) mma8_acc_v(st.O[cb], dup8(va[cb % (VPF + 1)]), sm.Pb, 127, sm.sp);
-    else mma8_acc(st.O[cb], dup8(va[cb % (VPF + 1)]), sm.Pb, 127, sm.sp);
+    if (cb == VBLK) mma8_acc_v(st.O[cb], va[cb % (VPF2 + 1)], sm.Pb, 127, sm.sp);
+    else mma8_acc(st.O[cb], va[cb % (VPF2 + 1)], sm.Pb, 127, sm.sp);
     hide.value_step(cb);
     __builtin_amdgcn_sched_barrier(0);
   }
