@@ -802,13 +802,9 @@ __device__ __forceinline__ void splitk_item(const mla_cache &c, int H, int Hr, i
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) st.qf[kk] = *reinterpret_cast<const f16x8 *>(qrow + 16 * kk);
   }
-  // bf16: tiles 1 and 2 after Q, so that the first scores wait for tile 0
-  // and Q only (with every workgroup loading at once, each kilobyte waited
-  // for delays the first product)
-  if (!FP8) {
-    dma_bf16<1>(it, 1, w, lane);
-    dma_bf16<2>(it, 2, w, lane);
-  }
+  // bf16: tiles 1 and 2 only once tile 0 and Q have landed (below): with
+  // every workgroup loading at once, a workgroup's tile 0 otherwise queues
+  // behind the others' tiles 1 and 2
 #pragma unroll
   for (int db = 0; db < DC / 32; ++db) {
     st.O[db] = f32x16{};
@@ -830,8 +826,10 @@ __device__ __forceinline__ void splitk_item(const mla_cache &c, int H, int Hr, i
     wait_lds();
     dma_raw<0>(it, 2, w, lane);
   } else {
-    wait_vm<18>();  // tile 0 and Q landed; tiles 1 and 2 may still fly
+    wait_vm<0>();  // tile 0 and Q landed
     __builtin_amdgcn_sched_barrier(0);
+    dma_bf16<1>(it, 1, w, lane);
+    dma_bf16<2>(it, 2, w, lane);
     widen_bf16_inplace<0>(tid);
     wait_lds();
   }
@@ -917,26 +915,32 @@ __device__ __forceinline__ void splitk_item(const mla_cache &c, int H, int Hr, i
     f32x4 inv4;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) inv4[hb] = l4[hb] > 0.0f ? 1.0f / l4[hb] : 0.0f;
+    // one head block at a time, so the stores of a block's rows start while
+    // the next block is converted (with every workgroup writing its partial
+    // at once, the stores are bound by the write bandwidth)
     char *tb = g_lds + w * 128 * OROWQ;
-#pragma unroll
-    for (int x = 0; x < DC / 32; ++x) {
-      const int cb = x >> 2, hb = x & 3;
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(st.O[x][4 * g4 + e] * inv4[hb]);
-        // head 32 hb + lane%32, columns 32 cb + 8 g4 + 4 half .. +3 of this wave's 128
-        *reinterpret_cast<f16x4 *>(tb + (32 * hb + (lane & 31)) * OROWQ + 64 * cb + 16 * g4 + 8 * half) = v;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the rows come from other lanes
     uint16_t *orow = ob + 128 * w + 8 * (lane & 15);
 #pragma unroll
-    for (int x = 0; x < 32; ++x) {
-      const int h = 4 * x + (lane >> 4);
-      *reinterpret_cast<u32x4 *>(orow + static_cast<size_t>(h) * DC) =
-          *reinterpret_cast<const u32x4 *>(tb + h * OROWQ + 16 * (lane & 15));
+    for (int hb = 0; hb < 4; ++hb) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int x = 4 * cb + hb;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(st.O[x][4 * g4 + e] * inv4[hb]);
+          // head 32 hb + lane%32, columns 32 cb + 8 g4 + 4 half .. +3 of this wave's 128
+          *reinterpret_cast<f16x4 *>(tb + (32 * hb + (lane & 31)) * OROWQ + 64 * cb + 16 * g4 + 8 * half) = v;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the rows come from other lanes
+#pragma unroll
+      for (int x = 8 * hb; x < 8 * hb + 8; ++x) {
+        const int h = 4 * x + (lane >> 4);
+        *reinterpret_cast<u32x4 *>(orow + static_cast<size_t>(h) * DC) =
+            *reinterpret_cast<const u32x4 *>(tb + h * OROWQ + 16 * (lane & 15));
+      }
     }
   }
 }
