@@ -333,11 +333,26 @@ def cpu_baseline(res, budget_s):
     # per (token, head) cost, scaled to the step's tokens x heads
     per_tok_head = elapsed / tokens
     step_s = per_tok_head * float(case.lens.sum()) * case.H
+    # informational: the oracle's absorbed fp64 form (every head of a sampled
+    # sequence at once), scaled the same way
+    abs_elapsed, abs_tokens = 0.0, 0
+    for b in seqs:
+        s0, L = int(case.seq_start[b]), int(case.lens[b])
+        t0 = time.perf_counter()
+        omla.decode_absorbed_heads(C[s0:s0 + L], R[s0:s0 + L], args["q_nope"][b], args["q_rope"][b], args["w_uk"],
+                                   args["w_uv"], case.softmax_scale, case.rope_base, L - 1)
+        abs_elapsed += time.perf_counter() - t0
+        abs_tokens += L
+    abs_step_s = abs_elapsed / abs_tokens * float(case.lens.sum())
     return {"value": round(res["cache_bytes"] / step_s / 1e9, 6), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle", "step_seconds": round(step_s, 3), "cpu_model": cpu_model,
+            "kind": "oracle", "step_seconds": round(step_s, 3), "tokens_per_s": round(case.B / step_s, 4),
+            "absorbed_value": round(res["cache_bytes"] / abs_step_s / 1e9, 4),
+            "absorbed_step_seconds": round(abs_step_s, 4), "cpu_model": cpu_model,
             "host_cpus": os.cpu_count(), "blas": blas, "parity_max_err_over_rms": round(parity, 6),
             "sample": f"{done} (sequence, head) pairs of the workload ({tokens} token-heads, "
-                      f"{elapsed:.1f} s of fp64 non-absorbed decode), scaled to {case.B} sequences x {case.H} heads"}
+                      f"{elapsed:.1f} s of fp64 non-absorbed decode), scaled to {case.B} sequences x {case.H} heads; "
+                      f"absorbed_*: the oracle's absorbed fp64 form on all heads of {len(seqs)} sequences "
+                      f"({abs_elapsed:.2f} s), informational"}
 
 
 def stream_read_ceiling(m, torch, mib=4096, reps=20):
