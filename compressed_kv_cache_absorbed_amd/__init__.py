@@ -147,9 +147,9 @@ def _stream(stream):
 
 
 def dims(n_heads, d_c, d_rope, d_nope, d_v, d_model=0, softmax_scale=None, rope_base=10000.0):
-    if softmax_scale is None:
-        softmax_scale = (d_nope + d_rope) ** -0.5
-    return MlaDims(n_heads, d_c, d_rope, d_nope, d_v, d_model, softmax_scale, rope_base)
+    """mla_dims; softmax_scale None passes 0, which the library reads as (d_nope + d_rope)^-1/2."""
+    return MlaDims(n_heads, d_c, d_rope, d_nope, d_v, d_model, 0.0 if softmax_scale is None else softmax_scale,
+                   rope_base)
 
 
 def cache(rows, row_stride, latent_dtype, rope_dtype, seq_start, seq_cap, seq_len, scale=None,

@@ -517,6 +517,8 @@ mla_status decode_launch(const mla_dims *dims, const mla_cache *cache, const mla
                          const void *q_rope, const int32_t *q_pos, const void *w_uk, const void *w_uv, mla_dtype qw,
                          void *o, mla_dtype od, void *ws, hipStream_t s, int32_t q_len, bool compact,
                          bool clear_status) {
+  const mla_dims dd = with_default_scale(*dims);
+  dims = &dd;
   const bool fast = decode_fast_path(*dims, *cache, qw);
   const DecodeWs w = decode_ws_layout(*dims, *plan, q_len, compact && fast);
   char *base = static_cast<char *>(ws);
@@ -759,7 +761,7 @@ mla_status mla_decode_merged(const mla_dims *dims, const mla_cache *cache, const
   if (y_dtype != MLA_F32 && y_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(q_rope) || !aligned16(a) || !aligned16(bm) || !aligned16(y) || !aligned16(ws))
     return MLA_ERR_INVALID_ARG;
-  const mla_dims &d = *dims;
+  const mla_dims d = with_default_scale(*dims);
   const MergedWs w = merged_ws_layout(d, *plan, d_out);
   if (ws_bytes < w.total) return MLA_ERR_WORKSPACE;
   const bool fast = merged_fast_path(d, *cache, w_dtype, d_x, d_out);

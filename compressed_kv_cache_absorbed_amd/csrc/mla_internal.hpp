@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
+#include <cmath>
 #include <cstdint>
 #include <vector>
 
@@ -233,6 +234,13 @@ mla_status decode_check_args(const mla_dims *dims, const mla_cache *cache, const
                              mla_dtype qw, const void *o, mla_dtype od, const void *ws, size_t ws_bytes,
                              int32_t q_len);
 size_t decode_compact_bytes(const mla_dims &d, const mla_cache &c, const mla_plan &plan, mla_dtype qw);
+// softmax_scale 0 in mla_dims stands for the default (d_nope + d_rope)^(-1/2),
+// computed in double and rounded once to float.
+inline mla_dims with_default_scale(const mla_dims &d) {
+  mla_dims r = d;
+  if (r.softmax_scale == 0.0f) r.softmax_scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d.d_nope + d.d_rope)));
+  return r;
+}
 mla_status decode_launch(const mla_dims *dims, const mla_cache *cache, const mla_plan *plan, const void *q_nope,
                          const void *q_rope, const int32_t *q_pos, const void *w_uk, const void *w_uv, mla_dtype qw,
                          void *o, mla_dtype od, void *ws, hipStream_t s, int32_t q_len, bool compact,

@@ -77,7 +77,8 @@ typedef enum {
 } mla_dtype;
 
 /* Shapes of one MLA layer. softmax_scale multiplies the whole
- * (d_nope + d_rope)-wide score; rope_base is the RoPE base (10000 in the
+ * (d_nope + d_rope)-wide score; 0 selects (d_nope + d_rope)^(-1/2), the
+ * scale of the workloads (computed in double, rounded once to float); rope_base is the RoPE base (10000 in the
  * workloads). RoPE pairs are interleaved, (2j, 2j+1), at frequency
  * rope_base^(-2j/d_rope), positions absolute from 0. d_model is used only by
  * mla_append. d_rope must be even. */

@@ -368,3 +368,22 @@ def test_tensor_level_calls_match_the_abi(gpu):
     assert torch.equal(got, ref)
     with pytest.raises(ValueError):
         gpu.decode(b.d, b.cache, plan, b.t["q_nope"], b.t["q_rope"], b.t["w_uk"], b.t["w_uv"])  # int16 bits
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_default_softmax_scale_is_the_library_default(gpu, generic, monkeypatch):
+    """softmax_scale 0 in mla_dims (what dims() passes when none is given)
+    decodes bit for bit like an explicit (d_nope + d_rope)^-1/2, computed in
+    double and rounded once to float, on both paths."""
+    case = v3_case([77, 300, 1025], seed=57)
+    run = DeviceRun(gpu, case)
+    if generic:
+        monkeypatch.setenv("MLA_FORCE_GENERIC", "1")
+    explicit = float(np.float32(1.0 / np.sqrt(np.float64(case.d_nope + case.d_rope))))
+    run.d = gpu.dims(case.H, case.d_c, case.d_rope, case.d_nope, case.d_v, case.d_model, explicit, case.rope_base)
+    o1 = run.decode(n_workers=8)
+    run.d = gpu.dims(case.H, case.d_c, case.d_rope, case.d_nope, case.d_v, case.d_model, None, case.rope_base)
+    assert run.d.softmax_scale == 0.0
+    o2 = run.decode(n_workers=8)
+    assert run.status() == 0
+    assert torch.equal(o1, o2)
